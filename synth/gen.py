@@ -1,0 +1,202 @@
+"""Seeded synthetic inputs for the routed MoE FFN layer.
+
+Test and benchmark infrastructure shared by the fp64 oracle and the GPU path.
+It draws inputs and prepares them in the storage formats the layer consumes;
+it holds none of the layer's own steps (no routing, grouping, dequantization,
+matmul, activation or combine).
+
+Storage formats produced here (the formats the C ABI consumes):
+
+* router logits: float32 ``[T, E]``;
+* activations ``x``: bfloat16 bit patterns in a uint16 ``[T, H]`` array
+  (float32 draw rounded to nearest-even);
+* each expert matrix ``W[N, K]`` (gate and up: ``N=I, K=H``; down: ``N=H, K=I``)
+  as symmetric 4-bit integers in groups of ``g`` consecutive K elements,
+  one fp16 scale per group: ``packed uint8 [E, N, K/2]`` holding the
+  offset-binary nibble ``u = q + 8`` with the even K index in the low nibble,
+  and ``scales float16 [E, N, K/g]``.
+
+Grouped 4-bit weights with a per-group scale are what the Strata reviews
+describe ("源码静态评测：Strata 如何在消费级硬件跑本地大模型" (yfxerp.com),
+§3.1; the lqnn.cn static review, §3.1 "量化方案选型", which names group sizes
+32/64/128).  The scale rule ``s = fp16(max|w| / 7)`` with symmetric codes is
+the workload definition this library is measured on; the pages leave the
+rounding of the scale and of the codes open, so both are round-to-nearest-even
+here and the oracle and the kernels consume the same ``q`` and ``s``.
+
+Draw order (fixed, so a seed names one input set):
+``root = SeedSequence(seed)``; ``root.spawn(4)`` gives the streams for
+(logits, x, Zipf ranks, weights); the weight stream spawns one child per
+expert, drawing gate ``[I, H]``, up ``[I, H]``, down ``[H, I]`` in that order,
+float32 N(0, 0.02) (0.02 is the standard deviation).
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field, replace
+
+import numpy as np
+
+WEIGHT_STD = 0.02
+
+
+@dataclass(frozen=True)
+class MoEConfig:
+    """Shape of one MoE FFN layer invocation.
+
+    T tokens, hidden size H, expert intermediate size I, E experts, top-k,
+    int4 group size g along K.  ``zipf_s`` set means router logits get a
+    per-expert bias ``-zipf_s * ln(rank_e)`` over a seeded rank permutation,
+    so that expert popularity follows a Zipf law of exponent ``zipf_s``.
+    """
+
+    name: str
+    T: int
+    H: int
+    I: int
+    E: int
+    k: int
+    g: int
+    seed: int
+    zipf_s: float | None = None
+
+    @property
+    def pairs(self) -> int:
+        return self.T * self.k
+
+
+CONFIGS: dict[str, MoEConfig] = {
+    # tiny layer, single seed
+    "tiny": MoEConfig("tiny", T=64, H=256, I=128, E=16, k=2, g=32, seed=0),
+    # one decode token plus three speculative drafts verified together
+    "decode": MoEConfig("decode", T=4, H=2048, I=512, E=512, k=10, g=64, seed=1),
+    # a 512-token prefill batch
+    "prefill512": MoEConfig("prefill512", T=512, H=2048, I=512, E=512, k=10, g=64, seed=2),
+    # a 6144-token prefill chunk
+    "prefill6144": MoEConfig("prefill6144", T=6144, H=2048, I=512, E=512, k=10, g=64, seed=3),
+    # skewed, larger-shape prefill: Zipf(1.1) expert popularity
+    "zipf6144": MoEConfig("zipf6144", T=6144, H=4096, I=1024, E=256, k=8, g=128, seed=4, zipf_s=1.1),
+}
+
+
+def config(name_or_cfg, **overrides) -> MoEConfig:
+    cfg = CONFIGS[name_or_cfg] if isinstance(name_or_cfg, str) else name_or_cfg
+    return replace(cfg, **overrides) if overrides else cfg
+
+
+def weight_bytes_per_expert(cfg: MoEConfig) -> int:
+    """Packed bytes of one expert's three matrices plus their fp16 scales."""
+    n = 3 * cfg.H * cfg.I
+    return n // 2 + 2 * (n // cfg.g)
+
+
+@dataclass
+class MoEInputs:
+    cfg: MoEConfig
+    logits: np.ndarray  # float32 [T, E]
+    x_bf16: np.ndarray  # uint16 [T, H]
+    weights: dict = field(default_factory=dict)  # see module docstring
+
+
+def bf16_bits_from_f32(a: np.ndarray) -> np.ndarray:
+    """Round float32 values to bfloat16 (nearest, ties to even); return bit patterns."""
+    b = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    rounded = (b + (np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1)))) >> np.uint32(16)
+    return rounded.astype(np.uint16)
+
+
+def quantize_int4_groups(w: np.ndarray, g: int) -> tuple[np.ndarray, np.ndarray]:
+    """Symmetric int4 group quantization of ``w[N, K]`` along K.
+
+    Returns ``(packed uint8 [N, K/2], scales float16 [N, K/g])`` with
+    ``s = fp16(fp32(max|w|)/7)`` per group, ``q = clamp(rint(w / s), -8, 7)``
+    (``q = 0`` where ``s = 0``), nibble ``u = q + 8``, even K in the low nibble.
+    """
+    n, kdim = w.shape
+    if kdim % g or kdim % 2:
+        raise ValueError(f"K={kdim} must be a multiple of g={g} and of 2")
+    grp = np.asarray(w, dtype=np.float32).reshape(n, kdim // g, g)
+    amax = np.abs(grp).max(axis=2)
+    s16 = (amax / np.float32(7.0)).astype(np.float16)
+    s = s16.astype(np.float64)[..., None]
+    safe = np.where(s > 0, s, 1.0)
+    r = np.where(s > 0, grp.astype(np.float64) / safe, 0.0)
+    q = np.clip(np.rint(r), -8, 7).astype(np.int16)
+    u = (q + 8).astype(np.uint8).reshape(n, kdim)
+    packed = (u[:, 0::2] | (u[:, 1::2] << np.uint8(4))).astype(np.uint8)
+    return packed, s16
+
+
+def _streams(seed: int):
+    root = np.random.SeedSequence(seed)
+    return root.spawn(4)  # logits, x, zipf ranks, weights
+
+
+def make_logits(cfg: MoEConfig, seq: np.random.SeedSequence, rank_seq=None) -> np.ndarray:
+    rng = np.random.default_rng(seq)
+    logits = rng.standard_normal((cfg.T, cfg.E), dtype=np.float32)
+    if cfg.zipf_s is not None:
+        ranks = np.random.default_rng(rank_seq).permutation(cfg.E) + 1
+        bias = (-cfg.zipf_s * np.log(ranks.astype(np.float64))).astype(np.float32)
+        logits = logits + bias[None, :]
+    return np.ascontiguousarray(logits, dtype=np.float32)
+
+
+def make_x(cfg: MoEConfig, seq: np.random.SeedSequence) -> np.ndarray:
+    rng = np.random.default_rng(seq)
+    return bf16_bits_from_f32(rng.standard_normal((cfg.T, cfg.H), dtype=np.float32))
+
+
+def _expert_weights(cfg: MoEConfig, seq, e: int, out: dict) -> None:
+    rng = np.random.default_rng(seq)
+    std = np.float32(WEIGHT_STD)
+    for name, (n, kdim) in (("gate", (cfg.I, cfg.H)), ("up", (cfg.I, cfg.H)), ("down", (cfg.H, cfg.I))):
+        w = rng.standard_normal((n, kdim), dtype=np.float32) * std
+        packed, scales = quantize_int4_groups(w, cfg.g)
+        out[name][e] = packed
+        out[name + "_scale"][e] = scales
+
+
+def make_weights(cfg: MoEConfig, seq: np.random.SeedSequence, threads: int | None = None) -> dict:
+    E, H, I, g = cfg.E, cfg.H, cfg.I, cfg.g
+    out = {
+        "gate": np.empty((E, I, H // 2), np.uint8),
+        "gate_scale": np.empty((E, I, H // g), np.float16),
+        "up": np.empty((E, I, H // 2), np.uint8),
+        "up_scale": np.empty((E, I, H // g), np.float16),
+        "down": np.empty((E, H, I // 2), np.uint8),
+        "down_scale": np.empty((E, H, I // g), np.float16),
+    }
+    kids = seq.spawn(E)
+    threads = threads or min(16, os.cpu_count() or 1)
+    if threads <= 1 or E == 1:
+        for e in range(E):
+            _expert_weights(cfg, kids[e], e, out)
+    else:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(lambda e: _expert_weights(cfg, kids[e], e, out), range(E)))
+    return out
+
+
+def make_inputs(name_or_cfg, with_weights: bool = True, **overrides) -> MoEInputs:
+    cfg = config(name_or_cfg, **overrides)
+    s_logits, s_x, s_rank, s_w = _streams(cfg.seed)
+    inp = MoEInputs(cfg, make_logits(cfg, s_logits, s_rank), make_x(cfg, s_x))
+    if with_weights:
+        inp.weights = make_weights(cfg, s_w)
+    return inp
+
+
+def decode_steps(cfg: MoEConfig, steps: int) -> list[tuple[np.ndarray, np.ndarray]]:
+    """Independent (logits, x) draws for ``steps`` decode steps over one expert pool.
+
+    Step ``s`` uses ``SeedSequence([seed, 1000 + s])``; the Zipf ranks (if any)
+    are those of the layer's own seed, so every step sees the same pool.
+    """
+    _, _, s_rank, _ = _streams(cfg.seed)
+    out = []
+    for s in range(steps):
+        a, b = np.random.SeedSequence([cfg.seed, 1000 + s]).spawn(2)
+        out.append((make_logits(cfg, a, s_rank), make_x(cfg, b)))
+    return out
