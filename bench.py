@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed MoE FFN layer on one MI355X.
+
+Headline: MoE-layer prefill throughput (tokens/s) on the 6144-token chunk
+(T=6144, H=2048, I=512, E=512, top-10, int4 g=64).  One step = one layer
+invocation = route + permute + ffn (fused weighted combine) on inputs already
+resident in HBM.  Also reported on the same JSON line:
+
+* roofline of the dominant kernel, timed with HIP events the library records
+  around its own launches (on the launch stream), over a second timed region
+  of the same length;
+* decode: microseconds per step on the T=4 draft-verify layer (E=512, top-10),
+  cycling through 64 pre-drawn steps so each step touches a fresh expert
+  subset, with its HBM roofline;
+* the fp64 CPU oracle timed on this host on a bounded sample of the prefill
+  workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer prefill tokens/s @6144-tok chunk; decode µs/step; % roofline"
+PEAK_MFMA_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+KERNEL_SOURCES = {
+    "gemm_gateup": "quantized_expert_ffn_histogram_amd/csrc/ffn_gemm.hip",
+    "gemm_down": "quantized_expert_ffn_histogram_amd/csrc/ffn_gemm.hip",
+    "gemv_gateup": "quantized_expert_ffn_histogram_amd/csrc/ffn_gemv.hip",
+    "gemv_down": "quantized_expert_ffn_histogram_amd/csrc/ffn_gemv.hip",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(kernel: str) -> str | None:
+    rel = KERNEL_SOURCES.get(kernel)
+    if rel is None:
+        return None
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counted_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current source of the kernel; otherwise None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = data.get(f"{kernel}@{workload}")
+    if not rec or rec.get("source_sha") != source_sha(kernel):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def expert_weight_bytes(cfg, matrices: int = 3) -> int:
+    n = matrices * cfg.H * cfg.I
+    return n // 2 + 2 * (n // cfg.g)
+
+
+def kernel_work(kernel: str, cfg, pairs: int, distinct: int):
+    """Algorithmic work of one launch: (amount, unit, bound)."""
+    P, H, I = pairs, cfg.H, cfg.I
+    if kernel == "gemm_gateup":
+        return 4.0 * P * H * I, "flop", "mfma"
+    if kernel == "gemm_down":
+        return 2.0 * P * H * I, "flop", "mfma"
+    if kernel == "gemv_gateup":  # gate + up weights of the selected experts, plus x
+        return float(distinct * expert_weight_bytes(cfg, 2) + cfg.T * H * 2), "byte", "hbm"
+    if kernel == "gemv_down":  # down weights of the selected experts, plus out
+        return float(distinct * expert_weight_bytes(cfg, 1) + cfg.T * H * 4), "byte", "hbm"
+    return None, None, None
+
+
+def time_region(fn, steps: int):
+    import torch
+
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        fn(i)
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / 1e3  # seconds
+
+
+def kernel_table(qe):
+    rows = {}
+    for name in qe.timing_kernels():
+        n, ms = qe.timing_query(name)
+        if n:
+            rows[name] = dict(launches=n, avg_us=1e3 * ms / n, total_ms=ms)
+    return rows
+
+
+def roofline_of(kernel: str, avg_us: float, cfg, pairs: int, distinct: int, workload: str):
+    work, unit, bound = kernel_work(kernel, cfg, pairs, distinct)
+    if work is None:
+        return None
+    if unit == "flop":
+        achieved = work / (avg_us * 1e-6) / 1e12
+        peak, u = PEAK_MFMA_TFLOPS, "TFLOP/s"
+    else:
+        achieved = work / (avg_us * 1e-6) / 1e9
+        peak, u = PEAK_HBM_GBS, "GB/s"
+    return {
+        "kernel": kernel,
+        "bound": bound,
+        "achieved": round(achieved, 2),
+        "peak": peak,
+        "unit": u,
+        "frac": round(achieved / peak, 4),
+        "traffic": counted_traffic(kernel, workload),
+        "avg_us": round(avg_us, 2),
+        "work_per_launch": work,
+        "work_unit": unit,
+    }
+
+
+def bench_prefill(qe, args):
+    import torch
+
+    import synth
+
+    cfg = synth.config(args.workload)
+    t0 = time.time()
+    inp = synth.make_inputs(cfg)
+    log(f"[bench] inputs for {cfg.name} drawn in {time.time() - t0:.1f}s")
+    dev = torch.device("cuda:0")
+    logits = torch.from_numpy(inp.logits).to(dev)
+    x = torch.from_numpy(inp.x_bf16.view(np.int16)).to(dev).view(torch.bfloat16)
+    experts = qe.QuantizedExperts.from_numpy(inp.weights, cfg.g, dev)
+    run = qe.LayerRunner(experts, cfg.T, cfg.E, cfg.k, fused=True, device=dev)
+
+    for _ in range(args.warmup):
+        run(logits, x)
+    secs = time_region(lambda i: run(logits, x), args.steps)
+    log(f"[bench] {cfg.name}: {args.steps} steps in {secs * 1e3:.2f} ms")
+
+    qe.timing_enable(True)
+    secs_timed = time_region(lambda i: run(logits, x), args.steps)
+    table = kernel_table(qe)
+    qe.timing_enable(False)
+    for k_, v in table.items():
+        log(f"[bench]   {k_:16s} launches={v['launches']:5d} avg={v['avg_us']:9.2f} us")
+
+    distinct = int((run.counts > 0).sum().item())  # experts this layer call touches
+    dominant = max(table, key=lambda n: table[n]["total_ms"])
+    roof = roofline_of(dominant, table[dominant]["avg_us"], cfg, cfg.T * cfg.k, distinct, cfg.name)
+    kernels = {n: round(v["avg_us"], 2) for n, v in table.items()}
+    return cfg, inp, secs, secs_timed, roof, kernels
+
+
+def bench_decode(qe, args):
+    import torch
+
+    import synth
+
+    cfg = synth.config("decode")
+    inp = synth.make_inputs(cfg)
+    steps = synth.decode_steps(cfg, 64)
+    dev = torch.device("cuda:0")
+    experts = qe.QuantizedExperts.from_numpy(inp.weights, cfg.g, dev)
+    L = [torch.from_numpy(lg).to(dev) for lg, _ in steps]
+    X = [torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16) for _, xb in steps]
+    run = qe.LayerRunner(experts, cfg.T, cfg.E, cfg.k, fused=True, device=dev)
+    n = len(steps)
+    distinct = []
+    for i in range(n):  # also counts the experts each pre-drawn step touches
+        run(L[i], X[i])
+        distinct.append(int((run.counts > 0).sum().item()))
+    for i in range(args.warmup):
+        run(L[i % n], X[i % n])
+    K = args.decode_steps
+    secs = time_region(lambda i: run(L[i % n], X[i % n]), K)
+    qe.timing_enable(True)
+    time_region(lambda i: run(L[i % n], X[i % n]), K)
+    table = kernel_table(qe)
+    qe.timing_enable(False)
+    avg_distinct = float(np.mean([distinct[i % n] for i in range(K)]))
+    step_bytes = avg_distinct * expert_weight_bytes(cfg) + cfg.T * (cfg.H * 2 + cfg.E * 4 + cfg.k * 8 + cfg.H * 4)
+    us = secs / K * 1e6
+    kern = {}
+    for name in ("gemv_gateup", "gemv_down"):
+        if name in table:
+            r = roofline_of(name, table[name]["avg_us"], cfg, cfg.T * cfg.k, avg_distinct, cfg.name)
+            kern[name] = {k_: r[k_] for k_ in ("avg_us", "achieved", "frac", "traffic")}
+    device_us = sum(v["total_ms"] for v in table.values()) * 1e3 / K
+    return {
+        "workload": "decode: T=4 (1 token + 3 drafts) H=2048 I=512 E=512 k=10 g=64, 64 rotating steps",
+        "us_per_step": round(us, 2),
+        "device_us_per_step": round(device_us, 2),
+        "steps": K,
+        "alg_bytes_per_step": int(step_bytes),
+        "hbm_frac_step": round(step_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        "kernels_us": {n: round(v["avg_us"], 2) for n, v in table.items()},
+        "roofline": kern,
+    }
+
+
+def cpu_baseline(cfg, inp):
+    """The fp64 oracle on this host over the whole prefill layer (route, grouping,
+    per-expert dequant + SwiGLU, combine), timed once."""
+    import oracle
+
+    try:
+        import threadpoolctl
+
+        threads = max(p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()) or 1
+    except Exception:  # pragma: no cover
+        threads = 1
+    t0 = time.perf_counter()
+    oracle.moe_layer(inp.logits, inp.x_bf16, inp.weights, cfg.k, cfg.g)
+    secs = time.perf_counter() - t0
+    return {
+        "value": round(cfg.T / secs, 2),
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"the whole {cfg.name} layer ({cfg.T} tokens) once, fp64 NumPy with BLAS threads",
+        "seconds": round(secs, 2),
+        "affinity_cores": len(os.sched_getaffinity(0)),
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=2000)
+    ap.add_argument("--workload", default="prefill6144")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the MoE layer here is single-GPU (no sharding or collectives); "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import quantized_expert_ffn_histogram_amd as qe
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    qe.load()
+
+    cfg, inp, secs, secs_timed, roof, kernels = bench_prefill(qe, args)
+    result = {
+        "metric": METRIC,
+        "value": round(cfg.T * args.steps / secs, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(secs / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} g={cfg.g}",
+            "weights": "int4 symmetric, fp16 scale per group",
+            "activations": "bf16 in, fp32 out",
+            "global_batch": cfg.T,
+            "parallelism": "single GPU",
+        },
+        "roofline": roof,
+        "kernels_us": kernels,
+        "ms_per_step_with_kernel_events": round(secs_timed / args.steps * 1e3, 4),
+    }
+    if not args.no_decode:
+        result["decode"] = bench_decode(qe, args)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, inp)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,254 @@
+"""Routed mixture-of-experts FFN layer for AMD Instinct MI355X (gfx950).
+
+Python binding of ``libstrata_moe.so``: argument marshalling only.  Every step
+of the layer runs in the library's HIP kernels; PyTorch supplies device memory
+and the current stream.  The names follow the C ABI in ``include/strata_moe.h``:
+
+    ids, w = route(logits, k)
+    counts, offsets, perm, inv_perm = permute(ids, E)
+    out = ffn(x, experts, offsets, perm, k, topk_w=w)      # fused combine
+    y = ffn(x, experts, offsets, perm, k)                  # grouped rows
+    out = combine(y, inv_perm, w, k)                       # deterministic combine
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from ._abi import LIB_PATH, StrataError, StrataMoeWeights, check, load  # noqa: F401
+
+__all__ = [
+    "QuantizedExperts",
+    "StrataError",
+    "route",
+    "permute",
+    "ffn",
+    "combine",
+    "moe_layer",
+    "LayerRunner",
+    "workspace_size",
+    "timing_enable",
+    "timing_query",
+    "timing_kernels",
+    "load",
+    "LIB_PATH",
+]
+
+
+def _stream(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _p(t: torch.Tensor | None) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _need(t: torch.Tensor, dtype, name: str) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+@dataclass
+class QuantizedExperts:
+    """Group-quantized int4 expert weights resident on the GPU.
+
+    gate, up: uint8 [E, I, H/2]; down: uint8 [E, H, I/2]; *_scale: float16
+    [E, N, K/g].  Nibble u = q + 8, even K in the low nibble.
+    """
+
+    gate: torch.Tensor
+    gate_scale: torch.Tensor
+    up: torch.Tensor
+    up_scale: torch.Tensor
+    down: torch.Tensor
+    down_scale: torch.Tensor
+    group: int
+
+    @property
+    def num_experts(self) -> int:
+        return int(self.gate.shape[0])
+
+    @property
+    def inter(self) -> int:
+        return int(self.gate.shape[1])
+
+    @property
+    def hidden(self) -> int:
+        return int(self.gate.shape[2] * 2)
+
+    @classmethod
+    def from_numpy(cls, w: dict, group: int, device="cuda") -> "QuantizedExperts":
+        def u8(a):
+            return torch.from_numpy(a).to(device)
+
+        def f16(a):
+            return torch.from_numpy(a).to(device)
+
+        return cls(u8(w["gate"]), f16(w["gate_scale"]), u8(w["up"]), f16(w["up_scale"]),
+                   u8(w["down"]), f16(w["down_scale"]), group)
+
+    def descriptor(self) -> StrataMoeWeights:
+        for name, dt in (("gate", torch.uint8), ("up", torch.uint8), ("down", torch.uint8),
+                         ("gate_scale", torch.float16), ("up_scale", torch.float16),
+                         ("down_scale", torch.float16)):
+            _need(getattr(self, name), dt, name)
+        return StrataMoeWeights(
+            self.gate.data_ptr(), self.gate_scale.data_ptr(), self.up.data_ptr(),
+            self.up_scale.data_ptr(), self.down.data_ptr(), self.down_scale.data_ptr(),
+            self.num_experts, self.hidden, self.inter, self.group,
+        )
+
+
+def workspace_size(T: int, E: int, k: int, H: int, I: int, g: int) -> int:
+    return int(load().strata_moe_workspace_size(T, E, k, H, I, g))
+
+
+def _workspace(device, nbytes: int, workspace: torch.Tensor | None) -> torch.Tensor:
+    if workspace is not None:
+        return workspace
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def route(logits: torch.Tensor, k: int):
+    """``strata_moe_route``: returns (topk_ids int32 [T, k], topk_w float32 [T, k])."""
+    _need(logits, torch.float32, "logits")
+    T, E = logits.shape
+    ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    check(load().strata_moe_route(_p(logits), T, E, k, _p(ids), _p(w), _stream(logits)))
+    return ids, w
+
+
+def permute(topk_ids: torch.Tensor, E: int, workspace: torch.Tensor | None = None):
+    """``strata_moe_permute``: returns (counts [E], offsets [E+1], perm [T*k], inv_perm [T*k])."""
+    _need(topk_ids, torch.int32, "topk_ids")
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    counts = torch.empty(E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+    perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+    inv = torch.empty(T * k, dtype=torch.int32, device=dev)
+    ws = _workspace(dev, load().strata_moe_workspace_size(T, E, k, 256, 128, 32), workspace)
+    check(load().strata_moe_permute(_p(topk_ids), T, E, k, _p(counts), _p(offsets), _p(perm), _p(inv),
+                                    _p(ws), ws.numel(), _stream(topk_ids)))
+    return counts, offsets, perm, inv
+
+
+def ffn(x: torch.Tensor, experts: QuantizedExperts, offsets: torch.Tensor, perm: torch.Tensor, k: int,
+        topk_w: torch.Tensor | None = None, out: torch.Tensor | None = None,
+        workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """``strata_moe_ffn``: out [T, H] float32 when ``topk_w`` is given (fused combine),
+    otherwise y [T*k, H] float32 in grouped order."""
+    _need(x, torch.bfloat16, "x")
+    _need(offsets, torch.int32, "offsets")
+    _need(perm, torch.int32, "perm")
+    if topk_w is not None:
+        _need(topk_w, torch.float32, "topk_w")
+    T, H = x.shape
+    rows = T if topk_w is not None else T * k
+    if out is None:
+        out = torch.empty((rows, H), dtype=torch.float32, device=x.device)
+    desc = experts.descriptor()
+    need = load().strata_moe_workspace_size(T, experts.num_experts, k, experts.hidden, experts.inter,
+                                            experts.group)
+    ws = _workspace(x.device, need, workspace)
+    check(load().strata_moe_ffn(_p(x), T, k, ctypes.byref(desc), _p(offsets), _p(perm), _p(topk_w), _p(out),
+                                _p(ws), ws.numel(), _stream(x)))
+    return out
+
+
+def combine(y: torch.Tensor, inv_perm: torch.Tensor, topk_w: torch.Tensor, k: int) -> torch.Tensor:
+    """``strata_moe_combine``: out [T, H] float32, summed in slot order."""
+    _need(y, torch.float32, "y")
+    _need(inv_perm, torch.int32, "inv_perm")
+    _need(topk_w, torch.float32, "topk_w")
+    P, H = y.shape
+    T = P // k
+    out = torch.empty((T, H), dtype=torch.float32, device=y.device)
+    check(load().strata_moe_combine(_p(y), _p(inv_perm), _p(topk_w), T, k, H, _p(out), _stream(y)))
+    return out
+
+
+def moe_layer(logits: torch.Tensor, x: torch.Tensor, experts: QuantizedExperts, k: int, fused: bool = True,
+              workspace: torch.Tensor | None = None) -> dict:
+    """All four calls for one layer invocation on the current stream."""
+    E = experts.num_experts
+    T = x.shape[0]
+    if workspace is None:
+        workspace = _workspace(x.device, workspace_size(T, E, k, experts.hidden, experts.inter, experts.group), None)
+    ids, w = route(logits, k)
+    counts, offsets, perm, inv = permute(ids, E, workspace)
+    res = dict(ids=ids, w=w, counts=counts, offsets=offsets, perm=perm, inv_perm=inv)
+    if fused:
+        res["out"] = ffn(x, experts, offsets, perm, k, topk_w=w, workspace=workspace)
+    else:
+        y = ffn(x, experts, offsets, perm, k, workspace=workspace)
+        res["y"] = y
+        res["out"] = combine(y, inv, w, k)
+    return res
+
+
+def timing_enable(on: bool = True) -> None:
+    """Start (or stop) per-kernel event timing inside the library; clears old records."""
+    check(load().strata_moe_timing_enable(1 if on else 0))
+
+
+def timing_query(kernel: str | None = None) -> tuple[int, float]:
+    """(launches, total device ms) of ``kernel`` (None: all) since timing_enable."""
+    n = ctypes.c_int32(0)
+    ms = ctypes.c_double(0.0)
+    check(load().strata_moe_timing_query(kernel.encode() if kernel else None, ctypes.byref(n), ctypes.byref(ms)))
+    return int(n.value), float(ms.value)
+
+
+def timing_kernels() -> list[str]:
+    lib = load()
+    n = lib.strata_moe_timing_kernels(None, 0)
+    arr = (ctypes.c_char_p * max(n, 1))()
+    lib.strata_moe_timing_kernels(arr, n)
+    return [arr[i].decode() for i in range(n)]
+
+
+class LayerRunner:
+    """One layer invocation (route, permute, ffn[, combine]) with preallocated
+    outputs and workspace, for timing loops.  Marshalling only: each call is
+    the same three or four C-ABI calls as ``moe_layer``."""
+
+    def __init__(self, experts: QuantizedExperts, T: int, E: int, k: int, fused: bool = True, device="cuda"):
+        self.experts, self.T, self.E, self.k, self.fused = experts, T, E, k, fused
+        H = experts.hidden
+        dev = torch.device(device)
+        self.ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.counts = torch.empty(E, dtype=torch.int32, device=dev)
+        self.offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        self.perm = torch.empty(T * k, dtype=torch.int32, device=dev)
+        self.inv = torch.empty(T * k, dtype=torch.int32, device=dev)
+        self.out = torch.empty((T, H), dtype=torch.float32, device=dev)
+        self.y = None if fused else torch.empty((T * k, H), dtype=torch.float32, device=dev)
+        nbytes = workspace_size(T, E, k, H, experts.inter, experts.group)
+        self.ws = _workspace(dev, nbytes, None)
+        self.desc = experts.descriptor()
+        self.lib = load()
+
+    def __call__(self, logits: torch.Tensor, x: torch.Tensor) -> torch.Tensor:
+        lib, T, E, k = self.lib, self.T, self.E, self.k
+        s = _stream(x)
+        check(lib.strata_moe_route(_p(logits), T, E, k, _p(self.ids), _p(self.w), s))
+        check(lib.strata_moe_permute(_p(self.ids), T, E, k, _p(self.counts), _p(self.offsets), _p(self.perm),
+                                     _p(self.inv), _p(self.ws), self.ws.numel(), s))
+        if self.fused:
+            check(lib.strata_moe_ffn(_p(x), T, k, ctypes.byref(self.desc), _p(self.offsets), _p(self.perm),
+                                     _p(self.w), _p(self.out), _p(self.ws), self.ws.numel(), s))
+        else:
+            check(lib.strata_moe_ffn(_p(x), T, k, ctypes.byref(self.desc), _p(self.offsets), _p(self.perm),
+                                     None, _p(self.y), _p(self.ws), self.ws.numel(), s))
+            check(lib.strata_moe_combine(_p(self.y), _p(self.inv), _p(self.w), T, k, self.experts.hidden,
+                                         _p(self.out), s))
+        return self.out

@@ -1,0 +1,91 @@
+"""ctypes declarations of libstrata_moe.so (the C ABI in include/strata_moe.h)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_NAME = "libstrata_moe.so"
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+STATUS = {
+    0: "STRATA_OK",
+    1: "STRATA_ERR_INVALID_ARGUMENT",
+    2: "STRATA_ERR_UNSUPPORTED",
+    3: "STRATA_ERR_WORKSPACE",
+    4: "STRATA_ERR_HIP",
+}
+
+# Every symbol the public header declares, with (restype, argtypes).
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_sz = ctypes.c_size_t
+
+
+class StrataMoeWeights(ctypes.Structure):
+    """Mirror of ``strata_moe_weights`` (device pointers + sizes)."""
+
+    _fields_ = [
+        ("gate", _vp),
+        ("gate_scale", _vp),
+        ("up", _vp),
+        ("up_scale", _vp),
+        ("down", _vp),
+        ("down_scale", _vp),
+        ("num_experts", _i32),
+        ("hidden", _i32),
+        ("inter", _i32),
+        ("group", _i32),
+    ]
+
+
+SIGNATURES = {
+    "strata_moe_route": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "strata_moe_permute": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "strata_moe_ffn": (
+        ctypes.c_int,
+        [_vp, _i32, _i32, ctypes.POINTER(StrataMoeWeights), _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    ),
+    "strata_moe_combine": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "strata_moe_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "strata_moe_last_error": (ctypes.c_char_p, []),
+    "strata_moe_timing_enable": (ctypes.c_int, [_i32]),
+    "strata_moe_timing_query": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(_i32), ctypes.POINTER(ctypes.c_double)]),
+    "strata_moe_timing_kernels": (_i32, [ctypes.POINTER(ctypes.c_char_p), _i32]),
+}
+
+_lib = None
+
+
+class StrataError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{STATUS.get(code, code)}: {message}")
+        self.code = code
+        self.status = STATUS.get(code, str(code))
+        self.message = message
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load the HIP library; raise if it has not been built (there is no fallback)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"{p} is missing: build it with `python -m quantized_expert_ffn_histogram_amd.build_lib` "
+            "(there is no CPU or PyTorch fallback for the MoE layer)"
+        )
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def check(code: int) -> None:
+    if code != 0:
+        msg = load().strata_moe_last_error()
+        raise StrataError(code, msg.decode() if msg else "")

@@ -1,0 +1,262 @@
+// C ABI of the MoE FFN library: argument checks, error reporting, workspace
+// carving and path selection.  Every check runs before anything is enqueued;
+// errors name the parameter and its value and never fall back silently to
+// another path (yfxerp.com static review §5.2 "explicit error path" and §6.2
+// "messages carry the parameter name and current value").
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/strata_moe.h"
+#include "moe_internal.h"
+
+namespace strata {
+bool gemv_supported(int T, int H, int I);
+}
+
+using namespace strata;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char *fn, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = std::string(fn) + ": " + buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return STRATA_OK;
+}
+
+int hip_fail(const char *fn, hipError_t e) {
+  return fail(STRATA_ERR_HIP, fn, "HIP error %d (%s)", (int)e, hipGetErrorString(e));
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE_PTR(fn, p)                                                                      \
+  do {                                                                                          \
+    if ((p) == nullptr) return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "%s is NULL", #p);        \
+    if (!aligned16(p))                                                                          \
+      return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "%s=%p is not 16-byte aligned", #p, (const void *)(p)); \
+  } while (0)
+
+// Common T/E/k checks.
+int check_tek(const char *fn, long long T, long long E, long long k) {
+  if (T < 0) return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "T=%lld is negative", T);
+  if (E < 1) return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "E=%lld must be >= 1", E);
+  if (E > kMaxExperts) return fail(STRATA_ERR_UNSUPPORTED, fn, "E=%lld exceeds the supported maximum %d", E, kMaxExperts);
+  if (k < 1) return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "k=%lld must be >= 1", k);
+  if (k > E) return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "k=%lld exceeds E=%lld", k, E);
+  if (k > kMaxTopK) return fail(STRATA_ERR_UNSUPPORTED, fn, "k=%lld exceeds the supported maximum %d", k, kMaxTopK);
+  if (T * k >= (1ll << 31)) return fail(STRATA_ERR_UNSUPPORTED, fn, "T*k=%lld must be < 2^31", T * k);
+  return STRATA_OK;
+}
+
+int check_shape(const char *fn, long long H, long long I, long long g) {
+  if (g != 32 && g != 64 && g != 128)
+    return fail(STRATA_ERR_UNSUPPORTED, fn, "group=%lld is not one of 32, 64, 128", g);
+  if (H < 256 || H > 16384 || H % 256)
+    return fail(STRATA_ERR_UNSUPPORTED, fn, "hidden=%lld must be a multiple of 256 in [256, 16384]", H);
+  if (I < 128 || I > 16384 || I % 128)
+    return fail(STRATA_ERR_UNSUPPORTED, fn, "inter=%lld must be a multiple of 128 in [128, 16384]", I);
+  return STRATA_OK;
+}
+
+enum class FfnPath { Auto, Gemm, Gemv };
+
+// Read on every call (a getenv is negligible next to a kernel launch), so a
+// process can switch paths between calls.
+FfnPath ffn_path_env() {
+  const char *v = std::getenv("STRATA_MOE_FFN_PATH");
+  if (!v || !*v || !std::strcmp(v, "auto")) return FfnPath::Auto;
+  if (!std::strcmp(v, "gemm")) return FfnPath::Gemm;
+  if (!std::strcmp(v, "gemv")) return FfnPath::Gemv;
+  return FfnPath::Auto;
+}
+
+bool ffn_path_env_valid() {
+  const char *v = std::getenv("STRATA_MOE_FFN_PATH");
+  return !v || !*v || !std::strcmp(v, "auto") || !std::strcmp(v, "gemm") || !std::strcmp(v, "gemv");
+}
+
+}  // namespace
+
+namespace strata {
+
+size_t ffn_workspace_bytes(long long pairs, int E, int H, int I) {
+  (void)H;
+  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+  const long long tiles_gemm = (pairs + kGemmRows - 1) / kGemmRows + std::min<long long>(E, pairs);
+  const long long tiles_gemv = (pairs + kGemvRows - 1) / kGemvRows + std::min<long long>(E, pairs);
+  const long long tiles = std::max(tiles_gemm, tiles_gemv) + 1;
+  return up((size_t)pairs * I * 2) + up((size_t)tiles * sizeof(Tile)) + 256;
+}
+
+FfnWorkspace carve_ffn_workspace(void *base, long long pairs, int E, int H, int I) {
+  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+  char *p = static_cast<char *>(base);
+  FfnWorkspace w{};
+  w.h = reinterpret_cast<uint16_t *>(p);
+  p += up((size_t)pairs * I * 2);
+  const long long tiles_gemm = (pairs + kGemmRows - 1) / kGemmRows + std::min<long long>(E, pairs);
+  const long long tiles_gemv = (pairs + kGemvRows - 1) / kGemvRows + std::min<long long>(E, pairs);
+  const long long tiles = std::max(tiles_gemm, tiles_gemv) + 1;
+  w.tiles = reinterpret_cast<Tile *>(p);
+  p += up((size_t)tiles * sizeof(Tile));
+  w.meta = reinterpret_cast<int *>(p);
+  w.bytes = ffn_workspace_bytes(pairs, E, H, I);
+  return w;
+}
+
+}  // namespace strata
+
+extern "C" {
+
+const char *strata_moe_last_error(void) { return g_last_error.c_str(); }
+
+size_t strata_moe_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I, int32_t g) {
+  if (check_tek("strata_moe_workspace_size", T, E, k) != STRATA_OK) return 0;
+  if (check_shape("strata_moe_workspace_size", H, I, g) != STRATA_OK) return 0;
+  const long long pairs = (long long)T * k;
+  return std::max(permute_workspace_bytes(pairs, E), ffn_workspace_bytes(pairs, E, H, I));
+}
+
+int strata_moe_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *topk_ids,
+                     float *topk_w, void *stream) {
+  static const char *fn = "strata_moe_route";
+  if (int rc = check_tek(fn, T, E, k)) return rc;
+  if (T == 0) return ok();
+  REQUIRE_PTR(fn, logits);
+  REQUIRE_PTR(fn, topk_ids);
+  REQUIRE_PTR(fn, topk_w);
+  const hipError_t e = launch_route(logits, T, E, k, topk_ids, topk_w, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(fn, e);
+}
+
+int strata_moe_permute(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k, int32_t *counts,
+                       int32_t *offsets, int32_t *perm, int32_t *inv_perm, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+  static const char *fn = "strata_moe_permute";
+  if (int rc = check_tek(fn, T, E, k)) return rc;
+  REQUIRE_PTR(fn, counts);
+  REQUIRE_PTR(fn, offsets);
+  if (T > 0) {
+    REQUIRE_PTR(fn, topk_ids);
+    REQUIRE_PTR(fn, perm);
+    REQUIRE_PTR(fn, inv_perm);
+  }
+  const long long pairs = (long long)T * k;
+  const size_t need = permute_workspace_bytes(pairs, E);
+  if (need > 0) {
+    if (workspace == nullptr)
+      return fail(STRATA_ERR_WORKSPACE, fn, "workspace is NULL but %zu bytes are required", need);
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "workspace=%p is not 256-byte aligned", workspace);
+    if (workspace_bytes < need)
+      return fail(STRATA_ERR_WORKSPACE, fn, "workspace_bytes=%zu is smaller than the required %zu", workspace_bytes, need);
+  }
+  // T == 0 still defines counts = 0 and offsets = 0 (the small path handles it).
+  const hipError_t e = launch_permute(topk_ids, (int)pairs, E, counts, offsets, perm, inv_perm, workspace,
+                                      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(fn, e);
+}
+
+int strata_moe_ffn(const uint16_t *x_bf16, int32_t T, int32_t k, const strata_moe_weights *w,
+                   const int32_t *offsets, const int32_t *perm, const float *topk_w, float *y_or_out,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+  static const char *fn = "strata_moe_ffn";
+  if (w == nullptr) return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "w is NULL");
+  if (int rc = check_tek(fn, T, w->num_experts, k)) return rc;
+  if (int rc = check_shape(fn, w->hidden, w->inter, w->group)) return rc;
+  if (!ffn_path_env_valid())
+    return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "STRATA_MOE_FFN_PATH=%s is not one of auto, gemm, gemv",
+                std::getenv("STRATA_MOE_FFN_PATH"));
+  if (T == 0) return ok();
+  REQUIRE_PTR(fn, x_bf16);
+  REQUIRE_PTR(fn, offsets);
+  REQUIRE_PTR(fn, perm);
+  REQUIRE_PTR(fn, y_or_out);
+  REQUIRE_PTR(fn, w->gate);
+  REQUIRE_PTR(fn, w->gate_scale);
+  REQUIRE_PTR(fn, w->up);
+  REQUIRE_PTR(fn, w->up_scale);
+  REQUIRE_PTR(fn, w->down);
+  REQUIRE_PTR(fn, w->down_scale);
+  if (topk_w != nullptr && !aligned16(topk_w))
+    return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "topk_w=%p is not 16-byte aligned", (const void *)topk_w);
+  const int E = w->num_experts, H = w->hidden, I = w->inter, g = w->group;
+  const long long pairs = (long long)T * k;
+  const size_t need = ffn_workspace_bytes(pairs, E, H, I);
+  if (workspace == nullptr)
+    return fail(STRATA_ERR_WORKSPACE, fn, "workspace is NULL but %zu bytes are required", need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "workspace=%p is not 256-byte aligned", workspace);
+  if (workspace_bytes < need)
+    return fail(STRATA_ERR_WORKSPACE, fn, "workspace_bytes=%zu is smaller than the required %zu", workspace_bytes, need);
+
+  const FfnPath forced = ffn_path_env();
+  const bool gemv_ok = gemv_supported(T, H, I);
+  if (forced == FfnPath::Gemv && !gemv_ok)
+    return fail(STRATA_ERR_UNSUPPORTED, fn,
+                "STRATA_MOE_FFN_PATH=gemv needs T <= %d, hidden in {256,512,1024,2048,4096} and inter a power of two "
+                "in [128, 2048] (T=%d, hidden=%d, inter=%d)",
+                kGemvMaxTokens, T, H, I);
+  const bool use_gemv = forced == FfnPath::Gemv || (forced == FfnPath::Auto && gemv_ok);
+
+  FfnWeights fw{w->gate, w->up, w->down, w->gate_scale, w->up_scale, w->down_scale, E, H, I, g};
+  const FfnWorkspace ws = carve_ffn_workspace(workspace, pairs, E, H, I);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = use_gemv ? launch_ffn_gemv(x_bf16, T, k, fw, offsets, perm, topk_w, y_or_out, ws, s)
+                                : launch_ffn_gemm(x_bf16, T, k, fw, offsets, perm, topk_w, y_or_out, ws, s);
+  return e == hipSuccess ? ok() : hip_fail(fn, e);
+}
+
+int strata_moe_combine(const float *y, const int32_t *inv_perm, const float *topk_w, int32_t T, int32_t k,
+                       int32_t H, float *out, void *stream) {
+  static const char *fn = "strata_moe_combine";
+  if (T < 0) return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "T=%d is negative", T);
+  if (k < 1) return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "k=%d must be >= 1", k);
+  if (k > kMaxTopK) return fail(STRATA_ERR_UNSUPPORTED, fn, "k=%d exceeds the supported maximum %d", k, kMaxTopK);
+  if (H < 4 || H % 4) return fail(STRATA_ERR_UNSUPPORTED, fn, "H=%d must be a positive multiple of 4", H);
+  if ((long long)T * k >= (1ll << 31)) return fail(STRATA_ERR_UNSUPPORTED, fn, "T*k=%lld must be < 2^31", (long long)T * k);
+  if (T == 0) return ok();
+  REQUIRE_PTR(fn, y);
+  REQUIRE_PTR(fn, inv_perm);
+  REQUIRE_PTR(fn, topk_w);
+  REQUIRE_PTR(fn, out);
+  const hipError_t e = launch_combine(y, inv_perm, topk_w, T, k, H, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(fn, e);
+}
+
+int strata_moe_timing_enable(int32_t on) {
+  timing_enable(on);
+  return ok();
+}
+
+int strata_moe_timing_query(const char *kernel, int32_t *launches, double *total_ms) {
+  static const char *fn = "strata_moe_timing_query";
+  if (launches == nullptr || total_ms == nullptr)
+    return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "launches and total_ms must not be NULL");
+  int n = 0;
+  double ms = 0.0;
+  if (timing_query(kernel, &n, &ms) != 0) return fail(STRATA_ERR_HIP, fn, "waiting for timing events failed");
+  *launches = n;
+  *total_ms = ms;
+  return ok();
+}
+
+int32_t strata_moe_timing_kernels(const char **names, int32_t max_names) {
+  return timing_names(names, names ? max_names : 0);
+}
+
+}  // extern "C"

@@ -1,0 +1,41 @@
+// Weighted combine of each token's k expert outputs (deterministic form):
+//   out[t][n] = sum_{j=0}^{k-1} topk_w[t*k+j] * y[inv_perm[t*k+j]][n],
+// summed in j order.  The fused form of the same sum is the down-GEMM
+// epilogue; this kernel finishes the layer when the FFN wrote grouped rows.
+#include "moe_internal.h"
+
+namespace strata {
+namespace {
+
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y,
+                                                      const int *__restrict__ inv_perm,
+                                                      const float *__restrict__ topk_w, int T, int k,
+                                                      int H, float *__restrict__ out) {
+  const int chunks = (H / 4 + 255) / 256;
+  const int t = blockIdx.x / chunks;
+  const int n4 = (blockIdx.x - t * chunks) * 256 + threadIdx.x;  // float4 column index
+  if (n4 * 4 >= H) return;
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const int i = inv_perm[(size_t)t * k + j];
+    const float w = topk_w[(size_t)t * k + j];
+    const float4 v = reinterpret_cast<const float4 *>(y + (size_t)i * H)[n4];
+    acc.x += w * v.x;
+    acc.y += w * v.y;
+    acc.z += w * v.z;
+    acc.w += w * v.w;
+  }
+  reinterpret_cast<float4 *>(out + (size_t)t * H)[n4] = acc;
+}
+
+}  // namespace
+
+hipError_t launch_combine(const float *y, const int *inv_perm, const float *topk_w, int T, int k,
+                          int H, float *out, hipStream_t s) {
+  const long long blocks = (long long)ceil_div(H / 4, 256) * T;
+  KernelTimer timer("combine", s);
+  combine_kernel<<<dim3((unsigned)blocks), 256, 0, s>>>(y, inv_perm, topk_w, T, k, H, out);
+  return hipGetLastError();
+}
+
+}  // namespace strata

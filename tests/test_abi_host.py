@@ -1,0 +1,171 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared
+symbol, sizes workspaces, and rejects bad arguments before touching a GPU.
+
+No call here reaches a kernel launch: every call either is a pure host query
+or fails argument validation, which runs before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "strata_moe.h")
+
+
+def _lib():
+    from quantized_expert_ffn_histogram_amd import _abi
+
+    if not os.path.exists(_abi.LIB_PATH):
+        pytest.skip("library not built")
+    return _abi, _abi.load()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(strata_moe_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    syms = declared_symbols()
+    for name in ("strata_moe_route", "strata_moe_permute", "strata_moe_ffn", "strata_moe_combine"):
+        assert name in syms
+
+
+def test_every_declared_symbol_is_exported():
+    abi, lib = _lib()
+    syms = declared_symbols()
+    out = subprocess.run(["nm", "-D", "--defined-only", abi.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (strata_moe_\w+)", out))
+    for name in syms:
+        assert name in exported, name
+        assert hasattr(lib, name)
+        assert name in abi.SIGNATURES
+
+
+def test_workspace_size_valid_and_invalid():
+    _, lib = _lib()
+    # prefill chunk: h (T*k*I fp16) dominates
+    n = lib.strata_moe_workspace_size(6144, 512, 10, 2048, 512, 64)
+    assert n >= 6144 * 10 * 512 * 2
+    assert n % 256 == 0
+    assert lib.strata_moe_workspace_size(4, 512, 10, 2048, 512, 64) > 0
+    assert lib.strata_moe_workspace_size(4, 512, 600, 2048, 512, 64) == 0  # k > E
+    assert lib.strata_moe_workspace_size(4, 512, 10, 2048, 512, 48) == 0  # bad group
+    assert lib.strata_moe_workspace_size(-1, 512, 10, 2048, 512, 64) == 0
+
+
+def _err(lib):
+    return lib.strata_moe_last_error().decode()
+
+
+@pytest.mark.parametrize(
+    "T,E,k,code,needle",
+    [
+        (-1, 16, 2, 1, "T=-1"),
+        (4, 0, 1, 1, "E=0"),
+        (4, 2000, 2, 2, "E=2000"),
+        (4, 16, 0, 1, "k=0"),
+        (4, 16, 17, 1, "k=17 exceeds E=16"),
+        (4, 512, 40, 2, "k=40"),
+    ],
+)
+def test_route_rejects_bad_sizes(T, E, k, code, needle):
+    _, lib = _lib()
+    assert lib.strata_moe_route(None, T, E, k, None, None, None) == code
+    assert needle in _err(lib)
+    assert _err(lib).startswith("strata_moe_route")
+
+
+def test_route_rejects_null_and_misaligned_pointers():
+    _, lib = _lib()
+    assert lib.strata_moe_route(None, 4, 16, 2, None, None, None) == 1
+    assert "logits is NULL" in _err(lib)
+    assert lib.strata_moe_route(ctypes.c_void_p(0x1004), 4, 16, 2, ctypes.c_void_p(0x2000),
+                                ctypes.c_void_p(0x3000), None) == 1
+    assert "not 16-byte aligned" in _err(lib)
+
+
+def test_zero_tokens_is_ok_and_launches_nothing():
+    _, lib = _lib()
+    assert lib.strata_moe_route(None, 0, 16, 2, None, None, None) == 0
+    assert _err(lib) == ""
+    assert lib.strata_moe_combine(None, None, None, 0, 2, 256, None, None) == 0
+
+
+def test_permute_requires_workspace_for_large_inputs():
+    _, lib = _lib()
+    fake = ctypes.c_void_p(0x10000)
+    args = [fake, 6144, 512, 10, fake, fake, fake, fake]
+    assert lib.strata_moe_permute(*args, None, 0, None) == 3
+    assert "workspace is NULL" in _err(lib)
+    assert lib.strata_moe_permute(*args, fake, 16, None) == 3
+    assert "workspace_bytes=16" in _err(lib)
+    assert lib.strata_moe_permute(*args, ctypes.c_void_p(0x10010), 1 << 30, None) == 1
+    assert "256-byte aligned" in _err(lib)
+
+
+def _weights(abi, E=16, H=256, I=128, g=32, ptr=0x10000):
+    p = ctypes.c_void_p(ptr).value
+    return abi.StrataMoeWeights(p, p, p, p, p, p, E, H, I, g)
+
+
+@pytest.mark.parametrize(
+    "kw,code,needle",
+    [
+        (dict(g=48), 2, "group=48"),
+        (dict(H=300), 2, "hidden=300"),
+        (dict(I=100), 2, "inter=100"),
+        (dict(E=2000), 2, "E=2000"),
+    ],
+)
+def test_ffn_rejects_unsupported_shapes(kw, code, needle):
+    abi, lib = _lib()
+    w = _weights(abi, **kw)
+    fake = ctypes.c_void_p(0x10000)
+    rc = lib.strata_moe_ffn(fake, 8, 2, ctypes.byref(w), fake, fake, None, fake, fake, 1 << 30, None)
+    assert rc == code
+    assert needle in _err(lib)
+
+
+def test_ffn_rejects_null_weights_and_small_workspace():
+    abi, lib = _lib()
+    fake = ctypes.c_void_p(0x10000)
+    assert lib.strata_moe_ffn(fake, 8, 2, None, fake, fake, None, fake, fake, 1 << 30, None) == 1
+    assert "w is NULL" in _err(lib)
+    w = _weights(abi)
+    w.down = None
+    assert lib.strata_moe_ffn(fake, 8, 2, ctypes.byref(w), fake, fake, None, fake, fake, 1 << 30, None) == 1
+    assert "w->down is NULL" in _err(lib)
+    w = _weights(abi)
+    assert lib.strata_moe_ffn(fake, 8, 2, ctypes.byref(w), fake, fake, None, fake, fake, 64, None) == 3
+    assert "workspace_bytes=64" in _err(lib)
+
+
+def test_ffn_path_override_is_checked(monkeypatch):
+    abi, lib = _lib()
+    fake = ctypes.c_void_p(0x10000)
+    w = _weights(abi)
+    monkeypatch.setenv("STRATA_MOE_FFN_PATH", "fastest")
+    assert lib.strata_moe_ffn(fake, 8, 2, ctypes.byref(w), fake, fake, None, fake, fake, 1 << 30, None) == 1
+    assert "STRATA_MOE_FFN_PATH=fastest" in _err(lib)
+    monkeypatch.setenv("STRATA_MOE_FFN_PATH", "gemv")  # T=64 is outside the GEMV envelope
+    assert lib.strata_moe_ffn(fake, 64, 2, ctypes.byref(w), fake, fake, None, fake, fake, 1 << 30, None) == 2
+    assert "gemv" in _err(lib)
+
+
+def test_combine_rejects_bad_h():
+    _, lib = _lib()
+    fake = ctypes.c_void_p(0x10000)
+    assert lib.strata_moe_combine(fake, fake, fake, 4, 2, 6, fake, None) == 2
+    assert "H=6" in _err(lib)
+
+
+def test_binding_raises_without_library(tmp_path):
+    from quantized_expert_ffn_histogram_amd import _abi
+
+    with pytest.raises(RuntimeError, match="no CPU or PyTorch fallback"):
+        _abi.load(str(tmp_path / "missing.so"))

@@ -1,0 +1,253 @@
+"""GPU parity of every C-ABI call against the fp64 oracle.
+
+Routing ids, counts, offsets and the permutation are compared bit-exactly;
+routing weights to 1e-6; layer outputs to max|err| <= 2e-2 * RMS(ref) and
+sum|err| / sum|ref| <= 5e-3.  Small layers are compared element by element in
+full; the full-size layers on sampled tokens and sampled grouped rows, which
+the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from moe_testutil import W_ATOL, check_close, inputs, to_device
+
+pytestmark = pytest.mark.gpu
+
+FULL = ["tiny", "decode", "prefill512", "prefill6144", "zipf6144"]
+
+
+@pytest.fixture(scope="module")
+def qe(gpu_available):
+    import quantized_expert_ffn_histogram_amd as qe
+
+    qe.load()
+    return qe
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+# ----------------------------------------------------------------------------- route
+def _check_route(qe, logits_np, k):
+    import torch
+
+    ids, w = qe.route(torch.from_numpy(np.ascontiguousarray(logits_np, np.float32)).cuda(), k)
+    rid, rw = oracle.route(logits_np, k)
+    assert (_np(ids) == rid).all(), "routing ids differ from the oracle"
+    wg = _np(w).astype(np.float64)
+    assert np.abs(wg - rw).max() <= W_ATOL
+    assert np.abs(wg.sum(1) - 1.0).max() <= W_ATOL
+    return ids, w
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_route_bitexact(qe, name):
+    inp = inputs(name)
+    _check_route(qe, inp.logits, inp.cfg.k)
+
+
+@pytest.mark.parametrize(
+    "T,E,k,kind",
+    [
+        (64, 512, 10, "equal"),
+        (1000, 512, 10, "grid"),
+        (300, 256, 8, "grid_coarse"),
+        (50, 16, 4, "signed_zero"),
+        (37, 33, 5, "normal"),
+        (70, 100, 32, "grid"),
+        (45, 1000, 7, "grid"),
+        (20, 1024, 32, "normal"),
+        (9, 1, 1, "normal"),
+        (11, 32, 32, "grid"),
+        (3, 64, 1, "huge"),
+    ],
+)
+def test_route_ties_and_shapes(qe, T, E, k, kind):
+    rng = np.random.default_rng(T * 1000 + E + k)
+    z = rng.standard_normal((T, E))
+    if kind == "equal":
+        logits = np.full((T, E), 0.25)
+    elif kind == "grid":
+        logits = np.round(z * 4) / 4
+    elif kind == "grid_coarse":
+        logits = np.round(z)
+    elif kind == "signed_zero":
+        logits = np.where(rng.random((T, E)) < 0.5, -0.0, 0.0)
+        logits[:, ::5] = -1.0
+    elif kind == "huge":
+        logits = z * 1e30
+    else:
+        logits = z
+    _check_route(qe, logits.astype(np.float32), k)
+
+
+# ----------------------------------------------------------------------------- permute
+def _check_permute(qe, ids_np, E):
+    import torch
+
+    ids = torch.from_numpy(np.ascontiguousarray(ids_np, np.int32)).cuda()
+    counts, offsets, perm, inv = qe.permute(ids, E)
+    rc = oracle.histogram(ids_np, E)
+    ro = oracle.exclusive_scan(rc)
+    rp, ri = oracle.permutation(ids_np)
+    assert (_np(counts) == rc).all()
+    assert (_np(offsets) == ro).all()
+    assert (_np(perm) == rp).all()
+    assert (_np(inv) == ri).all()
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_permute_bitexact(qe, name):
+    inp = inputs(name)
+    ids, _ = oracle.route(inp.logits, inp.cfg.k)
+    _check_permute(qe, ids, inp.cfg.E)
+
+
+@pytest.mark.parametrize(
+    "T,E,k,kind",
+    [
+        (5000, 16, 1, "one_hot"),
+        (20000, 1024, 3, "random"),
+        (1, 8, 1, "random"),
+        (512, 512, 2, "random"),    # 1024 pairs: single-workgroup path, at its limit
+        (1025, 300, 1, "random"),   # 1025 pairs: segmented path, ragged last segment
+        (3001, 64, 7, "skewed"),
+        (2048, 1024, 1, "empty_half"),
+    ],
+)
+def test_permute_edge_cases(qe, T, E, k, kind):
+    rng = np.random.default_rng(T + E + k)
+    if kind == "one_hot":
+        ids = np.full((T, k), 3, np.int32)
+    elif kind == "skewed":
+        ids = np.minimum(rng.zipf(1.5, (T, k)) - 1, E - 1).astype(np.int32)
+    elif kind == "empty_half":
+        ids = (2 * rng.integers(0, E // 2, (T, k))).astype(np.int32)
+    else:
+        ids = rng.integers(0, E, (T, k)).astype(np.int32)
+    _check_permute(qe, ids, E)
+
+
+def test_zero_tokens(qe):
+    import torch
+
+    ids, w = qe.route(torch.zeros((0, 16), dtype=torch.float32, device="cuda"), 2)
+    assert ids.shape == (0, 2)
+    counts, offsets, perm, inv = qe.permute(ids, 16)
+    assert (_np(counts) == 0).all() and (_np(offsets) == 0).all()
+
+
+# ----------------------------------------------------------------------------- ffn, full compare
+SMALL_CFGS = [
+    synth.config("tiny"),
+    # several 128-row tiles per expert with ragged tails, several column slices
+    synth.MoEConfig("ragged64", T=400, H=512, I=256, E=4, k=2, g=64, seed=31),
+    synth.MoEConfig("ragged32", T=333, H=768, I=384, E=5, k=3, g=32, seed=32),
+    synth.MoEConfig("ragged128", T=260, H=1024, I=256, E=3, k=1, g=128, seed=33),
+    synth.MoEConfig("manyexperts", T=96, H=256, I=128, E=64, k=6, g=32, seed=34),
+]
+
+
+def _run_layer(qe, inp, fused):
+    logits, x, ex = to_device(inp)
+    return qe.moe_layer(logits, x, ex, inp.cfg.k, fused=fused)
+
+
+@pytest.mark.parametrize("path", ["gemm", "auto"])
+@pytest.mark.parametrize("cfg", SMALL_CFGS, ids=lambda c: c.name)
+def test_ffn_full_compare(qe, cfg, path, monkeypatch):
+    monkeypatch.setenv("STRATA_MOE_FFN_PATH", path)
+    inp = inputs(cfg)
+    ref = oracle.moe_layer(inp.logits, inp.x_bf16, inp.weights, cfg.k, cfg.g)
+    det = _run_layer(qe, inp, fused=False)
+    check_close(_np(det["y"]), ref["y"], "y")
+    check_close(_np(det["out"]), ref["out"], "out (deterministic)")
+    fus = _run_layer(qe, inp, fused=True)
+    check_close(_np(fus["out"]), ref["out"], "out (fused)")
+
+
+GEMV_CFGS = [
+    synth.MoEConfig("gemv_tiny", T=16, H=256, I=128, E=16, k=2, g=32, seed=41),
+    synth.MoEConfig("gemv_t1", T=1, H=2048, I=512, E=64, k=10, g=64, seed=42),
+    synth.MoEConfig("gemv_wide", T=8, H=4096, I=1024, E=32, k=8, g=128, seed=43),
+    synth.MoEConfig("gemv_shared", T=12, H=1024, I=256, E=4, k=3, g=64, seed=44),
+]
+
+
+@pytest.mark.parametrize("path", ["gemv", "gemm"])
+@pytest.mark.parametrize("cfg", GEMV_CFGS, ids=lambda c: c.name)
+def test_ffn_decode_paths(qe, cfg, path, monkeypatch):
+    monkeypatch.setenv("STRATA_MOE_FFN_PATH", path)
+    inp = inputs(cfg)
+    ref = oracle.moe_layer(inp.logits, inp.x_bf16, inp.weights, cfg.k, cfg.g)
+    det = _run_layer(qe, inp, fused=False)
+    check_close(_np(det["y"]), ref["y"], "y")
+    fus = _run_layer(qe, inp, fused=True)
+    check_close(_np(fus["out"]), ref["out"], "out (fused)")
+
+
+# ----------------------------------------------------------------------------- ffn, full-size sampled
+def _sample_tokens(T, n, seed):
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(T, size=min(n, T), replace=False).tolist()) | {0, T - 1}
+    return np.array(sorted(pick))
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill512", "prefill6144", "zipf6144"])
+def test_ffn_full_size_sampled_tokens(qe, name):
+    inp = inputs(name)
+    cfg = inp.cfg
+    res = _run_layer(qe, inp, fused=True)
+    ids, w = oracle.route(inp.logits, cfg.k)
+    assert (_np(res["ids"]) == ids).all()
+    toks = _sample_tokens(cfg.T, 10, cfg.seed)
+    ref = oracle.moe_out_tokens(toks, ids, w, inp.x_bf16, inp.weights, cfg.g)
+    check_close(_np(res["out"])[toks], ref, f"{name} out[sampled tokens]")
+
+
+@pytest.mark.parametrize("name", ["prefill6144", "zipf6144"])
+def test_ffn_full_size_sampled_grouped_rows(qe, name):
+    """Deterministic path: grouped rows y[i] of the busiest expert (many tiles,
+    ragged last tile) and of a median expert, against the oracle row by row."""
+    inp = inputs(name)
+    cfg = inp.cfg
+    res = _run_layer(qe, inp, fused=False)
+    ids, _ = oracle.route(inp.logits, cfg.k)
+    counts = oracle.histogram(ids, cfg.E)
+    offsets = oracle.exclusive_scan(counts)
+    perm, _ = oracle.permutation(ids)
+    y = _np(res["y"])
+    nz = np.nonzero(counts)[0]
+    busiest = int(np.argmax(counts))
+    median = int(nz[np.argsort(counts[nz])[len(nz) // 2]])
+    x = oracle.bf16_to_f64(inp.x_bf16)
+    for e in (busiest, median):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        rows = np.unique(np.concatenate([np.arange(lo, min(hi, lo + 40)), np.arange(max(lo, hi - 40), hi)]))
+        W = [oracle.dequant(inp.weights[m][e], inp.weights[m + "_scale"][e], cfg.g) for m in ("gate", "up", "down")]
+        ref = oracle.expert_ffn(x[perm[rows] // cfg.k], *W)
+        check_close(y[rows], ref, f"{name} y rows of expert {e} ({hi - lo} rows)")
+
+
+# ----------------------------------------------------------------------------- determinism
+def test_deterministic_path_is_bitwise_repeatable(qe):
+    inp = inputs(SMALL_CFGS[1])
+    a = _run_layer(qe, inp, fused=False)
+    b = _run_layer(qe, inp, fused=False)
+    for key in ("ids", "w", "counts", "offsets", "perm", "inv_perm", "y", "out"):
+        assert (_np(a[key]) == _np(b[key])).all(), key
+
+
+def test_one_hot_routing_layer(qe):
+    """Every token routed to the same k experts: k experts with T rows each."""
+    cfg = synth.MoEConfig("onehot", T=700, H=512, I=256, E=8, k=2, g=64, seed=51)
+    inp = synth.make_inputs(cfg)
+    inp.logits[:, 5] += 50.0
+    inp.logits[:, 2] += 40.0
+    ref = oracle.moe_layer(inp.logits, inp.x_bf16, inp.weights, cfg.k, cfg.g)
+    assert ref["counts"][5] == 700 and ref["counts"][2] == 700
+    res = _run_layer(qe, inp, fused=True)
+    check_close(_np(res["out"]), ref["out"], "one-hot out")
