@@ -149,7 +149,7 @@ def bench_prefill(qe, args):
     logits = torch.from_numpy(inp.logits).to(dev)
     x = torch.from_numpy(inp.x_bf16.view(np.int16)).to(dev).view(torch.bfloat16)
     experts = qe.QuantizedExperts.from_numpy(inp.weights, cfg.g, dev)
-    run = qe.LayerRunner(experts, cfg.T, cfg.E, cfg.k, fused=True, device=dev)
+    run = qe.LayerRunner(experts, cfg.T, cfg.E, cfg.k, fused=bool(args.fused), device=dev)
 
     for _ in range(args.warmup):
         run(logits, x)
@@ -251,6 +251,9 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default="prefill6144")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fused", type=int, default=1, help="1: fused weighted scatter-add; 0: y rows + combine")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -266,6 +269,14 @@ def main(argv=None) -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     qe.load()
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration: 3 copies of 1 GiB (read 1 GiB + write 1 GiB each)")
+        del src, dst
 
     cfg, inp, secs, secs_timed, roof, kernels = bench_prefill(qe, args)
     result = {

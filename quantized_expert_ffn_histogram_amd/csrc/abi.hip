@@ -9,7 +9,7 @@
 #include <cstring>
 #include <string>
 
-#include "../../include/strata_moe.h"
+#include "strata_moe.h"
 #include "moe_internal.h"
 
 namespace strata {
@@ -93,28 +93,32 @@ bool ffn_path_env_valid() {
 
 namespace strata {
 
-size_t ffn_workspace_bytes(long long pairs, int E, int H, int I) {
-  (void)H;
-  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
-  const long long tiles_gemm = (pairs + kGemmRows - 1) / kGemmRows + std::min<long long>(E, pairs);
-  const long long tiles_gemv = (pairs + kGemvRows - 1) / kGemvRows + std::min<long long>(E, pairs);
-  const long long tiles = std::max(tiles_gemm, tiles_gemv) + 1;
-  return up((size_t)pairs * I * 2) + up((size_t)tiles * sizeof(Tile)) + 256;
+namespace {
+size_t up256(size_t b) { return (b + 255) / 256 * 256; }
+long long max_tiles(long long pairs, int E) {
+  const long long gemm = (pairs + kGemmRows - 1) / kGemmRows + std::min<long long>(E, pairs);
+  const long long gemv = (pairs + kGemvRows - 1) / kGemvRows + std::min<long long>(E, pairs);
+  return std::max(gemm, gemv) + 1;
+}
+}  // namespace
+
+size_t ffn_workspace_bytes(long long T, int k, int E, int H, int I) {
+  const long long pairs = T * k;
+  return up256((size_t)T * H * 2) + up256((size_t)pairs * I * 2) + up256((size_t)max_tiles(pairs, E) * sizeof(Tile)) + 256;
 }
 
-FfnWorkspace carve_ffn_workspace(void *base, long long pairs, int E, int H, int I) {
-  auto up = [](size_t b) { return (b + 255) / 256 * 256; };
+FfnWorkspace carve_ffn_workspace(void *base, long long T, int k, int E, int H, int I) {
+  const long long pairs = T * k;
   char *p = static_cast<char *>(base);
   FfnWorkspace w{};
+  w.xq = reinterpret_cast<uint16_t *>(p);
+  p += up256((size_t)T * H * 2);
   w.h = reinterpret_cast<uint16_t *>(p);
-  p += up((size_t)pairs * I * 2);
-  const long long tiles_gemm = (pairs + kGemmRows - 1) / kGemmRows + std::min<long long>(E, pairs);
-  const long long tiles_gemv = (pairs + kGemvRows - 1) / kGemvRows + std::min<long long>(E, pairs);
-  const long long tiles = std::max(tiles_gemm, tiles_gemv) + 1;
+  p += up256((size_t)pairs * I * 2);
   w.tiles = reinterpret_cast<Tile *>(p);
-  p += up((size_t)tiles * sizeof(Tile));
+  p += up256((size_t)max_tiles(pairs, E) * sizeof(Tile));
   w.meta = reinterpret_cast<int *>(p);
-  w.bytes = ffn_workspace_bytes(pairs, E, H, I);
+  w.bytes = ffn_workspace_bytes(T, k, E, H, I);
   return w;
 }
 
@@ -128,7 +132,7 @@ size_t strata_moe_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int
   if (check_tek("strata_moe_workspace_size", T, E, k) != STRATA_OK) return 0;
   if (check_shape("strata_moe_workspace_size", H, I, g) != STRATA_OK) return 0;
   const long long pairs = (long long)T * k;
-  return std::max(permute_workspace_bytes(pairs, E), ffn_workspace_bytes(pairs, E, H, I));
+  return std::max(permute_workspace_bytes(pairs, E), ffn_workspace_bytes(T, k, E, H, I));
 }
 
 int strata_moe_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *topk_ids,
@@ -195,8 +199,7 @@ int strata_moe_ffn(const uint16_t *x_bf16, int32_t T, int32_t k, const strata_mo
   if (topk_w != nullptr && !aligned16(topk_w))
     return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "topk_w=%p is not 16-byte aligned", (const void *)topk_w);
   const int E = w->num_experts, H = w->hidden, I = w->inter, g = w->group;
-  const long long pairs = (long long)T * k;
-  const size_t need = ffn_workspace_bytes(pairs, E, H, I);
+  const size_t need = ffn_workspace_bytes(T, k, E, H, I);
   if (workspace == nullptr)
     return fail(STRATA_ERR_WORKSPACE, fn, "workspace is NULL but %zu bytes are required", need);
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
@@ -214,7 +217,7 @@ int strata_moe_ffn(const uint16_t *x_bf16, int32_t T, int32_t k, const strata_mo
   const bool use_gemv = forced == FfnPath::Gemv || (forced == FfnPath::Auto && gemv_ok);
 
   FfnWeights fw{w->gate, w->up, w->down, w->gate_scale, w->up_scale, w->down_scale, E, H, I, g};
-  const FfnWorkspace ws = carve_ffn_workspace(workspace, pairs, E, H, I);
+  const FfnWorkspace ws = carve_ffn_workspace(workspace, T, k, E, H, I);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = use_gemv ? launch_ffn_gemv(x_bf16, T, k, fw, offsets, perm, topk_w, y_or_out, ws, s)
                                 : launch_ffn_gemm(x_bf16, T, k, fw, offsets, perm, topk_w, y_or_out, ws, s);

@@ -32,6 +32,8 @@
 // XCDs round-robin by block index; each XCD gets a contiguous range of
 // (tile, slice) work items so that the slices of one tile (which share its A
 // rows) run on the same XCD and hit its L2.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace strata {
@@ -43,10 +45,11 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kXcds = 8;
 constexpr int kMB = kGemmRows / 32;            // 32-row MFMA blocks per tile
-constexpr int kLdsLd = kGemmKChunk + 8;        // fp16 per LDS row (pad breaks bank aliasing)
+constexpr int kKC = kGemmKChunk;               // K per pipelined chunk
+constexpr int kSegs = kKC / 8;                 // 16-byte segments per A row per chunk
 
 struct GemmArgs {
-  const void *A;          // gate/up: x bf16 [T][K]; down: h fp16 [pairs][K]
+  const uint16_t *A;      // fp16 rows in fragment slot order: gate/up: x [T][K]; down: h [pairs][K]
   const uint8_t *B0;      // gate or down, packed [E][N][K/2]
   const uint16_t *S0;     // fp16 scales [E][N][K/g]
   const uint8_t *B1;      // up (gate/up only)
@@ -57,7 +60,7 @@ struct GemmArgs {
   const float *topk_w;    // down, fused: routing weight per pair
   const Tile *tiles;
   const int *meta;        // meta[0] = number of tiles
-  void *C;                // gate/up: h fp16 [pairs][N]; down: out [T][N] or y [pairs][N] (fp32)
+  void *C;                // gate/up: h fp16 [pairs][N] (slot order); down: out [T][N] or y [pairs][N] (fp32)
   int nslices;
   int fused;
 };
@@ -75,8 +78,7 @@ __device__ __forceinline__ half8 dequant8(uint32_t d, half2_t s2) {
   return half8{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
 }
 
-__device__ __forceinline__ uint32_t dword_of(const uint4 (&r)[2], int j) {
-  const uint4 v = r[j >> 2];
+__device__ __forceinline__ uint32_t dword_of(const uint4 v, int j) {
   switch (j & 3) {
     case 0: return v.x;
     case 1: return v.y;
@@ -85,37 +87,220 @@ __device__ __forceinline__ uint32_t dword_of(const uint4 (&r)[2], int j) {
   }
 }
 
-// 8 bf16 (natural K order) -> 8 fp16 in fragment slot order (0,4,1,5,2,6,3,7).
-__device__ __forceinline__ uint4 bf16x8_to_f16_slots(uint4 v) {
-  auto lo = [](uint32_t d) { return __uint_as_float(d << 16); };
-  auto hi = [](uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); };
-  uint4 o;
-  o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo(v.x), lo(v.z)));
-  o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi(v.x), hi(v.z)));
-  o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo(v.y), lo(v.w)));
-  o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi(v.y), hi(v.w)));
-  return o;
+// LDS position (in 16-byte units) of logical segment c of tile row r: the XOR
+// spreads the 8 rows that one 8-lane group of a ds_read_b128 touches over all
+// bank quads.
+__device__ __forceinline__ int a_slot(int r, int c) { return r * kSegs + (c ^ (r & 7)); }
+
+// Position of column n inside a row stored in fragment slot order.
+__device__ __forceinline__ int slot_pos(int n) { return (n & ~7) | (((n & 3) << 1) | ((n >> 2) & 1)); }
+
+struct RowTables {
+  int src[kGemmRows];    // gate/up: token row of x; down: grouped row of h
+  int tok[kGemmRows];    // down: output row (token)
+  float wt[kGemmRows];   // down, fused: routing weight
+};
+
+constexpr int kStages = 4;                         // LDS ring depth (prefetch distance kStages-1)
+constexpr int kStageSegs = kGemmRows * kSegs;      // 16-byte A segments per stage
+
+// Wait until at most N vector-memory operations of this wavefront are
+// outstanding (expcnt and lgkmcnt left unconstrained), N < 64.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
 }
 
-// 8 fp16 (natural K order) -> fragment slot order (0,4,1,5,2,6,3,7).
-__device__ __forceinline__ uint4 f16x8_to_slots(uint4 v) {
-  uint4 o;
-  o.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);
-  o.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);
-  o.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);
-  o.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);
-  return o;
+// Compiler-only memory barrier: keeps loads, DMA issues and LDS reads on
+// their side of the waits and barriers below.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// One pipeline stage in LDS: a K chunk of the tile's A rows, the packed
+// weights of the workgroup's 256 B-matrix rows and their scales.
+struct Stage {
+  uint4 a[kStageSegs];          // [row][segment], XOR-swizzled (a_slot)
+  uint4 b[2 * 256];             // [B row][lane half] 16 bytes = 32 K values
+  uint32_t s[2 * 256];          // [B row][lane half] fp16 group scale in the low half
+};
+
+// Direct-to-LDS loads take an LDS-address-space pointer; the cast makes the
+// conversion from the generic pointer of a __shared__ object explicit.
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+__device__ __forceinline__ lds_ptr_t as_lds(void *p) { return (lds_ptr_t)p; }
+
+// B-matrix row of the workgroup held by wavefront `wave`, column block nb, lane column col.
+__device__ __forceinline__ int brow_of(int wave, int nb, int col) { return wave * 64 + nb * 32 + col; }
+
+// One K chunk of MFMAs from one stage: NMB row blocks x 2 column blocks x 4 K-steps.
+template <int NMB>
+__device__ __forceinline__ void mma_chunk(floatx16 (&acc)[NMB][2], const Stage &st, int wave, int col, int half) {
+  uint4 bw[2];
+  half2_t s2[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int br = brow_of(wave, nb, col);
+    bw[nb] = st.b[br * 2 + half];
+    const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)st.s[br * 2 + half]);
+    s2[nb] = half2_t{sv, sv};
+  }
+  // A fragments are read one K-step ahead of the MFMAs that use them.
+  half8 af[2][NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) af[0][mb] = __builtin_bit_cast(half8, st.a[a_slot(mb * 32 + col, 4 * half)]);
+#pragma unroll
+  for (int j = 0; j < kKC / 16; ++j) {
+    if (j + 1 < kKC / 16) {
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+        af[(j + 1) & 1][mb] = __builtin_bit_cast(half8, st.a[a_slot(mb * 32 + col, 4 * half + j + 1)]);
+    }
+    half8 bf[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) bf[nb] = dequant8(dword_of(bw[nb], j), s2[nb]);
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[j & 1][mb], bf[nb], acc[mb][nb], 0, 0, 0);
+  }
+}
+
+// Four stages as distinct LDS objects: the compiler then tracks each
+// stage's direct-to-LDS loads separately instead of waiting for all of them.
+struct Ring {
+  Stage *st[kStages];
+};
+
+template <int S>
+__device__ __forceinline__ Stage &stage_ref(const Ring &R) { return *R.st[S]; }
+
+// One work item: the tile's rows (NMB 32-row blocks, nrows valid) x this
+// workgroup's column slice, over all of K.  Every operand moves global -> LDS
+// with direct-to-LDS loads (no registers), kStages-1 chunks ahead:
+//   * A (token rows, fp16 slot order): wavefront instruction i fills
+//     segments [(4i + wave)*64, +64), i.e. 8 rows x 128 bytes, written in the
+//     XOR-swizzled layout;
+//   * packed weights: 32 B-rows x 32 bytes per instruction;
+//   * scales: 32 B-rows x 2 halves per instruction (a 2-byte direct-to-LDS
+//     load writes one zero-extended dword per lane).
+// Per chunk: wait for this wavefront's loads of the chunk, one barrier (all
+// wavefronts' loads of the chunk have landed; the oldest stage is free), issue
+// chunk c+3 into it, then dequant + MFMAs.  Past the last chunk the issue
+// repeats the last chunk (loads are never skipped), so every wait counts the
+// same number of operations.
+template <int MODE, int NMB>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &a, const Ring &R, const RowTables &rt, int e, int row0,
+                                          int nrows, int slice) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 31, half = lane >> 5;
+  const int nchunks = a.K / kKC;
+  constexpr int V = NMB + 4;  // direct-to-LDS loads per stage per wavefront
+
+  uint32_t aoff[NMB];
+#pragma unroll
+  for (int i = 0; i < NMB; ++i) {
+    const int p = (4 * i + wave) * 64 + lane;
+    const int r = p >> 3, c = (p & 7) ^ (r & 7);
+    aoff[i] = (uint32_t)rt.src[r] * (uint32_t)a.K + 8 * c;
+  }
+  // Loads of B rows: lane -> (row col2 = lane>>1 of the 32-row block, half hh = lane&1).
+  const int col2 = lane >> 1, hh = lane & 1;
+  const uint8_t *bsrc[2];
+  const uint16_t *ssrc[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int n = MODE == 0 ? slice * kGateUpColsPerWG + wave * 32 + col2
+                            : slice * kDownColsPerWG + wave * 64 + nb * 32 + col2;
+    const uint8_t *B = (MODE == 0 && nb == 1) ? a.B1 : a.B0;
+    const uint16_t *Sc = (MODE == 0 && nb == 1) ? a.S1 : a.S0;
+    bsrc[nb] = B + ((size_t)e * a.N + n) * (a.K / 2) + 16 * hh;
+    ssrc[nb] = Sc + ((size_t)e * a.N + n) * (a.K / a.g);
+  }
+  const int g_shift = 31 - __clz(a.g);  // g is a power of two
+
+  auto issue = [&](Stage &st, int c) {
+    const int kc = c * kKC;
+#pragma unroll
+    for (int i = 0; i < NMB; ++i)
+      __builtin_amdgcn_global_load_lds(a.A + aoff[i] + kc, as_lds(&st.a[(4 * i + wave) * 64]), 16, 0, 0);
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int base = brow_of(wave, nb, 0) * 2;
+      __builtin_amdgcn_global_load_lds(bsrc[nb] + kc / 2, as_lds(&st.b[base]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(ssrc[nb] + ((kc + 32 * hh) >> g_shift), as_lds(&st.s[base]), 2, 0, 0);
+    }
+  };
+
+  floatx16 acc[NMB][2];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = floatx16{};
+
+  const int last = nchunks - 1;
+  compiler_fence();
+  issue(stage_ref<0>(R), 0);
+  issue(stage_ref<1>(R), min(1, last));
+  issue(stage_ref<2>(R), min(2, last));
+
+  auto step = [&](auto stage_tag, int c) {
+    constexpr int S = decltype(stage_tag)::value;
+    compiler_fence();
+    wait_vmcnt<2 * V>();            // this wavefront's loads of chunk c are done
+    __builtin_amdgcn_s_barrier();  // ... and every other wavefront's; stage S-1 is free
+    compiler_fence();
+    issue(stage_ref<(S + 3) % kStages>(R), min(c + 3, last));
+    compiler_fence();
+    if (c < nchunks) mma_chunk<NMB>(acc, stage_ref<S>(R), wave, col, half);
+  };
+
+  for (int c0 = 0; c0 < nchunks; c0 += kStages) {
+    step(std::integral_constant<int, 0>{}, c0);
+    step(std::integral_constant<int, 1>{}, c0 + 1);
+    step(std::integral_constant<int, 2>{}, c0 + 2);
+    step(std::integral_constant<int, 3>{}, c0 + 3);
+  }
+  compiler_fence();
+  wait_vmcnt<0>();  // no load of this tile may land in the next tile's stages
+  compiler_fence();
+
+  // Epilogue.  Accumulator element v of a lane: row 8*(v/4) + 4*half + v%4, column col.
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int r = mb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
+      if (r >= nrows) continue;
+      if (MODE == 0) {
+        const int n = slice * kGateUpColsPerWG + wave * 32 + col;
+        const float gv = acc[mb][0][v], uv = acc[mb][1][v];
+        const float hv = gv / (1.0f + __expf(-gv)) * uv;
+        _Float16 *hout = static_cast<_Float16 *>(a.C);
+        hout[(size_t)(row0 + r) * a.N + slot_pos(n)] = (_Float16)hv;
+      } else {
+        float *outp = static_cast<float *>(a.C);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const int n = slice * kDownColsPerWG + wave * 64 + nb * 32 + col;
+          const float yv = acc[mb][nb][v];
+          if (a.fused)
+            unsafeAtomicAdd(outp + (size_t)rt.tok[r] * a.N + n, rt.wt[r] * yv);
+          else
+            outp[(size_t)(row0 + r) * a.N + n] = yv;
+        }
+      }
+    }
+  }
 }
 
 template <int MODE>  // 0: gate/up + silu*mul -> h;  1: down + weighted combine
-__global__ __launch_bounds__(256, 2) void moe_gemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 As[kGemmRows * kLdsLd];
-  __shared__ int rtok[kGemmRows];
-  __shared__ float rwt[kGemmRows];
+__global__ __launch_bounds__(256, 1) void moe_gemm_kernel(GemmArgs a) {
+  __shared__ Stage st0, st1, st2, st3;
+  __shared__ RowTables rt;
+  const Ring R{{&st0, &st1, &st2, &st3}};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 31, half = lane >> 5;
-
+  const int tid = threadIdx.x;
   const int total = a.meta[0] * a.nslices;
   const int xcd = blockIdx.x % kXcds, lb = blockIdx.x / kXcds, per_xcd_wgs = gridDim.x / kXcds;
   const int base = total / kXcds, rem = total % kXcds;
@@ -123,133 +308,52 @@ __global__ __launch_bounds__(256, 2) void moe_gemm_kernel(GemmArgs a) {
   const int start = xcd * base + min(xcd, rem);
 
   for (int local = lb; local < cnt; local += per_xcd_wgs) {
-    const int L = start + local;
-    const int entry = L / a.nslices, slice = L - entry * a.nslices;
+    const int Lw = start + local;
+    const int entry = Lw / a.nslices, slice = Lw - entry * a.nslices;
     const Tile tile = a.tiles[entry];
-    const int e = tile.e, row0 = tile.row0, nrows = tile.rows;
-    const int nmb = (nrows + 31) >> 5;
+    const int nmb = (tile.rows + 31) >> 5;
 
-    __syncthreads();  // previous work item finished with LDS
+    __syncthreads();  // previous work item is done with LDS and the row tables
     if (tid < kGemmRows) {
-      int tok = 0;
-      float wt = 0.0f;
-      if (tid < nrows) {
-        const int p = a.perm[row0 + tid];
-        tok = p / a.k;
-        if (MODE == 1 && a.fused) wt = a.topk_w[p];
-      }
-      rtok[tid] = tok;
-      rwt[tid] = wt;
-    }
-
-    const uint8_t *bp[2];
-    const uint16_t *sp[2];
-    int ncol[2];
-    if (MODE == 0) {
-      const int n = slice * kGateUpColsPerWG + wave * 32 + col;
-      ncol[0] = ncol[1] = n;
-      bp[0] = a.B0 + ((size_t)e * a.N + n) * (a.K / 2);
-      bp[1] = a.B1 + ((size_t)e * a.N + n) * (a.K / 2);
-      sp[0] = a.S0 + ((size_t)e * a.N + n) * (a.K / a.g);
-      sp[1] = a.S1 + ((size_t)e * a.N + n) * (a.K / a.g);
-    } else {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int n = slice * kDownColsPerWG + wave * 64 + nb * 32 + col;
-        ncol[nb] = n;
-        bp[nb] = a.B0 + ((size_t)e * a.N + n) * (a.K / 2);
-        sp[nb] = a.S0 + ((size_t)e * a.N + n) * (a.K / a.g);
+      const int r = tid < tile.rows ? tid : 0;  // padding rows repeat row 0 (results dropped)
+      const int p = a.perm[tile.row0 + r];
+      if (MODE == 0) {
+        rt.src[tid] = p / a.k;
+      } else {
+        rt.src[tid] = tile.row0 + r;
+        rt.tok[tid] = p / a.k;
+        rt.wt[tid] = a.fused ? a.topk_w[p] : 0.0f;
       }
     }
-
-    floatx16 acc[kMB][2];
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = floatx16{};
-
-    for (int kc = 0; kc < a.K; kc += kGemmKChunk) {
-      // Weights: this lane's 64 K values [kc + 64*half, +64) of its row = 32 bytes.
-      uint4 raw[2][2];
-      half2_t sA[2], sB[2];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(bp[nb] + kc / 2 + half * 32);
-        raw[nb][0] = src[0];
-        raw[nb][1] = src[1];
-        const int k0 = kc + 64 * half;
-        const _Float16 s0 = __builtin_bit_cast(_Float16, sp[nb][k0 / a.g]);
-        const _Float16 s1 = __builtin_bit_cast(_Float16, sp[nb][(k0 + 32) / a.g]);
-        sA[nb] = half2_t{s0, s0};
-        sB[nb] = half2_t{s1, s1};
-      }
-
-      __syncthreads();  // LDS free (previous chunk read) and row table visible
-      // Stage A rows [0,128) x K [kc, kc+128) as fp16 in slot order.
-#pragma unroll
-      for (int i = 0; i < (kGemmRows * kGemmKChunk / 8) / 256; ++i) {
-        const int seg = tid + 256 * i;
-        const int r = seg >> 4, c8 = seg & 15;
-        uint4 v = {0u, 0u, 0u, 0u};
-        if (r < nrows) {
-          if (MODE == 0) {
-            const uint16_t *x = static_cast<const uint16_t *>(a.A);
-            v = *reinterpret_cast<const uint4 *>(x + (size_t)rtok[r] * a.K + kc + 8 * c8);
-            v = bf16x8_to_f16_slots(v);
-          } else {
-            const uint16_t *h = static_cast<const uint16_t *>(a.A);
-            v = *reinterpret_cast<const uint4 *>(h + (size_t)(row0 + r) * a.K + kc + 8 * c8);
-            v = f16x8_to_slots(v);
-          }
-        }
-        *reinterpret_cast<uint4 *>(&As[r * kLdsLd + 8 * c8]) = v;
-      }
-      __syncthreads();
-
-#pragma unroll
-      for (int j = 0; j < kGemmKChunk / 16; ++j) {
-        half8 bf[2];
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) bf[nb] = dequant8(dword_of(raw[nb], j), j < 4 ? sA[nb] : sB[nb]);
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) {
-          if (mb < nmb) {
-            const half8 af = *reinterpret_cast<const half8 *>(&As[(mb * 32 + col) * kLdsLd + 64 * half + 8 * j]);
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb)
-              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[nb], acc[mb][nb], 0, 0, 0);
-          }
-        }
-      }
-    }
-
-    // Epilogue.  Accumulator element v of a lane: row 8*(v/4) + 4*half + v%4, column `col`.
-#pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) {
-      if (mb >= nmb) continue;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int r = mb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-        if (r >= nrows) continue;
-        if (MODE == 0) {
-          const float gv = acc[mb][0][v], uv = acc[mb][1][v];
-          const float hv = gv / (1.0f + __expf(-gv)) * uv;
-          _Float16 *hout = static_cast<_Float16 *>(a.C);
-          hout[(size_t)(row0 + r) * a.N + ncol[0]] = (_Float16)hv;
-        } else {
-          float *outp = static_cast<float *>(a.C);
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            const float yv = acc[mb][nb][v];
-            if (a.fused)
-              unsafeAtomicAdd(outp + (size_t)rtok[r] * a.N + ncol[nb], rwt[r] * yv);
-            else
-              outp[(size_t)(row0 + r) * a.N + ncol[nb]] = yv;
-          }
-        }
-      }
+    __syncthreads();
+    switch (nmb) {
+      case 1: gemm_tile<MODE, 1>(a, R, rt, tile.e, tile.row0, tile.rows, slice); break;
+      case 2: gemm_tile<MODE, 2>(a, R, rt, tile.e, tile.row0, tile.rows, slice); break;
+      case 3: gemm_tile<MODE, 3>(a, R, rt, tile.e, tile.row0, tile.rows, slice); break;
+      default: gemm_tile<MODE, 4>(a, R, rt, tile.e, tile.row0, tile.rows, slice); break;
     }
   }
+}
+
+// Prologue of the GEMM path: x (bf16) -> fp16 in fragment slot order, and the
+// fused output cleared.  Grid-stride over 8-element groups.
+__global__ __launch_bounds__(256) void prep_kernel(const uint4 *__restrict__ x, uint4 *__restrict__ xq,
+                                                   size_t n8, float4 *__restrict__ out, size_t n_out4) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n8; i += stride) {
+    const uint4 v = x[i];
+    auto lo = [](uint32_t d) { return __uint_as_float(d << 16); };
+    auto hi = [](uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); };
+    uint4 o;
+    o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo(v.x), lo(v.z)));
+    o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi(v.x), hi(v.z)));
+    o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo(v.y), lo(v.w)));
+    o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi(v.y), hi(v.w)));
+    xq[i] = o;
+  }
+  if (out)
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n_out4; i += stride)
+      out[i] = float4{0.f, 0.f, 0.f, 0.f};
 }
 
 __global__ __launch_bounds__(1024) void plan_kernel(const int *__restrict__ offsets, int E,
@@ -280,14 +384,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int *__restrict__ offs
   if (e == 1023) meta[0] = part[1023];
 }
 
-__global__ void zero_kernel(float4 *p, size_t n4) {
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x)
-    p[i] = float4{0.f, 0.f, 0.f, 0.f};
-}
-
-// Persistent grid: at most two workgroups per CU (256 CUs), whole XCD rounds.
+// Persistent grid: one workgroup per CU (256 CUs), whole XCD rounds.
 int persistent_grid(long long work_upper) {
-  long long g = work_upper < 512 ? work_upper : 512;
+  long long g = work_upper < 256 ? work_upper : 256;
   g = (g + kXcds - 1) / kXcds * kXcds;
   return (int)(g < kXcds ? kXcds : g);
 }
@@ -301,14 +400,6 @@ hipError_t launch_plan(const int *offsets, int E, int rows_per_tile, Tile *tiles
   return hipGetLastError();
 }
 
-hipError_t launch_zero(float *p, size_t n, hipStream_t s) {
-  const size_t n4 = n / 4;
-  const int blocks = (int)std::min<size_t>(2048, (n4 + 255) / 256);
-  KernelTimer timer("zero_out", s);
-  if (blocks > 0) zero_kernel<<<blocks, 256, 0, s>>>(reinterpret_cast<float4 *>(p), n4);
-  return hipGetLastError();
-}
-
 hipError_t launch_ffn_gemm(const uint16_t *x, int T, int k, const FfnWeights &w, const int *offsets,
                            const int *perm, const float *topk_w, float *y_or_out,
                            const FfnWorkspace &ws, hipStream_t s) {
@@ -317,8 +408,19 @@ hipError_t launch_ffn_gemm(const uint16_t *x, int T, int k, const FfnWeights &w,
   hipError_t err = launch_plan(offsets, w.E, kGemmRows, ws.tiles, ws.meta, s);
   if (err != hipSuccess) return err;
 
+  const bool fused = topk_w != nullptr;
+  {
+    KernelTimer timer("ffn_prep", s);
+    const size_t n8 = (size_t)T * w.H / 8;
+    const int blocks = (int)std::min<size_t>(4096, (n8 + 255) / 256);
+    prep_kernel<<<blocks, 256, 0, s>>>(reinterpret_cast<const uint4 *>(x), reinterpret_cast<uint4 *>(ws.xq), n8,
+                                       fused ? reinterpret_cast<float4 *>(y_or_out) : nullptr,
+                                       fused ? (size_t)T * w.H / 4 : 0);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+  }
+
   GemmArgs g{};
-  g.A = x;
+  g.A = ws.xq;
   g.B0 = w.gate;
   g.S0 = w.gate_s;
   g.B1 = w.up;
@@ -340,8 +442,6 @@ hipError_t launch_ffn_gemm(const uint16_t *x, int T, int k, const FfnWeights &w,
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
 
-  const bool fused = topk_w != nullptr;
-  if (fused && (err = launch_zero(y_or_out, (size_t)T * w.H, s)) != hipSuccess) return err;
   GemmArgs d = g;
   d.A = ws.h;
   d.B0 = w.down;

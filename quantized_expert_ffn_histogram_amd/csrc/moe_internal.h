@@ -20,7 +20,7 @@ constexpr int kPermuteSmallMax = 1024;
 
 // Grouped GEMM tiling (rows of one expert per tile, K per LDS chunk).
 constexpr int kGemmRows = 128;
-constexpr int kGemmKChunk = 128;
+constexpr int kGemmKChunk = 64;
 constexpr int kGateUpColsPerWG = 128;     // h columns per workgroup (gate+up: 256 B rows)
 constexpr int kDownColsPerWG = 256;       // output columns per workgroup
 
@@ -53,13 +53,14 @@ hipError_t launch_permute(const int *ids, int pairs, int E, int *counts, int *of
 
 // Workspace carving for the FFN (h, tile list, counters).
 struct FfnWorkspace {
+  uint16_t *xq;      // fp16 [T][H], fragment slot order (GEMM path)
   uint16_t *h;       // fp16 [pairs][I]
   Tile *tiles;       // grouped-work list
   int *meta;         // meta[0] = number of tiles
   size_t bytes;
 };
-size_t ffn_workspace_bytes(long long pairs, int E, int H, int I);
-FfnWorkspace carve_ffn_workspace(void *base, long long pairs, int E, int H, int I);
+size_t ffn_workspace_bytes(long long T, int k, int E, int H, int I);
+FfnWorkspace carve_ffn_workspace(void *base, long long T, int k, int E, int H, int I);
 
 hipError_t launch_ffn_gemm(const uint16_t *x, int T, int k, const FfnWeights &w,
                            const int *offsets, const int *perm, const float *topk_w,
@@ -72,9 +73,55 @@ hipError_t launch_combine(const float *y, const int *inv_perm, const float *topk
                           int k, int H, float *out, hipStream_t s);
 hipError_t launch_plan(const int *offsets, int E, int rows_per_tile, Tile *tiles, int *meta,
                        hipStream_t s);
-hipError_t launch_zero(float *p, size_t n, hipStream_t s);
 
 inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// ---------------------------------------------------------------- wavefront reductions
+// Reduce within each row of 16 lanes with DPP (quad_perm [1,0,3,2], [2,3,0,1],
+// row_ror 4, row_ror 8), then combine the four row results read from lanes
+// 0, 16, 32, 48.  The result is wavefront-uniform and its order of operations
+// is fixed.
+#define STRATA_DPP_ROW_REDUCE(v, OP, T)                                                           \
+  do {                                                                                            \
+    v = OP(v, (T)__builtin_amdgcn_update_dpp(0, (int)(v), 0xB1, 0xF, 0xF, false));               \
+    v = OP(v, (T)__builtin_amdgcn_update_dpp(0, (int)(v), 0x4E, 0xF, 0xF, false));               \
+    v = OP(v, (T)__builtin_amdgcn_update_dpp(0, (int)(v), 0x124, 0xF, 0xF, false));              \
+    v = OP(v, (T)__builtin_amdgcn_update_dpp(0, (int)(v), 0x128, 0xF, 0xF, false));              \
+  } while (0)
+
+__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t umin32(uint32_t a, uint32_t b) { return a < b ? a : b; }
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  STRATA_DPP_ROW_REDUCE(v, umax32, uint32_t);
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return umax32(umax32(a, b), umax32(c, d));
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  STRATA_DPP_ROW_REDUCE(v, umin32, uint32_t);
+  const uint32_t a = __builtin_amdgcn_readlane(v, 0), b = __builtin_amdgcn_readlane(v, 16);
+  const uint32_t c = __builtin_amdgcn_readlane(v, 32), d = __builtin_amdgcn_readlane(v, 48);
+  return umin32(umin32(a, b), umin32(c, d));
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v = v + dpp_f32<0xB1>(v);
+  v = v + dpp_f32<0x4E>(v);
+  v = v + dpp_f32<0x124>(v);
+  v = v + dpp_f32<0x128>(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (a + b) + (c + d);
+}
 
 // Optional per-kernel timing (see timing.hip).  A KernelTimer brackets one
 // kernel launch with events on its stream while timing is enabled.

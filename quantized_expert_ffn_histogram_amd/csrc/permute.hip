@@ -40,21 +40,30 @@ __device__ __forceinline__ uint64_t match_any(int key, int nbits) {
 
 __device__ __forceinline__ int id_bits(int E) { return 32 - __clz(E); }  // bits of E (sentinel)
 
-// Wavefront `wave` of the block walks pairs [p0, p1) in rounds of 64 and
-// places each at running[e] + rank; running[] lives in LDS.
+// Wavefront `wave` of the block walks pairs [p0, p1) (at most kPermuteSeg) in
+// rounds of 64 and places each at running[e] + rank; running[] lives in LDS.
+// All expert ids of the segment are loaded up front so their latency overlaps.
 __device__ __forceinline__ void scatter_rounds(const int *__restrict__ ids, int p0, int p1, int E,
                                                int *running, int *__restrict__ perm,
                                                int *__restrict__ inv_perm) {
+  constexpr int R = kPermuteSeg / kWave;
   const int lane = threadIdx.x & (kWave - 1);
   const int nbits = id_bits(E);
-  for (int base = p0; base < p1; base += kWave) {
-    const int p = base + lane;
-    const bool valid = p < p1;
-    const int e = valid ? ids[p] : E;  // sentinel E never matches a real expert
+  int ev[R];
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    const int p = p0 + q * kWave + lane;
+    ev[q] = p < p1 ? ids[p] : E;  // sentinel E never matches a real expert
+  }
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    if (p0 + q * kWave >= p1) break;
+    const int p = p0 + q * kWave + lane;
+    const int e = ev[q];
     const uint64_t same = match_any(e, nbits);
     const int rank = __popcll(same & lanemask_lt(lane));
     const bool last = (same >> lane) == 1ull;  // highest lane of my group
-    if (valid) {
+    if (p < p1) {
       const int old = running[e];
       const int dst = old + rank;
       perm[dst] = p;
@@ -68,47 +77,74 @@ __device__ __forceinline__ void scatter_rounds(const int *__restrict__ ids, int 
 
 __global__ __launch_bounds__(256) void seg_hist_kernel(const int *__restrict__ ids, int pairs, int E,
                                                        int nseg, int *__restrict__ hist) {
+  constexpr int R = kPermuteSeg / kWave;
   __shared__ int h[4][kMaxExperts];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int s = blockIdx.x * 4 + wave;
   for (int e = lane; e < E; e += kWave) h[wave][e] = 0;
-  __syncthreads();
-  if (s < nseg) {
-    const int p0 = s * kPermuteSeg, p1 = min(pairs, p0 + kPermuteSeg);
-    for (int p = p0 + lane; p < p1; p += kWave) atomicAdd(&h[wave][ids[p]], 1);
+  int ev[R];
+  const int p0 = s * kPermuteSeg, p1 = min(pairs, p0 + kPermuteSeg);
+#pragma unroll
+  for (int q = 0; q < R; ++q) {
+    const int p = p0 + q * kWave + lane;
+    ev[q] = (s < nseg && p < p1) ? ids[p] : -1;
   }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < R; ++q)
+    if (ev[q] >= 0) atomicAdd(&h[wave][ev[q]], 1);
   __syncthreads();
   if (s < nseg)
     for (int e = lane; e < E; e += kWave) hist[(size_t)e * nseg + s] = h[wave][e];
 }
 
-// Exclusive scan of hist (E*nseg ints, e-major) in place by one workgroup.
+// Exclusive scan of hist (E*nseg ints, e-major) in place by one workgroup:
+// passes of 8192 ints are loaded into LDS with coalesced reads, scanned there
+// (8 contiguous values per thread, then across threads) and written back.
 __global__ __launch_bounds__(1024) void seg_scan_kernel(int *__restrict__ hist, int E, int nseg,
                                                         int pairs, int *__restrict__ counts,
                                                         int *__restrict__ offsets) {
-  __shared__ int part[1024];
+  constexpr int CH = 8192, PER = CH / 1024;
+  __shared__ int buf[CH + CH / 32];  // one pad int per 32 breaks the stride-8 bank pattern
+  __shared__ int wsum[16];
   const int n = E * nseg;
-  const int tid = threadIdx.x;
-  const int per = (n + 1023) / 1024;
-  const int lo = min(n, tid * per), hi = min(n, lo + per);
-  int sum = 0;
-  for (int i = lo; i < hi; ++i) sum += hist[i];
-  part[tid] = sum;
-  __syncthreads();
-  // Hillis-Steele inclusive scan of the 1024 partial sums.
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int v = tid >= off ? part[tid - off] : 0;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto at = [](int i) { return i + (i >> 5); };
+  int carry = 0;
+  for (int base = 0; base < n; base += CH) {
+    const int m = min(CH, n - base);
+    for (int i = tid; i < CH; i += 1024) buf[at(i)] = i < m ? hist[base + i] : 0;
     __syncthreads();
-    part[tid] += v;
+    int v[PER], sum = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      v[q] = buf[at(tid * PER + q)];
+      sum += v[q];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int t = __shfl_up(incl, off, kWave);
+      if (lane >= off) incl += t;
+    }
+    if (lane == kWave - 1) wsum[wave] = incl;
+    __syncthreads();
+    int run = carry + incl - sum;
+    int total = 0;
+    for (int w2 = 0; w2 < 16; ++w2) {
+      if (w2 < wave) run += wsum[w2];
+      total += wsum[w2];
+    }
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      buf[at(tid * PER + q)] = run;
+      run += v[q];
+    }
+    __syncthreads();
+    for (int i = tid; i < m; i += 1024) hist[base + i] = buf[at(i)];
+    carry += total;
     __syncthreads();
   }
-  int run = part[tid] - sum;  // exclusive prefix of this thread's range
-  for (int i = lo; i < hi; ++i) {
-    const int c = hist[i];
-    hist[i] = run;
-    run += c;
-  }
-  __syncthreads();
   for (int e = tid; e < E; e += 1024) {
     const int o0 = hist[(size_t)e * nseg];
     const int o1 = e + 1 < E ? hist[(size_t)(e + 1) * nseg] : pairs;

@@ -4,13 +4,12 @@
 // ("两天移植，预填充提速8倍：Strata引擎实测" (kongchang.com), section
 // "Strata快在哪：不是魔法，是物流", MoE note: 512 experts, about 10 active).
 //
-// Every lane holds ceil(E/64) logits as 64-bit keys
-//     key = orderable(logit) << 32 | (0xFFFFFFFF - e)
-// so that the unsigned maximum is the largest logit and, among equal logits,
-// the lowest expert index.  -0.0 is canonicalised to +0.0 first so that signed
-// zeros tie (IEEE equality).  k rounds of (per-lane max, wavefront max,
-// remove the winner) give the ordered top-k; lane j then owns winner j and the
-// softmax over the k selected logits is a wavefront sum.
+// Every lane holds ceil(E/64) logits as order-preserving unsigned keys
+// (-0.0 is canonicalised to +0.0 first, so signed zeros tie as under IEEE
+// equality).  Each of k rounds takes the wavefront maximum key and then the
+// minimum expert index among the lanes holding it (ties go to the lowest
+// index), and removes the winner.  Lane j then owns winner j, and the softmax
+// over the k selected logits is a wavefront sum in fixed order.
 #include "moe_internal.h"
 
 namespace strata {
@@ -26,21 +25,6 @@ __device__ __forceinline__ float from_orderable(uint32_t u) {
   return __uint_as_float(b);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint64_t o = __shfl_xor(v, off, kWave);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
-
 template <int EPL>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict__ logits, int T,
                                                          int E, int k, int *__restrict__ ids,
@@ -50,34 +34,42 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
   if (t >= T) return;
   const float *row = logits + (size_t)t * E;
 
-  uint64_t key[EPL];
+  // u[i] = orderable value of expert i*64 + lane; 0 = absent or already taken
+  // (every finite logit maps above 0).
+  uint32_t u[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) {
     const int e = i * kWave + lane;
-    key[i] = 0;  // below every real key: never selected while k <= E
-    if (e < E) key[i] = ((uint64_t)orderable(row[e]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+    u[i] = e < E ? orderable(row[e]) : 0u;
   }
 
   int my_id = 0;
   float my_val = 0.0f;
   for (int r = 0; r < k; ++r) {
-    uint64_t best = key[0];
+    // Lane's best: largest value, lowest index among equals (smallest i).
+    uint32_t best = u[0];
+    int bi = 0;
 #pragma unroll
-    for (int i = 1; i < EPL; ++i) best = key[i] > best ? key[i] : best;
-    best = wave_max_u64(best);
-    const int e = (int)(0xFFFFFFFFu - (uint32_t)best);
+    for (int i = 1; i < EPL; ++i)
+      if (u[i] > best) {
+        best = u[i];
+        bi = i;
+      }
+    const uint32_t gmax = wave_max_u32(best);
+    const uint32_t cand = best == gmax ? (uint32_t)(bi * kWave + lane) : 0xFFFFFFFFu;
+    const int e = (int)wave_min_u32(cand);
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
-      if (i * kWave + lane == e) key[i] = 0;
+      if (i * kWave + lane == e) u[i] = 0u;
     if (lane == r) {
       my_id = e;
-      my_val = from_orderable((uint32_t)(best >> 32));
+      my_val = from_orderable(gmax);
     }
   }
 
   const float m = __shfl(my_val, 0, kWave);
   const float z = lane < k ? expf(my_val - m) : 0.0f;
-  const float s = wave_sum(z);
+  const float s = wave_sum_f32(z);
   if (lane < k) {
     ids[(size_t)t * k + lane] = my_id;
     w[(size_t)t * k + lane] = z / s;
