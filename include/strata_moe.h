@@ -132,9 +132,10 @@ int strata_moe_permute(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k,
  *   topk_w    in  float32 [T*k] routing weights, or NULL.
  *   y_or_out  out float32:
  *             topk_w != NULL: out[T][H] = sum_j topk_w[t][j] * y(t, j); the
- *                 library overwrites all of out (fused weighted scatter-add;
- *                 the summation order of the k terms is not fixed, so the
- *                 low bits may differ between runs);
+ *                 library overwrites all of out.  On the matrix-core path the
+ *                 expert outputs pass through fp16 rows in workspace and are
+ *                 summed in j order by a final kernel; both paths are
+ *                 deterministic;
  *             topk_w == NULL: y[T*k][H] in grouped order, row i = the expert
  *                 output of pair perm[i] (deterministic); finish the layer
  *                 with strata_moe_combine.

@@ -104,7 +104,8 @@ long long max_tiles(long long pairs, int E) {
 
 size_t ffn_workspace_bytes(long long T, int k, int E, int H, int I) {
   const long long pairs = T * k;
-  return up256((size_t)T * H * 2) + up256((size_t)pairs * I * 2) + up256((size_t)max_tiles(pairs, E) * sizeof(Tile)) + 256;
+  return up256((size_t)T * H * 2) + up256((size_t)pairs * I * 2) + up256((size_t)pairs * H * 2) +
+         up256((size_t)max_tiles(pairs, E) * sizeof(Tile)) + 256;
 }
 
 FfnWorkspace carve_ffn_workspace(void *base, long long T, int k, int E, int H, int I) {
@@ -115,6 +116,8 @@ FfnWorkspace carve_ffn_workspace(void *base, long long T, int k, int E, int H, i
   p += up256((size_t)T * H * 2);
   w.h = reinterpret_cast<uint16_t *>(p);
   p += up256((size_t)pairs * I * 2);
+  w.y16 = reinterpret_cast<uint16_t *>(p);
+  p += up256((size_t)pairs * H * 2);
   w.tiles = reinterpret_cast<Tile *>(p);
   p += up256((size_t)max_tiles(pairs, E) * sizeof(Tile));
   w.meta = reinterpret_cast<int *>(p);

@@ -28,7 +28,41 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   reinterpret_cast<float4 *>(out + (size_t)t * H)[n4] = acc;
 }
 
+// Fused-combine finish of the GEMM path: fp16 y rows in pair order, so the k
+// rows of token t are contiguous.  One thread: 8 consecutive features.
+__global__ __launch_bounds__(256) void combine_pairs_kernel(const uint4 *__restrict__ y16,
+                                                            const float *__restrict__ topk_w, int T, int k,
+                                                            int H, float4 *__restrict__ out) {
+  const int groups = H / 8;
+  const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (g >= (long long)T * groups) return;
+  const int t = (int)(g / groups), c = (int)(g - (long long)t * groups);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const float w = topk_w[(size_t)t * k + j];
+    const uint4 v = y16[((size_t)t * k + j) * groups + c];
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const auto h2 = __builtin_bit_cast(_Float16 __attribute__((ext_vector_type(2))), d[q]);
+      acc[2 * q] += w * (float)h2.x;
+      acc[2 * q + 1] += w * (float)h2.y;
+    }
+  }
+  out[g * 2] = float4{acc[0], acc[1], acc[2], acc[3]};
+  out[g * 2 + 1] = float4{acc[4], acc[5], acc[6], acc[7]};
+}
+
 }  // namespace
+
+hipError_t launch_combine_pairs(const uint16_t *y16, const float *topk_w, int T, int k, int H, float *out,
+                                hipStream_t s) {
+  const long long groups = (long long)T * (H / 8);
+  KernelTimer timer("combine", s);
+  combine_pairs_kernel<<<dim3((unsigned)((groups + 255) / 256)), 256, 0, s>>>(
+      reinterpret_cast<const uint4 *>(y16), topk_w, T, k, H, reinterpret_cast<float4 *>(out));
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const float *y, const int *inv_perm, const float *topk_w, int T, int k,
                           int H, float *out, hipStream_t s) {

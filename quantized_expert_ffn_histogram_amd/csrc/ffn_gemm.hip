@@ -57,10 +57,10 @@ struct GemmArgs {
   int N, K, g;
   const int *perm;
   int k;
-  const float *topk_w;    // down, fused: routing weight per pair
   const Tile *tiles;
   const int *meta;        // meta[0] = number of tiles
-  void *C;                // gate/up: h fp16 [pairs][N] (slot order); down: out [T][N] or y [pairs][N] (fp32)
+  void *C;                // gate/up: h fp16 [pairs][N] (slot order); down: fp16 y [pairs][N] in pair
+                          // order (fused combine follows) or fp32 y [pairs][N] in grouped order
   int nslices;
   int fused;
 };
@@ -97,11 +97,17 @@ __device__ __forceinline__ int slot_pos(int n) { return (n & ~7) | (((n & 3) << 
 
 struct RowTables {
   int src[kGemmRows];    // gate/up: token row of x; down: grouped row of h
-  int tok[kGemmRows];    // down: output row (token)
-  float wt[kGemmRows];   // down, fused: routing weight
+  int dst[kGemmRows];    // down: output row (pair index p for the fp16 y, grouped row otherwise)
 };
 
-constexpr int kStages = 4;                         // LDS ring depth (prefetch distance kStages-1)
+#ifndef STRATA_GEMM_STAGES
+#define STRATA_GEMM_STAGES 3
+#endif
+// LDS ring depth (prefetch distance kStages-1).  Three 26 KB stages let two
+// workgroups share a CU (two wavefronts per SIMD hide each other's stalls).
+constexpr int kStages = STRATA_GEMM_STAGES;
+static_assert(kStages == 3 || kStages == 4, "ring depth");
+constexpr int kWgPerCu = kStages == 3 ? 2 : 1;
 constexpr int kStageSegs = kGemmRows * kSegs;      // 16-byte A segments per stage
 
 // Wait until at most N vector-memory operations of this wavefront are
@@ -132,7 +138,10 @@ __device__ __forceinline__ lds_ptr_t as_lds(void *p) { return (lds_ptr_t)p; }
 // B-matrix row of the workgroup held by wavefront `wave`, column block nb, lane column col.
 __device__ __forceinline__ int brow_of(int wave, int nb, int col) { return wave * 64 + nb * 32 + col; }
 
-// One K chunk of MFMAs from one stage: NMB row blocks x 2 column blocks x 4 K-steps.
+// One K chunk of MFMAs from one stage: NMB token blocks x 2 feature blocks x
+// 4 K-steps.  The dequantized weights are the MFMA's A operand (32 features
+// x 16 K) and the token rows its B operand, so each lane's accumulator holds
+// runs of 4 consecutive output features of one token (vector stores).
 template <int NMB>
 __device__ __forceinline__ void mma_chunk(floatx16 (&acc)[NMB][2], const Stage &st, int wave, int col, int half) {
   uint4 bw[2];
@@ -162,7 +171,7 @@ __device__ __forceinline__ void mma_chunk(floatx16 (&acc)[NMB][2], const Stage &
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[j & 1][mb], bf[nb], acc[mb][nb], 0, 0, 0);
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[nb], af[j & 1][mb], acc[mb][nb], 0, 0, 0);
   }
 }
 
@@ -186,49 +195,57 @@ __device__ __forceinline__ Stage &stage_ref(const Ring &R) { return *R.st[S]; }
 //     load writes one zero-extended dword per lane).
 // Per chunk: wait for this wavefront's loads of the chunk, one barrier (all
 // wavefronts' loads of the chunk have landed; the oldest stage is free), issue
-// chunk c+3 into it, then dequant + MFMAs.  Past the last chunk the issue
+// chunk c+kStages-1 into it, then dequant + MFMAs.  Past the last chunk the issue
 // repeats the last chunk (loads are never skipped), so every wait counts the
 // same number of operations.
 template <int MODE, int NMB>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const Ring &R, const RowTables &rt, int e, int row0,
                                           int nrows, int slice) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform (scalar registers)
   const int col = lane & 31, half = lane >> 5;
   const int nchunks = a.K / kKC;
   constexpr int V = NMB + 4;  // direct-to-LDS loads per stage per wavefront
 
+  // Every load address is a wavefront-uniform base plus a 32-bit lane offset
+  // (bytes); the uniform parts advance by the chunk's K offset.
   uint32_t aoff[NMB];
 #pragma unroll
   for (int i = 0; i < NMB; ++i) {
     const int p = (4 * i + wave) * 64 + lane;
     const int r = p >> 3, c = (p & 7) ^ (r & 7);
-    aoff[i] = (uint32_t)rt.src[r] * (uint32_t)a.K + 8 * c;
+    aoff[i] = ((uint32_t)rt.src[r] * (uint32_t)a.K + 8 * c) * 2;
   }
-  // Loads of B rows: lane -> (row col2 = lane>>1 of the 32-row block, half hh = lane&1).
+  // B rows: lane -> (row lane>>1 of the 32-row block, half lane&1).
   const int col2 = lane >> 1, hh = lane & 1;
-  const uint8_t *bsrc[2];
-  const uint16_t *ssrc[2];
+  const char *bbase[2];
+  const char *sbase[2];
+  uint32_t boff[2], soff;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const int n = MODE == 0 ? slice * kGateUpColsPerWG + wave * 32 + col2
-                            : slice * kDownColsPerWG + wave * 64 + nb * 32 + col2;
+    const int n0 = MODE == 0 ? slice * kGateUpColsPerWG + wave * 32 : slice * kDownColsPerWG + wave * 64 + nb * 32;
     const uint8_t *B = (MODE == 0 && nb == 1) ? a.B1 : a.B0;
     const uint16_t *Sc = (MODE == 0 && nb == 1) ? a.S1 : a.S0;
-    bsrc[nb] = B + ((size_t)e * a.N + n) * (a.K / 2) + 16 * hh;
-    ssrc[nb] = Sc + ((size_t)e * a.N + n) * (a.K / a.g);
+    bbase[nb] = reinterpret_cast<const char *>(B + ((size_t)e * a.N + n0) * (a.K / 2));
+    sbase[nb] = reinterpret_cast<const char *>(Sc + ((size_t)e * a.N + n0) * (a.K / a.g));
+    boff[nb] = (uint32_t)col2 * (a.K / 2) + 16 * hh;
   }
+  soff = ((uint32_t)col2 * (a.K / a.g)) * 2;
   const int g_shift = 31 - __clz(a.g);  // g is a power of two
+  const char *abase = reinterpret_cast<const char *>(a.A);
 
   auto issue = [&](Stage &st, int c) {
     const int kc = c * kKC;
+    const char *ab = abase + 2 * kc;
 #pragma unroll
     for (int i = 0; i < NMB; ++i)
-      __builtin_amdgcn_global_load_lds(a.A + aoff[i] + kc, as_lds(&st.a[(4 * i + wave) * 64]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(ab + aoff[i], as_lds(&st.a[(4 * i + wave) * 64]), 16, 0, 0);
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int base = brow_of(wave, nb, 0) * 2;
-      __builtin_amdgcn_global_load_lds(bsrc[nb] + kc / 2, as_lds(&st.b[base]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(ssrc[nb] + ((kc + 32 * hh) >> g_shift), as_lds(&st.s[base]), 2, 0, 0);
+      __builtin_amdgcn_global_load_lds(bbase[nb] + kc / 2 + boff[nb], as_lds(&st.b[base]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(sbase[nb] + 2 * ((kc + 32 * hh) >> g_shift) + soff, as_lds(&st.s[base]), 2,
+                                       0, 0);
     }
   };
 
@@ -242,15 +259,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const Ring &R, cons
   compiler_fence();
   issue(stage_ref<0>(R), 0);
   issue(stage_ref<1>(R), min(1, last));
-  issue(stage_ref<2>(R), min(2, last));
+  if constexpr (kStages == 4) issue(stage_ref<2>(R), min(2, last));
 
   auto step = [&](auto stage_tag, int c) {
     constexpr int S = decltype(stage_tag)::value;
     compiler_fence();
-    wait_vmcnt<2 * V>();            // this wavefront's loads of chunk c are done
+    wait_vmcnt<(kStages - 2) * V>();  // this wavefront's loads of chunk c are done
     __builtin_amdgcn_s_barrier();  // ... and every other wavefront's; stage S-1 is free
     compiler_fence();
-    issue(stage_ref<(S + 3) % kStages>(R), min(c + 3, last));
+    issue(stage_ref<(S + kStages - 1) % kStages>(R), min(c + kStages - 1, last));
     compiler_fence();
     if (c < nchunks) mma_chunk<NMB>(acc, stage_ref<S>(R), wave, col, half);
   };
@@ -259,35 +276,72 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const Ring &R, cons
     step(std::integral_constant<int, 0>{}, c0);
     step(std::integral_constant<int, 1>{}, c0 + 1);
     step(std::integral_constant<int, 2>{}, c0 + 2);
-    step(std::integral_constant<int, 3>{}, c0 + 3);
+    if constexpr (kStages == 4) step(std::integral_constant<int, 3>{}, c0 + 3);
   }
   compiler_fence();
   wait_vmcnt<0>();  // no load of this tile may land in the next tile's stages
   compiler_fence();
 
-  // Epilogue.  Accumulator element v of a lane: row 8*(v/4) + 4*half + v%4, column col.
+  // Epilogue.  Accumulator element v of a lane: token row mb*32 + col of the
+  // tile, feature 8*(v/4) + 4*half + v%4 of the 32-feature block nb.
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
+    const int r = mb * 32 + col;
+    if (MODE == 0) {
+      // h = silu(g) * u, fp16.  Lanes l and l^32 hold the low and high four
+      // features of each 8-feature block; after one exchange each lane owns two
+      // whole blocks and stores them in fragment slot order (16 bytes each).
+      uint32_t hp[4][2];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = mb * 32 + 8 * (v >> 2) + 4 * half + (v & 3);
-      if (r >= nrows) continue;
-      if (MODE == 0) {
-        const int n = slice * kGateUpColsPerWG + wave * 32 + col;
-        const float gv = acc[mb][0][v], uv = acc[mb][1][v];
-        const float hv = gv / (1.0f + __expf(-gv)) * uv;
-        _Float16 *hout = static_cast<_Float16 *>(a.C);
-        hout[(size_t)(row0 + r) * a.N + slot_pos(n)] = (_Float16)hv;
-      } else {
-        float *outp = static_cast<float *>(a.C);
+      for (int i = 0; i < 4; ++i) {
+        float hv[4];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const int n = slice * kDownColsPerWG + wave * 64 + nb * 32 + col;
-          const float yv = acc[mb][nb][v];
-          if (a.fused)
-            unsafeAtomicAdd(outp + (size_t)rt.tok[r] * a.N + n, rt.wt[r] * yv);
-          else
-            outp[(size_t)(row0 + r) * a.N + n] = yv;
+        for (int q = 0; q < 4; ++q) {
+          const float gv = acc[mb][0][4 * i + q], uv = acc[mb][1][4 * i + q];
+          hv[q] = gv / (1.0f + __expf(-gv)) * uv;
+        }
+        hp[i][0] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)hv[0], (_Float16)hv[1]});
+        hp[i][1] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)hv[2], (_Float16)hv[3]});
+      }
+      uint32_t snd[4], rcv[4];
+      snd[0] = half ? hp[0][0] : hp[2][0];
+      snd[1] = half ? hp[0][1] : hp[2][1];
+      snd[2] = half ? hp[1][0] : hp[3][0];
+      snd[3] = half ? hp[1][1] : hp[3][1];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) rcv[x] = __shfl_xor(snd[x], 32, kWave);
+      if (r < nrows) {
+        uint16_t *hout = static_cast<uint16_t *>(a.C) + (size_t)(row0 + r) * a.N + slice * kGateUpColsPerWG + wave * 32;
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+          const int grp = 2 * half + gi;  // 8-feature block this lane stores
+          const uint32_t lo0 = half ? rcv[2 * gi] : hp[grp][0], lo1 = half ? rcv[2 * gi + 1] : hp[grp][1];
+          const uint32_t hi0 = half ? hp[grp][0] : rcv[2 * gi], hi1 = half ? hp[grp][1] : rcv[2 * gi + 1];
+          uint4 o;
+          o.x = __builtin_amdgcn_perm(hi0, lo0, 0x05040100u);
+          o.y = __builtin_amdgcn_perm(hi0, lo0, 0x07060302u);
+          o.z = __builtin_amdgcn_perm(hi1, lo1, 0x05040100u);
+          o.w = __builtin_amdgcn_perm(hi1, lo1, 0x07060302u);
+          *reinterpret_cast<uint4 *>(hout + 8 * grp) = o;
+        }
+      }
+    } else if (r < nrows) {
+      const size_t row = (size_t)rt.dst[r] * a.N;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int n = slice * kDownColsPerWG + wave * 64 + nb * 32 + 8 * i + 4 * half;
+          const float y4[4] = {acc[mb][nb][4 * i], acc[mb][nb][4 * i + 1], acc[mb][nb][4 * i + 2],
+                               acc[mb][nb][4 * i + 3]};
+          if (a.fused) {  // fp16 y rows in pair order, summed by the combine kernel
+            uint2 o;
+            o.x = __builtin_bit_cast(uint32_t, half2_t{(_Float16)y4[0], (_Float16)y4[1]});
+            o.y = __builtin_bit_cast(uint32_t, half2_t{(_Float16)y4[2], (_Float16)y4[3]});
+            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.C) + row + n) = o;
+          } else {        // fp32 y rows in grouped order
+            *reinterpret_cast<float4 *>(static_cast<float *>(a.C) + row + n) = float4{y4[0], y4[1], y4[2], y4[3]};
+          }
         }
       }
     }
@@ -295,10 +349,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const Ring &R, cons
 }
 
 template <int MODE>  // 0: gate/up + silu*mul -> h;  1: down + weighted combine
-__global__ __launch_bounds__(256, 1) void moe_gemm_kernel(GemmArgs a) {
-  __shared__ Stage st0, st1, st2, st3;
+__global__ __launch_bounds__(256, kWgPerCu) void moe_gemm_kernel(GemmArgs a) {
+  __shared__ Stage st0, st1, st2;
+#if STRATA_GEMM_STAGES == 4
+  __shared__ Stage st3;
+#else
+  Stage *const st3 = nullptr;
+#endif
   __shared__ RowTables rt;
+#if STRATA_GEMM_STAGES == 4
   const Ring R{{&st0, &st1, &st2, &st3}};
+#else
+  (void)st3;
+  const Ring R{{&st0, &st1, &st2}};
+#endif
 
   const int tid = threadIdx.x;
   const int total = a.meta[0] * a.nslices;
@@ -321,8 +385,7 @@ __global__ __launch_bounds__(256, 1) void moe_gemm_kernel(GemmArgs a) {
         rt.src[tid] = p / a.k;
       } else {
         rt.src[tid] = tile.row0 + r;
-        rt.tok[tid] = p / a.k;
-        rt.wt[tid] = a.fused ? a.topk_w[p] : 0.0f;
+        rt.dst[tid] = a.fused ? p : tile.row0 + r;
       }
     }
     __syncthreads();
@@ -335,31 +398,10 @@ __global__ __launch_bounds__(256, 1) void moe_gemm_kernel(GemmArgs a) {
   }
 }
 
-// Prologue of the GEMM path: x (bf16) -> fp16 in fragment slot order, and the
-// fused output cleared.  Grid-stride over 8-element groups.
-__global__ __launch_bounds__(256) void prep_kernel(const uint4 *__restrict__ x, uint4 *__restrict__ xq,
-                                                   size_t n8, float4 *__restrict__ out, size_t n_out4) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n8; i += stride) {
-    const uint4 v = x[i];
-    auto lo = [](uint32_t d) { return __uint_as_float(d << 16); };
-    auto hi = [](uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); };
-    uint4 o;
-    o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo(v.x), lo(v.z)));
-    o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi(v.x), hi(v.z)));
-    o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo(v.y), lo(v.w)));
-    o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi(v.y), hi(v.w)));
-    xq[i] = o;
-  }
-  if (out)
-    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n_out4; i += stride)
-      out[i] = float4{0.f, 0.f, 0.f, 0.f};
-}
-
-__global__ __launch_bounds__(1024) void plan_kernel(const int *__restrict__ offsets, int E,
-                                                    int rows_per_tile, Tile *__restrict__ tiles,
-                                                    int *__restrict__ meta) {
-  __shared__ int part[1024];
+// Tile list from the expert offsets: expert e gets ceil(count_e / rows_per_tile)
+// consecutive tiles; one workgroup of 1024 threads (E <= 1024).
+__device__ __forceinline__ void plan_tiles(const int *__restrict__ offsets, int E, int rows_per_tile,
+                                           Tile *__restrict__ tiles, int *__restrict__ meta, int *part) {
   const int e = threadIdx.x;
   const int lo = e < E ? offsets[e] : 0;
   const int c = e < E ? offsets[e + 1] - lo : 0;
@@ -384,9 +426,38 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int *__restrict__ offs
   if (e == 1023) meta[0] = part[1023];
 }
 
-// Persistent grid: one workgroup per CU (256 CUs), whole XCD rounds.
+__global__ __launch_bounds__(1024) void plan_kernel(const int *__restrict__ offsets, int E, int rows_per_tile,
+                                                    Tile *__restrict__ tiles, int *__restrict__ meta) {
+  __shared__ int part[1024];
+  plan_tiles(offsets, E, rows_per_tile, tiles, meta, part);
+}
+
+// Prologue of the GEMM path: block 0 builds the tile list; every block
+// converts x (bf16) to fp16 in fragment slot order (grid-stride, 8 elements
+// per thread).
+__global__ __launch_bounds__(1024) void prep_kernel(const int *__restrict__ offsets, int E, Tile *__restrict__ tiles,
+                                                    int *__restrict__ meta, const uint4 *__restrict__ x,
+                                                    uint4 *__restrict__ xq, size_t n8) {
+  __shared__ int part[1024];
+  if (blockIdx.x == 0) plan_tiles(offsets, E, kGemmRows, tiles, meta, part);
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n8; i += stride) {
+    const uint4 v = x[i];
+    auto lo = [](uint32_t d) { return __uint_as_float(d << 16); };
+    auto hi = [](uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); };
+    uint4 o;
+    o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo(v.x), lo(v.z)));
+    o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi(v.x), hi(v.z)));
+    o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo(v.y), lo(v.w)));
+    o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi(v.y), hi(v.w)));
+    xq[i] = o;
+  }
+}
+
+// Persistent grid: kWgPerCu workgroups per CU (256 CUs), whole XCD rounds.
 int persistent_grid(long long work_upper) {
-  long long g = work_upper < 256 ? work_upper : 256;
+  const long long cap = 256LL * kWgPerCu;
+  long long g = work_upper < cap ? work_upper : cap;
   g = (g + kXcds - 1) / kXcds * kXcds;
   return (int)(g < kXcds ? kXcds : g);
 }
@@ -405,17 +476,14 @@ hipError_t launch_ffn_gemm(const uint16_t *x, int T, int k, const FfnWeights &w,
                            const FfnWorkspace &ws, hipStream_t s) {
   const long long pairs = (long long)T * k;
   const long long tiles_upper = (pairs + kGemmRows - 1) / kGemmRows + std::min<long long>(w.E, pairs);
-  hipError_t err = launch_plan(offsets, w.E, kGemmRows, ws.tiles, ws.meta, s);
-  if (err != hipSuccess) return err;
-
   const bool fused = topk_w != nullptr;
+  hipError_t err;
   {
     KernelTimer timer("ffn_prep", s);
     const size_t n8 = (size_t)T * w.H / 8;
-    const int blocks = (int)std::min<size_t>(4096, (n8 + 255) / 256);
-    prep_kernel<<<blocks, 256, 0, s>>>(reinterpret_cast<const uint4 *>(x), reinterpret_cast<uint4 *>(ws.xq), n8,
-                                       fused ? reinterpret_cast<float4 *>(y_or_out) : nullptr,
-                                       fused ? (size_t)T * w.H / 4 : 0);
+    const int blocks = (int)std::max<size_t>(1, std::min<size_t>(1024, (n8 + 1023) / 1024));
+    prep_kernel<<<blocks, 1024, 0, s>>>(offsets, w.E, ws.tiles, ws.meta, reinterpret_cast<const uint4 *>(x),
+                                        reinterpret_cast<uint4 *>(ws.xq), n8);
     if ((err = hipGetLastError()) != hipSuccess) return err;
   }
 
@@ -430,7 +498,6 @@ hipError_t launch_ffn_gemm(const uint16_t *x, int T, int k, const FfnWeights &w,
   g.g = w.g;
   g.perm = perm;
   g.k = k;
-  g.topk_w = nullptr;
   g.tiles = ws.tiles;
   g.meta = ws.meta;
   g.C = ws.h;
@@ -439,8 +506,8 @@ hipError_t launch_ffn_gemm(const uint16_t *x, int T, int k, const FfnWeights &w,
   {
     KernelTimer timer("gemm_gateup", s);
     moe_gemm_kernel<0><<<persistent_grid(tiles_upper * g.nslices), 256, 0, s>>>(g);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  if ((err = hipGetLastError()) != hipSuccess) return err;
 
   GemmArgs d = g;
   d.A = ws.h;
@@ -450,15 +517,16 @@ hipError_t launch_ffn_gemm(const uint16_t *x, int T, int k, const FfnWeights &w,
   d.S1 = nullptr;
   d.N = w.H;
   d.K = w.I;
-  d.topk_w = topk_w;
-  d.C = y_or_out;
+  d.C = fused ? static_cast<void *>(ws.y16) : static_cast<void *>(y_or_out);
   d.nslices = w.H / kDownColsPerWG;
   d.fused = fused ? 1 : 0;
   {
     KernelTimer timer("gemm_down", s);
     moe_gemm_kernel<1><<<persistent_grid(tiles_upper * d.nslices), 256, 0, s>>>(d);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
   }
-  return hipGetLastError();
+  if (fused) return launch_combine_pairs(ws.y16, topk_w, T, k, w.H, y_or_out, s);
+  return hipSuccess;
 }
 
 }  // namespace strata

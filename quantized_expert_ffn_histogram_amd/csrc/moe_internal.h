@@ -55,6 +55,7 @@ hipError_t launch_permute(const int *ids, int pairs, int E, int *counts, int *of
 struct FfnWorkspace {
   uint16_t *xq;      // fp16 [T][H], fragment slot order (GEMM path)
   uint16_t *h;       // fp16 [pairs][I]
+  uint16_t *y16;     // fp16 [pairs][H], pair order (GEMM path, fused combine)
   Tile *tiles;       // grouped-work list
   int *meta;         // meta[0] = number of tiles
   size_t bytes;
@@ -71,6 +72,9 @@ hipError_t launch_ffn_gemv(const uint16_t *x, int T, int k, const FfnWeights &w,
 
 hipError_t launch_combine(const float *y, const int *inv_perm, const float *topk_w, int T,
                           int k, int H, float *out, hipStream_t s);
+// out[t] = sum_j topk_w[t*k+j] * y16[t*k+j] (fp16 rows in pair order), j in order.
+hipError_t launch_combine_pairs(const uint16_t *y16, const float *topk_w, int T, int k, int H, float *out,
+                                hipStream_t s);
 hipError_t launch_plan(const int *offsets, int E, int rows_per_tile, Tile *tiles, int *meta,
                        hipStream_t s);
 
