@@ -1,37 +1,41 @@
 // Grouped expert GEMMs with the int4 dequantization fused into the matmul
 // (matrix-core path, for prefill chunks with many tokens per expert).
 //
-// The pages' point is that 4-bit weights must be dequantized inside the matmul
-// kernel, not expanded to a full-precision copy before it (lqnn.cn static
-// review §1.2; kongchang.com hands-on, MMQ note: blocks of low-bit weights are
-// dequantized during the matrix product), and that larger batches per expert
-// amortise each expert's weight fetch ("两天移植，预填充提速8倍：Strata引擎实测",
-// section "Strata快在哪：不是魔法，是物流").  The SwiGLU activation is fused into
-// the gate/up kernel's epilogue and the weighted combine into the down kernel's
-// (activation fused with the FFN projection: yfxerp.com static review §5.1).
+// 4-bit weights are dequantized inside the matmul kernel, never expanded to a
+// full-precision copy first (lqnn.cn static review §1.2; kongchang.com
+// hands-on, MMQ note: low-bit weight blocks are dequantized during the matrix
+// product), and all tokens routed to an expert share one fetch of its weights
+// ("两天移植，预填充提速8倍：Strata引擎实测", section "Strata快在哪：不是魔法，是
+// 物流").  SwiGLU is fused into the gate/up kernel's epilogue (activation fused
+// with the FFN projection: yfxerp.com static review §5.1).
 //
-// Work unit: a tile of up to 128 grouped rows of one expert (a Tile from the
-// plan kernel) times a slice of output columns.  Workgroup = 4 wavefronts;
-// each wavefront owns 64 B-matrix rows (two 32-column MFMA blocks) across all
-// of the tile's rows, so every weight element is fetched and dequantized by
-// exactly one wavefront of the workgroup:
-//   gate/up: wavefront w owns h columns [w*32, w*32+32) of the slice, i.e. the
-//            gate rows and the up rows of those columns (silu(g)*u is local);
-//   down:    wavefront w owns output columns [w*64, w*64+64) of the slice.
-// A (token rows) is staged per K chunk of 128 through LDS as fp16; every
-// wavefront reads all of it.  Matrix cores: v_mfma_f32_32x32x16_f16.
+// Work item: a tile of up to 128 grouped rows of one expert (from the plan)
+// times a slice of weight rows ("features").  Workgroup = 4 wavefronts; each
+// wavefront owns NB blocks of 32 features for all of the tile's tokens, so
+// every weight element is fetched and dequantized by exactly one wavefront:
+//   gate/up: wavefront w owns NB/2 gate blocks and the NB/2 up blocks of the
+//            same h columns (silu(g)*u is local to the lane);
+//   down:    wavefront w owns NB blocks of output features.
+// NB = 2: two workgroups per CU (accumulators plus operands fit 256 VGPRs),
+// 3-stage ring.  (NB = 4 tiles halve the LDS reads per MFMA but need the AGPR
+// file and one workgroup per CU; on gfx950 they measured slower, since a
+// single wavefront per SIMD cannot hide the dequant, LDS and barrier
+// latencies.)  Matrix cores: v_mfma_f32_32x32x16_f16
+// with the dequantized weights as the A operand and token rows as B, so each
+// lane's accumulator holds runs of four consecutive features of one token.
 //
 // Dequant in registers: a dword holds 8 nibbles u_0..u_7 (even K low); the
-// pair (u_m, u_{m+4}) is moved into the mantissas of two fp16 1024.0 values
-// with one shift and one and-or, minus 1032 gives q exactly, times the fp16
-// group scale gives fp16(q*s) with a single rounding.  Operand slot e of a
-// fragment therefore holds K offset (e>>1) + 4*(e&1) of its 8-block; A is
-// written to LDS in the same order, so the contraction is over the true K.
+// pair (u_m, u_{m+4}) goes into the mantissas of two fp16 1024.0 values with a
+// shift and an and-or, minus 1032 gives q exactly, times the fp16 group scale
+// gives fp16(q*s) with a single rounding.  Fragment slot e therefore holds K
+// offset (e>>1) + 4*(e&1) of its 8-block; token rows are stored in the same
+// slot order, so the contraction runs over the true K.
 //
-// Tile scheduling: persistent workgroups.  Workgroups are dispatched to the 8
-// XCDs round-robin by block index; each XCD gets a contiguous range of
-// (tile, slice) work items so that the slices of one tile (which share its A
-// rows) run on the same XCD and hit its L2.
+// Pipeline: every operand moves global -> LDS with direct-to-LDS loads
+// (global_load_lds), kStages-1 K chunks ahead, one barrier per chunk.
+// Scheduling: persistent workgroups; workgroups reach the 8 XCDs round-robin
+// by block index, and each XCD gets a contiguous range of (tile, slice) items
+// so the slices of one tile, which share its token rows, meet in one L2.
 #include <type_traits>
 
 #include "moe_internal.h"
@@ -44,33 +48,76 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kXcds = 8;
-constexpr int kMB = kGemmRows / 32;            // 32-row MFMA blocks per tile
-constexpr int kKC = kGemmKChunk;               // K per pipelined chunk
-constexpr int kSegs = kKC / 8;                 // 16-byte segments per A row per chunk
+constexpr int kKC = kGemmKChunk;            // K per pipelined chunk (64)
+constexpr int kSegs = kKC / 8;              // 16-byte segments per token row per chunk
+constexpr int kStageSegs = kGemmRows * kSegs;
+
+template <int NB>
+struct Cfg {
+  static constexpr int kStages = 3;                // LDS ring depth
+  static constexpr int kWgPerCu = 2;
+  static constexpr int kBRows = 4 * NB * 32;       // weight rows per workgroup
+  static constexpr int kHCols = 2 * NB * 32;       // gate/up: h columns per workgroup
+  static constexpr int kOutCols = 4 * NB * 32;     // down: output features per workgroup
+};
 
 struct GemmArgs {
-  const uint16_t *A;      // fp16 rows in fragment slot order: gate/up: x [T][K]; down: h [pairs][K]
-  const uint8_t *B0;      // gate or down, packed [E][N][K/2]
-  const uint16_t *S0;     // fp16 scales [E][N][K/g]
-  const uint8_t *B1;      // up (gate/up only)
+  const uint16_t *A;   // fp16 rows in fragment slot order: gate/up: x [T][K]; down: h [pairs][K]
+  const uint8_t *B0;   // gate or down, packed [E][N][K/2]
+  const uint16_t *S0;  // fp16 scales [E][N][K/g]
+  const uint8_t *B1;   // up (gate/up only)
   const uint16_t *S1;
   int N, K, g;
   const int *perm;
   int k;
   const Tile *tiles;
-  const int *meta;        // meta[0] = number of tiles
-  void *C;                // gate/up: h fp16 [pairs][N] (slot order); down: fp16 y [pairs][N] in pair
-                          // order (fused combine follows) or fp32 y [pairs][N] in grouped order
+  const int *meta;     // meta[0] = number of tiles
+  void *C;             // gate/up: h fp16 [pairs][N] (slot order); down: fp16 y [pairs][N] in pair
+                       // order (fused combine follows) or fp32 y [pairs][N] in grouped order
   int nslices;
   int fused;
 };
 
-__device__ __forceinline__ half8 dequant8(uint32_t d, half2_t s2) {
+struct RowTables {
+  int src[kGemmRows];  // gate/up: token row of x; down: grouped row of h
+  int dst[kGemmRows];  // down: output row (pair index p for the fp16 y, grouped row otherwise)
+};
+
+template <int NB>
+struct Stage {
+  uint4 a[kStageSegs];              // token rows [row][segment], XOR-swizzled (a_slot)
+  uint4 b[2 * Cfg<NB>::kBRows];     // [weight row][lane half]: 16 bytes = 32 K values
+  uint32_t s[2 * Cfg<NB>::kBRows];  // [weight row][lane half]: fp16 group scale in the low half
+};
+
+template <int NB>
+struct Ring {
+  Stage<NB> *st[Cfg<NB>::kStages];
+};
+
+// Direct-to-LDS loads take an LDS-address-space pointer; the cast makes the
+// conversion from the generic pointer of a __shared__ object explicit.
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+__device__ __forceinline__ lds_ptr_t as_lds(void *p) { return (lds_ptr_t)p; }
+
+// Wait until at most N vector-memory operations of this wavefront are
+// outstanding (expcnt and lgkmcnt left unconstrained), N < 64.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Compiler-only memory barrier: keeps loads, direct-to-LDS issues and LDS
+// reads on their side of the explicit waits and barriers.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+__device__ __forceinline__ half8 dequant8(uint32_t d, half2_t s2, uint32_t mask, uint32_t magic) {
   const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
-  const uint32_t r0 = (d & 0x000F000Fu) | 0x64006400u;
-  const uint32_t r1 = ((d >> 4) & 0x000F000Fu) | 0x64006400u;
-  const uint32_t r2 = ((d >> 8) & 0x000F000Fu) | 0x64006400u;
-  const uint32_t r3 = ((d >> 12) & 0x000F000Fu) | 0x64006400u;
+  const uint32_t r0 = (d & mask) | magic;
+  const uint32_t r1 = ((d >> 4) & mask) | magic;
+  const uint32_t r2 = ((d >> 8) & mask) | magic;
+  const uint32_t r3 = ((d >> 12) & mask) | magic;
   const half2_t h0 = (__builtin_bit_cast(half2_t, r0) - off) * s2;
   const half2_t h1 = (__builtin_bit_cast(half2_t, r1) - off) * s2;
   const half2_t h2 = (__builtin_bit_cast(half2_t, r2) - off) * s2;
@@ -87,73 +134,30 @@ __device__ __forceinline__ uint32_t dword_of(const uint4 v, int j) {
   }
 }
 
-// LDS position (in 16-byte units) of logical segment c of tile row r: the XOR
-// spreads the 8 rows that one 8-lane group of a ds_read_b128 touches over all
-// bank quads.
+// LDS position (16-byte units) of logical segment c of tile row r: the XOR
+// spreads the 8 rows read by one 8-lane group of a ds_read_b128 over all bank
+// quads.
 __device__ __forceinline__ int a_slot(int r, int c) { return r * kSegs + (c ^ (r & 7)); }
 
-// Position of column n inside a row stored in fragment slot order.
-__device__ __forceinline__ int slot_pos(int n) { return (n & ~7) | (((n & 3) << 1) | ((n >> 2) & 1)); }
+template <int NB>
+__device__ __forceinline__ int brow_of(int wave, int nb, int col) { return (wave * NB + nb) * 32 + col; }
 
-struct RowTables {
-  int src[kGemmRows];    // gate/up: token row of x; down: grouped row of h
-  int dst[kGemmRows];    // down: output row (pair index p for the fp16 y, grouped row otherwise)
-};
-
-#ifndef STRATA_GEMM_STAGES
-#define STRATA_GEMM_STAGES 3
-#endif
-// LDS ring depth (prefetch distance kStages-1).  Three 26 KB stages let two
-// workgroups share a CU (two wavefronts per SIMD hide each other's stalls).
-constexpr int kStages = STRATA_GEMM_STAGES;
-static_assert(kStages == 3 || kStages == 4, "ring depth");
-constexpr int kWgPerCu = kStages == 3 ? 2 : 1;
-constexpr int kStageSegs = kGemmRows * kSegs;      // 16-byte A segments per stage
-
-// Wait until at most N vector-memory operations of this wavefront are
-// outstanding (expcnt and lgkmcnt left unconstrained), N < 64.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x0F70);
-}
-
-// Compiler-only memory barrier: keeps loads, DMA issues and LDS reads on
-// their side of the waits and barriers below.
-__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
-
-// One pipeline stage in LDS: a K chunk of the tile's A rows, the packed
-// weights of the workgroup's 256 B-matrix rows and their scales.
-struct Stage {
-  uint4 a[kStageSegs];          // [row][segment], XOR-swizzled (a_slot)
-  uint4 b[2 * 256];             // [B row][lane half] 16 bytes = 32 K values
-  uint32_t s[2 * 256];          // [B row][lane half] fp16 group scale in the low half
-};
-
-// Direct-to-LDS loads take an LDS-address-space pointer; the cast makes the
-// conversion from the generic pointer of a __shared__ object explicit.
-typedef __attribute__((address_space(3))) void *lds_ptr_t;
-__device__ __forceinline__ lds_ptr_t as_lds(void *p) { return (lds_ptr_t)p; }
-
-// B-matrix row of the workgroup held by wavefront `wave`, column block nb, lane column col.
-__device__ __forceinline__ int brow_of(int wave, int nb, int col) { return wave * 64 + nb * 32 + col; }
-
-// One K chunk of MFMAs from one stage: NMB token blocks x 2 feature blocks x
-// 4 K-steps.  The dequantized weights are the MFMA's A operand (32 features
-// x 16 K) and the token rows its B operand, so each lane's accumulator holds
-// runs of 4 consecutive output features of one token (vector stores).
-template <int NMB>
-__device__ __forceinline__ void mma_chunk(floatx16 (&acc)[NMB][2], const Stage &st, int wave, int col, int half) {
-  uint4 bw[2];
-  half2_t s2[2];
+// One K chunk of MFMAs from one stage: NMB token blocks x NB feature blocks x 4 K-steps.
+template <int NB, int NMB>
+__device__ __forceinline__ void mma_chunk(floatx16 (&acc)[NMB][NB], const Stage<NB> &st, int wave, int col,
+                                          int half) {
+  const uint32_t mask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
+  const uint32_t magic = __builtin_amdgcn_readfirstlane(0x64006400u);
+  uint4 bw[NB];
+  half2_t s2[NB];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int br = brow_of(wave, nb, col);
+  for (int nb = 0; nb < NB; ++nb) {
+    const int br = brow_of<NB>(wave, nb, col);
     bw[nb] = st.b[br * 2 + half];
     const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)st.s[br * 2 + half]);
     s2[nb] = half2_t{sv, sv};
   }
-  // A fragments are read one K-step ahead of the MFMAs that use them.
+  // Token fragments are read one K-step ahead of the MFMAs that use them.
   half8 af[2][NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) af[0][mb] = __builtin_bit_cast(half8, st.a[a_slot(mb * 32 + col, 4 * half)]);
@@ -164,51 +168,50 @@ __device__ __forceinline__ void mma_chunk(floatx16 (&acc)[NMB][2], const Stage &
       for (int mb = 0; mb < NMB; ++mb)
         af[(j + 1) & 1][mb] = __builtin_bit_cast(half8, st.a[a_slot(mb * 32 + col, 4 * half + j + 1)]);
     }
-    half8 bf[2];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) bf[nb] = dequant8(dword_of(bw[nb], j), s2[nb]);
+    for (int nb = 0; nb < NB; ++nb) {
+      const half8 bf = dequant8(dword_of(bw[nb], j), s2[nb], mask, magic);
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[nb], af[j & 1][mb], acc[mb][nb], 0, 0, 0);
+      for (int mb = 0; mb < NMB; ++mb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf, af[j & 1][mb], acc[mb][nb], 0, 0, 0);
+    }
   }
 }
 
-// Four stages as distinct LDS objects: the compiler then tracks each
-// stage's direct-to-LDS loads separately instead of waiting for all of them.
-struct Ring {
-  Stage *st[kStages];
-};
-
-template <int S>
-__device__ __forceinline__ Stage &stage_ref(const Ring &R) { return *R.st[S]; }
+// First weight row (within its matrix) of block nb of wavefront `wave` in a slice.
+template <int MODE, int NB>
+__device__ __forceinline__ int weight_row0(int slice, int wave, int nb) {
+  if (MODE == 0) {
+    const int hb = nb % (NB / 2);  // gate blocks first, then the up blocks of the same columns
+    return slice * Cfg<NB>::kHCols + (wave * (NB / 2) + hb) * 32;
+  }
+  return slice * Cfg<NB>::kOutCols + (wave * NB + nb) * 32;
+}
 
 // One work item: the tile's rows (NMB 32-row blocks, nrows valid) x this
-// workgroup's column slice, over all of K.  Every operand moves global -> LDS
-// with direct-to-LDS loads (no registers), kStages-1 chunks ahead:
-//   * A (token rows, fp16 slot order): wavefront instruction i fills
-//     segments [(4i + wave)*64, +64), i.e. 8 rows x 128 bytes, written in the
-//     XOR-swizzled layout;
-//   * packed weights: 32 B-rows x 32 bytes per instruction;
-//   * scales: 32 B-rows x 2 halves per instruction (a 2-byte direct-to-LDS
-//     load writes one zero-extended dword per lane).
-// Per chunk: wait for this wavefront's loads of the chunk, one barrier (all
-// wavefronts' loads of the chunk have landed; the oldest stage is free), issue
-// chunk c+kStages-1 into it, then dequant + MFMAs.  Past the last chunk the issue
+// workgroup's slice of weight rows, over all of K.  Loads, kStages-1 chunks
+// ahead, all direct-to-LDS:
+//   * token rows (fp16 slot order): wavefront instruction i fills segments
+//     [(4i + wave)*64, +64), i.e. 8 rows x 128 bytes, XOR-swizzled;
+//   * packed weights: 32 rows x 32 bytes per instruction;
+//   * scales: 32 rows x 2 halves per instruction (a 2-byte direct-to-LDS load
+//     writes one zero-extended dword per lane).
+// Per chunk: wait for this wavefront's loads of the chunk, one barrier (every
+// wavefront's loads have landed and the oldest stage is free), issue chunk
+// c+kStages-1 into it, then dequant + MFMAs.  Past the last chunk the issue
 // repeats the last chunk (loads are never skipped), so every wait counts the
 // same number of operations.
-template <int MODE, int NMB>
-__device__ __forceinline__ void gemm_tile(const GemmArgs &a, const Ring &R, const RowTables &rt, int e, int row0,
-                                          int nrows, int slice) {
+template <int MODE, int NB, int NMB>
+__device__ __forceinline__ void gemm_tile(const GemmArgs &a, const Ring<NB> &R, const RowTables &rt, int e,
+                                          int row0, int nrows, int slice) {
+  constexpr int S_ = Cfg<NB>::kStages;
+  constexpr int V = NMB + 2 * NB;  // direct-to-LDS loads per stage per wavefront
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform (scalar registers)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
   const int col = lane & 31, half = lane >> 5;
   const int nchunks = a.K / kKC;
-  constexpr int V = NMB + 4;  // direct-to-LDS loads per stage per wavefront
 
-  // Every load address is a wavefront-uniform base plus a 32-bit lane offset
-  // (bytes); the uniform parts advance by the chunk's K offset.
+  // Load addresses: a wavefront-uniform base plus a 32-bit lane offset (bytes).
   uint32_t aoff[NMB];
 #pragma unroll
   for (int i = 0; i < NMB; ++i) {
@@ -216,154 +219,150 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const Ring &R, cons
     const int r = p >> 3, c = (p & 7) ^ (r & 7);
     aoff[i] = ((uint32_t)rt.src[r] * (uint32_t)a.K + 8 * c) * 2;
   }
-  // B rows: lane -> (row lane>>1 of the 32-row block, half lane&1).
-  const int col2 = lane >> 1, hh = lane & 1;
-  const char *bbase[2];
-  const char *sbase[2];
-  uint32_t boff[2], soff;
+  const int col2 = lane >> 1, hh = lane & 1;  // weight-row loads: row lane>>1 of a block, half lane&1
+  const char *bbase[NB];
+  const char *sbase[NB];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int n0 = MODE == 0 ? slice * kGateUpColsPerWG + wave * 32 : slice * kDownColsPerWG + wave * 64 + nb * 32;
-    const uint8_t *B = (MODE == 0 && nb == 1) ? a.B1 : a.B0;
-    const uint16_t *Sc = (MODE == 0 && nb == 1) ? a.S1 : a.S0;
+  for (int nb = 0; nb < NB; ++nb) {
+    const int n0 = weight_row0<MODE, NB>(slice, wave, nb);
+    const bool up = MODE == 0 && nb >= NB / 2;
+    const uint8_t *B = up ? a.B1 : a.B0;
+    const uint16_t *Sc = up ? a.S1 : a.S0;
     bbase[nb] = reinterpret_cast<const char *>(B + ((size_t)e * a.N + n0) * (a.K / 2));
     sbase[nb] = reinterpret_cast<const char *>(Sc + ((size_t)e * a.N + n0) * (a.K / a.g));
-    boff[nb] = (uint32_t)col2 * (a.K / 2) + 16 * hh;
   }
-  soff = ((uint32_t)col2 * (a.K / a.g)) * 2;
+  const uint32_t boff = (uint32_t)col2 * (a.K / 2) + 16 * hh;
+  const uint32_t soff = ((uint32_t)col2 * (a.K / a.g)) * 2;
   const int g_shift = 31 - __clz(a.g);  // g is a power of two
   const char *abase = reinterpret_cast<const char *>(a.A);
 
-  auto issue = [&](Stage &st, int c) {
+  auto issue = [&](Stage<NB> &st, int c) {
     const int kc = c * kKC;
     const char *ab = abase + 2 * kc;
 #pragma unroll
     for (int i = 0; i < NMB; ++i)
       __builtin_amdgcn_global_load_lds(ab + aoff[i], as_lds(&st.a[(4 * i + wave) * 64]), 16, 0, 0);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int base = brow_of(wave, nb, 0) * 2;
-      __builtin_amdgcn_global_load_lds(bbase[nb] + kc / 2 + boff[nb], as_lds(&st.b[base]), 16, 0, 0);
+    for (int nb = 0; nb < NB; ++nb) {
+      const int base = brow_of<NB>(wave, nb, 0) * 2;
+      __builtin_amdgcn_global_load_lds(bbase[nb] + kc / 2 + boff, as_lds(&st.b[base]), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(sbase[nb] + 2 * ((kc + 32 * hh) >> g_shift) + soff, as_lds(&st.s[base]), 2,
                                        0, 0);
     }
   };
 
-  floatx16 acc[NMB][2];
+  floatx16 acc[NMB][NB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = floatx16{};
+    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = floatx16{};
 
   const int last = nchunks - 1;
   compiler_fence();
-  issue(stage_ref<0>(R), 0);
-  issue(stage_ref<1>(R), min(1, last));
-  if constexpr (kStages == 4) issue(stage_ref<2>(R), min(2, last));
+#pragma unroll
+  for (int st = 0; st < S_ - 1; ++st) issue(*R.st[st], min(st, last));
 
   auto step = [&](auto stage_tag, int c) {
     constexpr int S = decltype(stage_tag)::value;
-    compiler_fence();
-    wait_vmcnt<(kStages - 2) * V>();  // this wavefront's loads of chunk c are done
-    __builtin_amdgcn_s_barrier();  // ... and every other wavefront's; stage S-1 is free
-    compiler_fence();
-    issue(stage_ref<(S + kStages - 1) % kStages>(R), min(c + kStages - 1, last));
-    compiler_fence();
-    if (c < nchunks) mma_chunk<NMB>(acc, stage_ref<S>(R), wave, col, half);
+    if constexpr (S < S_) {
+      compiler_fence();
+      wait_vmcnt<(S_ - 2) * V>();    // this wavefront's loads of chunk c are done
+      __builtin_amdgcn_s_barrier();  // ... and every other wavefront's; stage S-1 is free
+      compiler_fence();
+      issue(*R.st[(S + S_ - 1) % S_], min(c + S_ - 1, last));
+      compiler_fence();
+      if (c < nchunks) mma_chunk<NB, NMB>(acc, *R.st[S], wave, col, half);
+    }
   };
-
-  for (int c0 = 0; c0 < nchunks; c0 += kStages) {
+  for (int c0 = 0; c0 < nchunks; c0 += S_) {
     step(std::integral_constant<int, 0>{}, c0);
     step(std::integral_constant<int, 1>{}, c0 + 1);
     step(std::integral_constant<int, 2>{}, c0 + 2);
-    if constexpr (kStages == 4) step(std::integral_constant<int, 3>{}, c0 + 3);
+    step(std::integral_constant<int, 3>{}, c0 + 3);
   }
   compiler_fence();
   wait_vmcnt<0>();  // no load of this tile may land in the next tile's stages
   compiler_fence();
 
   // Epilogue.  Accumulator element v of a lane: token row mb*32 + col of the
-  // tile, feature 8*(v/4) + 4*half + v%4 of the 32-feature block nb.
+  // tile, feature 8*(v/4) + 4*half + v%4 of its 32-feature block.
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
     const int r = mb * 32 + col;
     if (MODE == 0) {
-      // h = silu(g) * u, fp16.  Lanes l and l^32 hold the low and high four
-      // features of each 8-feature block; after one exchange each lane owns two
-      // whole blocks and stores them in fragment slot order (16 bytes each).
-      uint32_t hp[4][2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float hv[4];
+      for (int hb = 0; hb < NB / 2; ++hb) {
+        // h = silu(g) * u, fp16.  Lanes l and l^32 hold the low and high four
+        // features of each 8-feature group; after one exchange each lane owns
+        // two whole groups and stores them in fragment slot order (16 bytes).
+        uint32_t hp[4][2];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float gv = acc[mb][0][4 * i + q], uv = acc[mb][1][4 * i + q];
-          hv[q] = gv / (1.0f + __expf(-gv)) * uv;
+        for (int i = 0; i < 4; ++i) {
+          float hv[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float gv = acc[mb][hb][4 * i + q], uv = acc[mb][hb + NB / 2][4 * i + q];
+            hv[q] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
+          }
+          hp[i][0] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)hv[0], (_Float16)hv[1]});
+          hp[i][1] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)hv[2], (_Float16)hv[3]});
         }
-        hp[i][0] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)hv[0], (_Float16)hv[1]});
-        hp[i][1] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)hv[2], (_Float16)hv[3]});
-      }
-      uint32_t snd[4], rcv[4];
-      snd[0] = half ? hp[0][0] : hp[2][0];
-      snd[1] = half ? hp[0][1] : hp[2][1];
-      snd[2] = half ? hp[1][0] : hp[3][0];
-      snd[3] = half ? hp[1][1] : hp[3][1];
+        uint32_t snd[4], rcv[4];
+        snd[0] = half ? hp[0][0] : hp[2][0];
+        snd[1] = half ? hp[0][1] : hp[2][1];
+        snd[2] = half ? hp[1][0] : hp[3][0];
+        snd[3] = half ? hp[1][1] : hp[3][1];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) rcv[x] = __shfl_xor(snd[x], 32, kWave);
-      if (r < nrows) {
-        uint16_t *hout = static_cast<uint16_t *>(a.C) + (size_t)(row0 + r) * a.N + slice * kGateUpColsPerWG + wave * 32;
+        for (int x = 0; x < 4; ++x) rcv[x] = __shfl_xor(snd[x], 32, kWave);
+        if (r < nrows) {
+          uint16_t *hout =
+              static_cast<uint16_t *>(a.C) + (size_t)(row0 + r) * a.N + weight_row0<0, NB>(slice, wave, hb);
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-          const int grp = 2 * half + gi;  // 8-feature block this lane stores
-          const uint32_t lo0 = half ? rcv[2 * gi] : hp[grp][0], lo1 = half ? rcv[2 * gi + 1] : hp[grp][1];
-          const uint32_t hi0 = half ? hp[grp][0] : rcv[2 * gi], hi1 = half ? hp[grp][1] : rcv[2 * gi + 1];
-          uint4 o;
-          o.x = __builtin_amdgcn_perm(hi0, lo0, 0x05040100u);
-          o.y = __builtin_amdgcn_perm(hi0, lo0, 0x07060302u);
-          o.z = __builtin_amdgcn_perm(hi1, lo1, 0x05040100u);
-          o.w = __builtin_amdgcn_perm(hi1, lo1, 0x07060302u);
-          *reinterpret_cast<uint4 *>(hout + 8 * grp) = o;
+          for (int gi = 0; gi < 2; ++gi) {
+            const int grp = 2 * half + gi;  // 8-feature group this lane stores
+            const uint32_t lo0 = half ? rcv[2 * gi] : hp[grp][0], lo1 = half ? rcv[2 * gi + 1] : hp[grp][1];
+            const uint32_t hi0 = half ? hp[grp][0] : rcv[2 * gi], hi1 = half ? hp[grp][1] : rcv[2 * gi + 1];
+            uint4 o;
+            o.x = __builtin_amdgcn_perm(hi0, lo0, 0x05040100u);
+            o.y = __builtin_amdgcn_perm(hi0, lo0, 0x07060302u);
+            o.z = __builtin_amdgcn_perm(hi1, lo1, 0x05040100u);
+            o.w = __builtin_amdgcn_perm(hi1, lo1, 0x07060302u);
+            *reinterpret_cast<uint4 *>(hout + 8 * grp) = o;
+          }
         }
       }
     } else if (r < nrows) {
       const size_t row = (size_t)rt.dst[r] * a.N;
+      if (a.fused) {  // fp16 y rows in pair order, summed by the combine kernel
+        uint16_t *yrow = static_cast<uint16_t *>(a.C) + row;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
+        for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = slice * kDownColsPerWG + wave * 64 + nb * 32 + 8 * i + 4 * half;
-          const float y4[4] = {acc[mb][nb][4 * i], acc[mb][nb][4 * i + 1], acc[mb][nb][4 * i + 2],
-                               acc[mb][nb][4 * i + 3]};
-          if (a.fused) {  // fp16 y rows in pair order, summed by the combine kernel
+          for (int i = 0; i < 4; ++i) {
+            const int n = weight_row0<1, NB>(slice, wave, nb) + 8 * i + 4 * half;
             uint2 o;
-            o.x = __builtin_bit_cast(uint32_t, half2_t{(_Float16)y4[0], (_Float16)y4[1]});
-            o.y = __builtin_bit_cast(uint32_t, half2_t{(_Float16)y4[2], (_Float16)y4[3]});
-            *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.C) + row + n) = o;
-          } else {        // fp32 y rows in grouped order
-            *reinterpret_cast<float4 *>(static_cast<float *>(a.C) + row + n) = float4{y4[0], y4[1], y4[2], y4[3]};
+            o.x = __builtin_bit_cast(uint32_t, half2_t{(_Float16)acc[mb][nb][4 * i], (_Float16)acc[mb][nb][4 * i + 1]});
+            o.y = __builtin_bit_cast(uint32_t,
+                                     half2_t{(_Float16)acc[mb][nb][4 * i + 2], (_Float16)acc[mb][nb][4 * i + 3]});
+            *reinterpret_cast<uint2 *>(yrow + n) = o;
           }
-        }
+      } else {  // fp32 y rows in grouped order
+        float *yrow = static_cast<float *>(a.C) + row;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int n = weight_row0<1, NB>(slice, wave, nb) + 8 * i + 4 * half;
+            *reinterpret_cast<float4 *>(yrow + n) =
+                float4{acc[mb][nb][4 * i], acc[mb][nb][4 * i + 1], acc[mb][nb][4 * i + 2], acc[mb][nb][4 * i + 3]};
+          }
       }
     }
   }
 }
 
-template <int MODE>  // 0: gate/up + silu*mul -> h;  1: down + weighted combine
-__global__ __launch_bounds__(256, kWgPerCu) void moe_gemm_kernel(GemmArgs a) {
-  __shared__ Stage st0, st1, st2;
-#if STRATA_GEMM_STAGES == 4
-  __shared__ Stage st3;
-#else
-  Stage *const st3 = nullptr;
-#endif
-  __shared__ RowTables rt;
-#if STRATA_GEMM_STAGES == 4
-  const Ring R{{&st0, &st1, &st2, &st3}};
-#else
-  (void)st3;
-  const Ring R{{&st0, &st1, &st2}};
-#endif
-
+template <int MODE, int NB>
+__device__ __forceinline__ void gemm_persistent(const GemmArgs &a, const Ring<NB> &R, RowTables &rt) {
   const int tid = threadIdx.x;
   const int total = a.meta[0] * a.nslices;
   const int xcd = blockIdx.x % kXcds, lb = blockIdx.x / kXcds, per_xcd_wgs = gridDim.x / kXcds;
@@ -372,8 +371,8 @@ __global__ __launch_bounds__(256, kWgPerCu) void moe_gemm_kernel(GemmArgs a) {
   const int start = xcd * base + min(xcd, rem);
 
   for (int local = lb; local < cnt; local += per_xcd_wgs) {
-    const int Lw = start + local;
-    const int entry = Lw / a.nslices, slice = Lw - entry * a.nslices;
+    const int item = start + local;
+    const int entry = item / a.nslices, slice = item - entry * a.nslices;
     const Tile tile = a.tiles[entry];
     const int nmb = (tile.rows + 31) >> 5;
 
@@ -390,12 +389,22 @@ __global__ __launch_bounds__(256, kWgPerCu) void moe_gemm_kernel(GemmArgs a) {
     }
     __syncthreads();
     switch (nmb) {
-      case 1: gemm_tile<MODE, 1>(a, R, rt, tile.e, tile.row0, tile.rows, slice); break;
-      case 2: gemm_tile<MODE, 2>(a, R, rt, tile.e, tile.row0, tile.rows, slice); break;
-      case 3: gemm_tile<MODE, 3>(a, R, rt, tile.e, tile.row0, tile.rows, slice); break;
-      default: gemm_tile<MODE, 4>(a, R, rt, tile.e, tile.row0, tile.rows, slice); break;
+      case 1: gemm_tile<MODE, NB, 1>(a, R, rt, tile.e, tile.row0, tile.rows, slice); break;
+      case 2: gemm_tile<MODE, NB, 2>(a, R, rt, tile.e, tile.row0, tile.rows, slice); break;
+      case 3: gemm_tile<MODE, NB, 3>(a, R, rt, tile.e, tile.row0, tile.rows, slice); break;
+      default: gemm_tile<MODE, NB, 4>(a, R, rt, tile.e, tile.row0, tile.rows, slice); break;
     }
   }
+}
+
+// The ring stages are distinct LDS objects so the compiler tracks each
+// stage's direct-to-LDS loads separately instead of waiting for all of them.
+template <int MODE>  // 0: gate/up + silu*mul -> h;  1: down -> y
+__global__ __launch_bounds__(256, 2) void moe_gemm_nb2(GemmArgs a) {
+  __shared__ Stage<2> st0, st1, st2;
+  __shared__ RowTables rt;
+  const Ring<2> R{{&st0, &st1, &st2}};
+  gemm_persistent<MODE, 2>(a, R, rt);
 }
 
 // Tile list from the expert offsets: expert e gets ceil(count_e / rows_per_tile)
@@ -454,12 +463,19 @@ __global__ __launch_bounds__(1024) void prep_kernel(const int *__restrict__ offs
   }
 }
 
-// Persistent grid: kWgPerCu workgroups per CU (256 CUs), whole XCD rounds.
-int persistent_grid(long long work_upper) {
-  const long long cap = 256LL * kWgPerCu;
+// Persistent grid: wg_per_cu workgroups per CU (256 CUs), whole XCD rounds.
+int persistent_grid(long long work_upper, int wg_per_cu) {
+  const long long cap = 256LL * wg_per_cu;
   long long g = work_upper < cap ? work_upper : cap;
   g = (g + kXcds - 1) / kXcds * kXcds;
   return (int)(g < kXcds ? kXcds : g);
+}
+
+template <int MODE>
+hipError_t launch_gemm(GemmArgs args, long long tiles_upper, int matrix_rows, hipStream_t s) {
+  args.nslices = matrix_rows / (MODE == 0 ? Cfg<2>::kHCols : Cfg<2>::kOutCols);
+  moe_gemm_nb2<MODE><<<persistent_grid(tiles_upper * args.nslices, Cfg<2>::kWgPerCu), 256, 0, s>>>(args);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -501,12 +517,10 @@ hipError_t launch_ffn_gemm(const uint16_t *x, int T, int k, const FfnWeights &w,
   g.tiles = ws.tiles;
   g.meta = ws.meta;
   g.C = ws.h;
-  g.nslices = w.I / kGateUpColsPerWG;
   g.fused = 0;
   {
     KernelTimer timer("gemm_gateup", s);
-    moe_gemm_kernel<0><<<persistent_grid(tiles_upper * g.nslices), 256, 0, s>>>(g);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = launch_gemm<0>(g, tiles_upper, w.I, s)) != hipSuccess) return err;
   }
 
   GemmArgs d = g;
@@ -518,12 +532,10 @@ hipError_t launch_ffn_gemm(const uint16_t *x, int T, int k, const FfnWeights &w,
   d.N = w.H;
   d.K = w.I;
   d.C = fused ? static_cast<void *>(ws.y16) : static_cast<void *>(y_or_out);
-  d.nslices = w.H / kDownColsPerWG;
   d.fused = fused ? 1 : 0;
   {
     KernelTimer timer("gemm_down", s);
-    moe_gemm_kernel<1><<<persistent_grid(tiles_upper * d.nslices), 256, 0, s>>>(d);
-    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if ((err = launch_gemm<1>(d, tiles_upper, w.H, s)) != hipSuccess) return err;
   }
   if (fused) return launch_combine_pairs(ws.y16, topk_w, T, k, w.H, y_or_out, s);
   return hipSuccess;

@@ -21,8 +21,6 @@ constexpr int kPermuteSmallMax = 1024;
 // Grouped GEMM tiling (rows of one expert per tile, K per LDS chunk).
 constexpr int kGemmRows = 128;
 constexpr int kGemmKChunk = 64;
-constexpr int kGateUpColsPerWG = 128;     // h columns per workgroup (gate+up: 256 B rows)
-constexpr int kDownColsPerWG = 256;       // output columns per workgroup
 
 // GEMV (few pairs per expert): rows of one expert per work entry.
 constexpr int kGemvRows = 4;
