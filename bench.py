@@ -70,6 +70,52 @@ def counted_traffic(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
+# rocprofv3 kernel names -> library kernel names (and the workload bench.py runs them on)
+COUNTED_KERNELS = {
+    "moe_gemm_nb2<0>": ("gemm_gateup", "prefill"),
+    "moe_gemm_nb2<1>": ("gemm_down", "prefill"),
+    "gemv_gateup_kernel": ("gemv_gateup", "decode"),
+    "gemv_down_kernel": ("gemv_down", "decode"),
+}
+
+
+def record_traffic(fetch_csv: str, write_csv: str, prefill_workload: str) -> dict:
+    """HBM bytes per launch from two rocprofv3 --pmc runs of this script with
+    --calibrate-copy (FETCH_SIZE, then WRITE_SIZE; both in KiB per dispatch).
+    Each counter is scaled by what it reads for the 1 GiB device copy that
+    --calibrate-copy makes (the largest copy dispatch in the run)."""
+    import csv
+    import collections
+
+    def per_kernel(path, counter):
+        vals = collections.defaultdict(list)
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == counter:
+                    vals[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return vals
+
+    fetch, write = per_kernel(fetch_csv, "FETCH_SIZE"), per_kernel(write_csv, "WRITE_SIZE")
+    gib = float(1 << 30)
+    copy_f = max(max(v) for k, v in fetch.items() if "copyBuffer" in k or "copy_kernel" in k)
+    copy_w = max(max(v) for k, v in write.items() if "copyBuffer" in k or "copy_kernel" in k)
+    f_scale, w_scale = gib / (copy_f * 1024), gib / (copy_w * 1024)
+    out = {"_calibration": {"copy_bytes": int(gib), "fetch_kib": copy_f, "write_kib": copy_w,
+                            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4)}}
+    for pattern, (kernel, kind) in COUNTED_KERNELS.items():
+        fk = [v for k, vs in fetch.items() if pattern in k for v in vs]
+        wk = [v for k, vs in write.items() if pattern in k for v in vs]
+        if not fk or not wk:
+            continue
+        fb = float(np.mean(fk)) * 1024 * f_scale
+        wb = float(np.mean(wk)) * 1024 * w_scale
+        workload = prefill_workload if kind == "prefill" else "decode"
+        out[f"{kernel}@{workload}"] = {
+            "fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb),
+            "dispatches": min(len(fk), len(wk)), "source_sha": source_sha(kernel)}
+    return out
+
+
 def expert_weight_bytes(cfg, matrices: int = 3) -> int:
     n = matrices * cfg.H * cfg.I
     return n // 2 + 2 * (n // cfg.g)
@@ -254,7 +300,17 @@ def main(argv=None) -> int:
     ap.add_argument("--fused", type=int, default=1, help="1: fused weighted scatter-add; 0: y rows + combine")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic_counters.json from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args(argv)
+
+    if args.record_traffic:
+        rec = record_traffic(*args.record_traffic, prefill_workload=args.workload)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(rec, f, indent=1, sort_keys=True)
+            f.write("\n")
+        print(json.dumps(rec, indent=1, sort_keys=True))
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the MoE layer here is single-GPU (no sharding or collectives); "
