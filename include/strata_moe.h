@@ -132,10 +132,10 @@ int strata_moe_permute(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k,
  *   topk_w    in  float32 [T*k] routing weights, or NULL.
  *   y_or_out  out float32:
  *             topk_w != NULL: out[T][H] = sum_j topk_w[t][j] * y(t, j); the
- *                 library overwrites all of out.  On the matrix-core path the
- *                 expert outputs pass through fp16 rows in workspace and are
- *                 summed in j order by a final kernel; both paths are
- *                 deterministic;
+ *                 library overwrites all of out.  The expert outputs pass
+ *                 through fp16 rows in workspace (pair order) and a final
+ *                 kernel sums each token's k rows in j order in fp32, so the
+ *                 result is deterministic;
  *             topk_w == NULL: y[T*k][H] in grouped order, row i = the expert
  *                 output of pair perm[i] (deterministic); finish the layer
  *                 with strata_moe_combine.
@@ -193,8 +193,8 @@ const char *strata_moe_last_error(void);
  *                               (static strings) in first-launch order and
  *                               returns how many there are.
  * Kernel names: route_topk, permute_small, permute_hist, permute_scan,
- * permute_scatter, ffn_plan, gemm_gateup, gemm_down, zero_out, gemv_gateup,
- * gemv_down, combine.
+ * permute_scatter, ffn_prep, gemm_gateup, gemm_down, gemv_gateup, gemv_down,
+ * combine.
  */
 int strata_moe_timing_enable(int32_t on);
 int strata_moe_timing_query(const char *kernel, int32_t *launches, double *total_ms);

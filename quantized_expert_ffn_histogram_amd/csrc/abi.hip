@@ -95,13 +95,13 @@ namespace strata {
 
 namespace {
 size_t up256(size_t b) { return (b + 255) / 256 * 256; }
+// Tiles of the GEMM path: each expert's rows in kGemmRows pieces.
 long long max_tiles(long long pairs, int E) {
-  const long long gemm = (pairs + kGemmRows - 1) / kGemmRows + std::min<long long>(E, pairs);
-  const long long gemv = (pairs + kGemvRows - 1) / kGemvRows + std::min<long long>(E, pairs);
-  return std::max(gemm, gemv) + 1;
+  return (pairs + kGemmRows - 1) / kGemmRows + std::min<long long>(E, pairs) + 1;
 }
 }  // namespace
 
+// Regions: xq, h, y16, tiles, meta (256 B).
 size_t ffn_workspace_bytes(long long T, int k, int E, int H, int I) {
   const long long pairs = T * k;
   return up256((size_t)T * H * 2) + up256((size_t)pairs * I * 2) + up256((size_t)pairs * H * 2) +

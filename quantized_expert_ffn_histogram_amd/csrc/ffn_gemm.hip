@@ -435,12 +435,6 @@ __device__ __forceinline__ void plan_tiles(const int *__restrict__ offsets, int 
   if (e == 1023) meta[0] = part[1023];
 }
 
-__global__ __launch_bounds__(1024) void plan_kernel(const int *__restrict__ offsets, int E, int rows_per_tile,
-                                                    Tile *__restrict__ tiles, int *__restrict__ meta) {
-  __shared__ int part[1024];
-  plan_tiles(offsets, E, rows_per_tile, tiles, meta, part);
-}
-
 // Prologue of the GEMM path: block 0 builds the tile list; every block
 // converts x (bf16) to fp16 in fragment slot order (grid-stride, 8 elements
 // per thread).
@@ -479,13 +473,6 @@ hipError_t launch_gemm(GemmArgs args, long long tiles_upper, int matrix_rows, hi
 }
 
 }  // namespace
-
-hipError_t launch_plan(const int *offsets, int E, int rows_per_tile, Tile *tiles, int *meta,
-                       hipStream_t s) {
-  KernelTimer timer("ffn_plan", s);
-  plan_kernel<<<1, 1024, 0, s>>>(offsets, E, rows_per_tile, tiles, meta);
-  return hipGetLastError();
-}
 
 hipError_t launch_ffn_gemm(const uint16_t *x, int T, int k, const FfnWeights &w, const int *offsets,
                            const int *perm, const float *topk_w, float *y_or_out,

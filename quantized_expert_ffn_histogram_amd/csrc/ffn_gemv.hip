@@ -8,30 +8,40 @@
 // each decode token is a fresh trip through the weights, with one token plus
 // up to three drafts verified in one pass ("两天移植，预填充提速8倍：Strata引擎
 // 实测" (kongchang.com), section "Strata快在哪：不是魔法，是物流").  Only the
-// experts selected this step are touched: the work list holds one entry per
-// (expert, up to kGemvRows grouped rows).
+// experts selected this step are touched.
+//
+// Work list: entry i is the i-th expert (in index order) with a non-zero
+// count; every workgroup finds its expert from the offsets itself (a block
+// scan of the non-empty flags), so no planning kernel runs first.  An expert
+// holds at most T <= 16 pairs here (a token picks an expert at most once);
+// its weights are loaded into registers once and applied to its rows one
+// after another.  All weight loads of a wavefront are issued before any arithmetic,
+// so each lane has 8 (gate/up) or 8 (down) 16-byte loads in flight.
 //
 // Dot products: a dword of 8 nibbles gives four fp16 pairs (1024 + u_m,
 // 1024 + u_{m+4}) with one shift and one and-or; v_dot2_f32_f16 accumulates
 // x * (1024 + u) in fp32, and per lane (32 K values, inside one group since
 // g >= 32) the exact identity  sum x*q*s = s * (sum x*(1024+u) - 1032 * sum x)
-// removes the offset.  x is converted to fp16 pairs in the same slot order
-// once per work item.
+// removes the offset.  Activations are converted to fp16 pairs in the same
+// slot order.
 //
-//   gemv_gateup: work item = (entry, 16 h columns); wavefront = 4 columns; for
-//                each column the gate row and the up row are reduced across
-//                the wavefront and lane 0 writes h = silu(g)*u (fp16).
-//   gemv_down:   work item = 8 output rows of H for ALL entries (each expert's
-//                down rows are read once overall).  Wavefront w takes entries
-//                w, w+4, ...; per-token partial sums go to LDS in entry order and
-//                the four wavefronts' slots are added in fixed order, so the
-//                combined output is deterministic without atomics.
+//   gemv_gateup: workgroup = (entry, 16 h columns); wavefront = 4 columns,
+//                gate and up rows; lane 0 writes h = silu(g)*u (fp16).
+//   gemv_down:   workgroup = (entry, 2048/(I/32) output rows); each output
+//                row is reduced over I/32 lanes.  Fused combine: y goes to
+//                fp16 rows in pair order and the combine kernel of the
+//                matrix-core path sums each token's k rows in j order
+//                (deterministic, no atomics).
 #include "moe_internal.h"
 
 namespace strata {
 namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kGateUpCols = 16;  // h columns per workgroup (4 per wavefront)
+constexpr int kDownIter = 8;     // 16-byte weight loads per lane in gemv_down
+constexpr int kMaxChunks = kGemvMaxHidden / 2048;
 
 __device__ __forceinline__ half2_t magic_pair(uint32_t d, int m) {
   return __builtin_bit_cast(half2_t, ((d >> (4 * m)) & 0x000F000Fu) | 0x64006400u);
@@ -74,167 +84,227 @@ __device__ __forceinline__ float dot32(const uint4 wq, const half2_t *xp, float 
   return s * (acc - 1032.0f * xsum);
 }
 
+__device__ __forceinline__ float half_bits_to_float(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
+
+// Makes the compiler treat v as redefined here: it waits for v's load at this
+// point (so loads issued together are waited for together), and work derived
+// from v (the nibble unpacking) stays inside the row loop instead of being
+// hoisted out and held in registers for every row.
+__device__ __forceinline__ void opaque(uint4 &v) {
+  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+
 struct GemvArgs {
   const uint16_t *x;      // bf16 [T][H]
   const uint8_t *gate, *up, *down;
   const uint16_t *gate_s, *up_s, *down_s;
-  int T, H, I, g, k;
+  int T, H, I, g, k, E;
+  const int *offsets;     // [E+1]
   const int *perm;
   const float *topk_w;
-  const Tile *tiles;
-  const int *meta;
-  uint16_t *h;            // fp16 [pairs][I]
-  float *out;             // fused: [T][H]; else y [pairs][H]
+  uint16_t *h;            // fp16 [pairs][I], grouped order
+  float *out;             // not fused: y [pairs][H] in grouped order
+  uint16_t *y16;          // fused: fp16 y [pairs][H] in pair order, summed by the combine kernel
   int fused;
 };
 
-// H <= 4096: a lane covers K values [32*lane + 2048*c, +32) for c < H/2048 (or the
-// first H/32 lanes when H < 2048).
-constexpr int kMaxChunks = kGemvMaxHidden / 2048;
+struct Entry {
+  int e, row0, rows, nnz;  // e < 0: no such entry
+};
 
-__global__ __launch_bounds__(256) void gemv_gateup_kernel(GemvArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int ntiles = a.meta[0];
-  const int colsets = a.I / kGemvGateUpColsPerWG;
-  const int item = blockIdx.x;
-  if (item >= ntiles * colsets) return;
-  const int entry = item / colsets, cs = item - entry * colsets;
-  const Tile tile = a.tiles[entry];
-  const int e = tile.e, nrows = tile.rows;
-
-  const int nchunks = (a.H + 2047) / 2048;
-  const bool active = 32 * lane < min(a.H, 2048);
-
-  // x fragments of the tile's tokens, fp16 pairs in slot order, and their sums.
-  half2_t xp[kGemvRows][kMaxChunks][16];
-  float xs[kGemvRows][kMaxChunks];
+// The `entry`-th expert with a non-zero count (experts in index order) and the
+// number of such experts.  Block-wide (256 threads, E <= 1024), uniform result.
+__device__ Entry find_entry(const int *__restrict__ offsets, int E, int entry) {
+  __shared__ int wave_tot[4];
+  __shared__ Entry found;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int lo[5];
 #pragma unroll
-  for (int r = 0; r < kGemvRows; ++r)
+  for (int i = 0; i < 5; ++i) lo[i] = offsets[min(4 * tid + i, E)];  // unconditional loads, clamped
+  int cnt = 0;
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      xs[r][c] = 0.0f;
-      for (int i = 0; i < 16; ++i) xp[r][c][i] = half2_t{};
-      if (r < nrows && c < nchunks && active) {
-        const int t = a.perm[tile.row0 + r] / a.k;
-        const uint4 *src = reinterpret_cast<const uint4 *>(a.x + (size_t)t * a.H + 2048 * c + 32 * lane);
+  for (int i = 0; i < 4; ++i) cnt += (4 * tid + i < E && lo[i + 1] > lo[i]) ? 1 : 0;
+  int incl = cnt;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) bf16x8_pairs(src[q], &xp[r][c][4 * q]);
-        float s = 0.0f;
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int v = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += v;
+  }
+  if (lane == kWave - 1) wave_tot[wave] = incl;
+  if (tid == 0) found = Entry{-1, 0, 0, 0};
+  __syncthreads();
+  int base = 0, nnz = 0;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s += pair_sum(xp[r][c][i]);
-        xs[r][c] = s;
-      }
-    }
-
-  const int kb = a.H / 2, ng = a.H / a.g;
-#pragma unroll 1
-  for (int cc = 0; cc < kGemvGateUpColsPerWG / 4; ++cc) {
-    const int n = cs * kGemvGateUpColsPerWG + wave * (kGemvGateUpColsPerWG / 4) + cc;
-    float gs[kGemvRows], us[kGemvRows];
+  for (int w = 0; w < 4; ++w) {
+    base += w < wave ? wave_tot[w] : 0;
+    nnz += wave_tot[w];
+  }
+  int r = entry - (base + incl - cnt);
+  if (r >= 0 && r < cnt) {
 #pragma unroll
-    for (int r = 0; r < kGemvRows; ++r) gs[r] = us[r] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      if (c < nchunks && active) {
-        const size_t row = (size_t)e * a.I + n;
-        const int kk = 2048 * c + 32 * lane;
-        const uint4 wg = *reinterpret_cast<const uint4 *>(a.gate + row * kb + kk / 2);
-        const uint4 wu = *reinterpret_cast<const uint4 *>(a.up + row * kb + kk / 2);
-        const float sg = (float)__builtin_bit_cast(_Float16, a.gate_s[row * ng + kk / a.g]);
-        const float su = (float)__builtin_bit_cast(_Float16, a.up_s[row * ng + kk / a.g]);
-#pragma unroll
-        for (int r = 0; r < kGemvRows; ++r) {
-          if (r < nrows) {
-            gs[r] += dot32(wg, xp[r][c], xs[r][c], sg);
-            us[r] += dot32(wu, xp[r][c], xs[r][c], su);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kGemvRows; ++r) {
-      if (r < nrows) {
-        const float gv = group_sum<64>(gs[r]);
-        const float uv = group_sum<64>(us[r]);
-        if (lane == 0) {
-          const float hv = gv / (1.0f + __expf(-gv)) * uv;
-          reinterpret_cast<_Float16 *>(a.h)[(size_t)(tile.row0 + r) * a.I + n] = (_Float16)hv;
-        }
-      }
+    for (int i = 0; i < 4; ++i) {
+      const bool nz = 4 * tid + i < E && lo[i + 1] > lo[i];
+      if (nz && r == 0) found = Entry{4 * tid + i, lo[i], lo[i + 1] - lo[i], 0};
+      r -= nz ? 1 : 0;
     }
   }
+  __syncthreads();
+  Entry out = found;
+  out.nnz = nnz;
+  return out;
+}
+
+// A lane covers K values [32*lane + 2048*c, +32) for c < NCH = ceil(H/2048)
+// (only the first H/32 lanes when H < 2048).
+template <int NCH>
+__global__ __launch_bounds__(256, NCH == 1 ? 4 : 2) void gemv_gateup_kernel(GemvArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int colsets = a.I / kGateUpCols;
+  const int entry = blockIdx.x / colsets, cs = blockIdx.x - entry * colsets;
+  const Entry en = find_entry(a.offsets, a.E, entry);
+  if (en.e < 0) return;
+
+  // Lanes past H (H < 2048) load lane 0's data and get a zero scale, so every
+  // load is unconditional and all of them are in flight together.
+  const bool active = 32 * lane < a.H;
+  const int kl = active ? 32 * lane : 0;
+  const int kb = a.H / 2, ng = a.H / a.g;
+  const int n0 = cs * kGateUpCols + wave * 4;
+
+  // The first row's pair index is loaded before the weights: vector loads
+  // complete in order, so the x loads that depend on it wait only for it.
+  int p_first = a.perm[en.row0];
+  // This wavefront's gate and up rows (4 columns) and their scales (fp16 bits).
+  uint4 wg[4][NCH], wu[4][NCH];
+  uint32_t sgb[4][NCH], sub_[4][NCH];
+#pragma unroll
+  for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const size_t row = (size_t)en.e * a.I + n0 + cc;
+      const int kk = 2048 * c + kl;
+      wg[cc][c] = *reinterpret_cast<const uint4 *>(a.gate + row * kb + kk / 2);
+      wu[cc][c] = *reinterpret_cast<const uint4 *>(a.up + row * kb + kk / 2);
+      sgb[cc][c] = a.gate_s[row * ng + kk / a.g];
+      sub_[cc][c] = a.up_s[row * ng + kk / a.g];
+    }
+  asm volatile("" : "+v"(p_first) : : "memory");  // all of the above are issued before p_first is used
+  const float on = active ? 1.0f : 0.0f;
+
+  auto one_row = [&](int t, int r) {
+    uint4 xv[NCH][4];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        xv[c][q] = reinterpret_cast<const uint4 *>(a.x + (size_t)t * a.H + 2048 * c + kl)[q];
+    // One wait for this row's x loads (issued together); the weights and
+    // scales are pinned here too (see opaque()).
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) opaque(xv[c][q]);
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        opaque(wg[cc][c]);
+        opaque(wu[cc][c]);
+        asm volatile("" : "+v"(sgb[cc][c]), "+v"(sub_[cc][c]));
+      }
+    float gs[4] = {0.f, 0.f, 0.f, 0.f}, us[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      half2_t xp[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bf16x8_pairs(xv[c][q], &xp[4 * q]);
+      float xs = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xs += pair_sum(xp[i]);
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        gs[cc] += dot32(wg[cc][c], xp, xs, on * half_bits_to_float((uint16_t)sgb[cc][c]));
+        us[cc] += dot32(wu[cc][c], xp, xs, on * half_bits_to_float((uint16_t)sub_[cc][c]));
+      }
+    }
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const float gv = group_sum<kWave>(gs[cc]);
+      const float uv = group_sum<kWave>(us[cc]);
+      if (lane == 0) {
+        const float hv = gv / (1.0f + __expf(-gv)) * uv;
+        reinterpret_cast<_Float16 *>(a.h)[(size_t)(en.row0 + r) * a.I + n0 + cc] = (_Float16)hv;
+      }
+    }
+  };
+  one_row(p_first / a.k, 0);
+  for (int r = 1; r < en.rows; ++r) one_row(a.perm[en.row0 + r] / a.k, r);
 }
 
 template <int LPR>  // lanes per down row = I / 32
-__global__ __launch_bounds__(256) void gemv_down_kernel(GemvArgs a) {
-  constexpr int RPI = kWave / LPR;  // rows per wavefront instruction
-  constexpr int ITER = (kGemvDownRowsPerWG + RPI - 1) / RPI;
-  __shared__ float part[4][kGemvMaxTokens][kGemvDownRowsPerWG];
+__global__ __launch_bounds__(256, 4) void gemv_down_kernel(GemvArgs a) {
+  constexpr int RPI = kWave / LPR;              // rows per wavefront instruction
+  constexpr int kRowsWG = 4 * kDownIter * RPI;  // output rows per workgroup
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int sub = lane % LPR, rsel = lane / LPR;
-  const int nbase = blockIdx.x * kGemvDownRowsPerWG;
-  const int ntiles = a.meta[0];
-
-  if (a.fused)
-    for (int i = tid; i < 4 * kGemvMaxTokens * kGemvDownRowsPerWG; i += 256) (&part[0][0][0])[i] = 0.0f;
-  __syncthreads();
+  const int nslices = (a.H + kRowsWG - 1) / kRowsWG;
+  const int entry = blockIdx.x / nslices, slice = blockIdx.x - entry * nslices;
+  const Entry en = find_entry(a.offsets, a.E, entry);
+  if (en.e < 0) return;
 
   const int kb = a.I / 2, ng = a.I / a.g;
-  for (int entry = wave; entry < ntiles; entry += 4) {
-    const Tile tile = a.tiles[entry];
-    const int e = tile.e, nrows = tile.rows;
-    half2_t hp[kGemvRows][16];
-    float hs[kGemvRows], wt[kGemvRows];
-    int tok[kGemvRows];
+  const int nbase = slice * kRowsWG + wave * kDownIter * RPI + rsel;  // row of iteration it: nbase + it*RPI
+
+  // Row r's h fragment (fp16, 32 values per lane) and output row; the first
+  // row's are issued before the weights.
+  auto load_row = [&](int r, uint4 (&hv)[4], int &dst) {
+    const int gi = en.row0 + r;
+    dst = a.fused ? a.perm[gi] : gi;
+    const uint4 *src = reinterpret_cast<const uint4 *>(a.h + (size_t)gi * a.I + 32 * sub);
 #pragma unroll
-    for (int r = 0; r < kGemvRows; ++r) {
-      hs[r] = 0.0f;
-      wt[r] = 0.0f;
-      tok[r] = 0;
-      if (r < nrows) {
-        const int p = a.perm[tile.row0 + r];
-        tok[r] = p / a.k;
-        if (a.fused) wt[r] = a.topk_w[p];
-        const uint4 *src = reinterpret_cast<const uint4 *>(a.h + (size_t)(tile.row0 + r) * a.I + 32 * sub);
+    for (int q = 0; q < 4; ++q) hv[q] = src[q];
+  };
+  uint4 hv[4];
+  int dst;
+  load_row(0, hv, dst);
+
+  // Rows past H (only when H < 2048/(I/32)*32) load row 0 and are not stored.
+  uint4 wq[kDownIter];
+  uint32_t sdb[kDownIter];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) f16x8_pairs(src[q], &hp[r][4 * q]);
-        float s = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) s += pair_sum(hp[r][i]);
-        hs[r] = s;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) hp[r][i] = half2_t{};
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < ITER; ++it) {
-      const int nl = it * RPI + rsel;  // local output row
-      const bool rowok = nl < kGemvDownRowsPerWG;
-      const int n = nbase + (rowok ? nl : 0);
-      const size_t row = (size_t)e * a.H + n;
-      const uint4 wq = *reinterpret_cast<const uint4 *>(a.down + row * kb + 16 * sub);
-      const float sd = (float)__builtin_bit_cast(_Float16, a.down_s[row * ng + (32 * sub) / a.g]);
-#pragma unroll
-      for (int r = 0; r < kGemvRows; ++r) {
-        if (r < nrows) {
-          const float yv = group_sum<LPR>(dot32(wq, hp[r], hs[r], sd));
-          if (sub == 0 && rowok) {
-            if (a.fused)
-              part[wave][tok[r]][nl] += wt[r] * yv;
-            else
-              a.out[(size_t)(tile.row0 + r) * a.H + n] = yv;
-          }
-        }
-      }
-    }
+  for (int it = 0; it < kDownIter; ++it) {
+    const int n = nbase + it * RPI;
+    const size_t row = (size_t)en.e * a.H + (n < a.H ? n : 0);
+    wq[it] = *reinterpret_cast<const uint4 *>(a.down + row * kb + 16 * sub);
+    sdb[it] = a.down_s[row * ng + (32 * sub) / a.g];
   }
-  if (!a.fused) return;
-  __syncthreads();
-  for (int i = tid; i < a.T * kGemvDownRowsPerWG; i += 256) {
-    const int t = i / kGemvDownRowsPerWG, nl = i - t * kGemvDownRowsPerWG;
-    const float v = ((part[0][t][nl] + part[1][t][nl]) + part[2][t][nl]) + part[3][t][nl];
-    a.out[(size_t)t * a.H + nbase + nl] = v;
+
+  for (int r = 0; r < en.rows; ++r) {
+    if (r > 0) load_row(r, hv, dst);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) opaque(hv[q]);
+#pragma unroll
+    for (int it = 0; it < kDownIter; ++it) {
+      opaque(wq[it]);
+      asm volatile("" : "+v"(sdb[it]));
+    }
+    half2_t hp[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) f16x8_pairs(hv[q], &hp[4 * q]);
+    float hs = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) hs += pair_sum(hp[i]);
+#pragma unroll
+    for (int it = 0; it < kDownIter; ++it) {
+      const float yv = group_sum<LPR>(dot32(wq[it], hp, hs, half_bits_to_float((uint16_t)sdb[it])));
+      const int n = nbase + it * RPI;
+      if (sub == 0 && n < a.H) {
+        if (a.fused)
+          reinterpret_cast<_Float16 *>(a.y16)[(size_t)dst * a.H + n] = (_Float16)yv;
+        else
+          a.out[(size_t)dst * a.H + n] = yv;
+      }
+    }
   }
 }
 
@@ -242,16 +312,13 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(GemvArgs a) {
 
 bool gemv_supported(int T, int H, int I) {
   const bool pow2 = I >= 128 && I <= 2048 && (I & (I - 1)) == 0;
-  return T <= kGemvMaxTokens && H <= kGemvMaxHidden && (H <= 2048 ? (H & (H - 1)) == 0 : H % 2048 == 0) && pow2;
+  return T <= kGemvMaxTokens && H <= kGemvMaxHidden && (H & (H - 1)) == 0 && pow2;
 }
 
 hipError_t launch_ffn_gemv(const uint16_t *x, int T, int k, const FfnWeights &w, const int *offsets,
                            const int *perm, const float *topk_w, float *y_or_out,
                            const FfnWorkspace &ws, hipStream_t s) {
-  const long long pairs = (long long)T * k;
-  const long long tiles_upper = (pairs + kGemvRows - 1) / kGemvRows + std::min<long long>(w.E, pairs);
-  hipError_t err = launch_plan(offsets, w.E, kGemvRows, ws.tiles, ws.meta, s);
-  if (err != hipSuccess) return err;
+  const int entries = (int)std::min<long long>((long long)T * k, w.E);
   GemvArgs a{};
   a.x = x;
   a.gate = w.gate;
@@ -265,28 +332,40 @@ hipError_t launch_ffn_gemv(const uint16_t *x, int T, int k, const FfnWeights &w,
   a.I = w.I;
   a.g = w.g;
   a.k = k;
+  a.E = w.E;
+  a.offsets = offsets;
   a.perm = perm;
   a.topk_w = topk_w;
-  a.tiles = ws.tiles;
-  a.meta = ws.meta;
   a.h = ws.h;
   a.out = y_or_out;
+  a.y16 = ws.y16;
   a.fused = topk_w != nullptr;
   {
     KernelTimer timer("gemv_gateup", s);
-    gemv_gateup_kernel<<<(int)(tiles_upper * (w.I / kGemvGateUpColsPerWG)), 256, 0, s>>>(a);
+    const int grid = entries * (w.I / kGateUpCols);
+    if (w.H <= 2048)
+      gemv_gateup_kernel<1><<<grid, 256, 0, s>>>(a);
+    else
+      gemv_gateup_kernel<kMaxChunks><<<grid, 256, 0, s>>>(a);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int lpr = w.I / 32;
+  const int rows_wg = 4 * kDownIter * (kWave / lpr);
+  const int grid = entries * ((w.H + rows_wg - 1) / rows_wg);
+  {
+    KernelTimer timer("gemv_down", s);
+    switch (lpr) {
+      case 4: gemv_down_kernel<4><<<grid, 256, 0, s>>>(a); break;
+      case 8: gemv_down_kernel<8><<<grid, 256, 0, s>>>(a); break;
+      case 16: gemv_down_kernel<16><<<grid, 256, 0, s>>>(a); break;
+      case 32: gemv_down_kernel<32><<<grid, 256, 0, s>>>(a); break;
+      default: gemv_down_kernel<64><<<grid, 256, 0, s>>>(a); break;
+    }
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  const int grid = w.H / kGemvDownRowsPerWG;
-  KernelTimer timer("gemv_down", s);
-  switch (w.I / 32) {
-    case 4: gemv_down_kernel<4><<<grid, 256, 0, s>>>(a); break;
-    case 8: gemv_down_kernel<8><<<grid, 256, 0, s>>>(a); break;
-    case 16: gemv_down_kernel<16><<<grid, 256, 0, s>>>(a); break;
-    case 32: gemv_down_kernel<32><<<grid, 256, 0, s>>>(a); break;
-    default: gemv_down_kernel<64><<<grid, 256, 0, s>>>(a); break;
-  }
-  return hipGetLastError();
+  if (a.fused) return launch_combine_pairs(ws.y16, topk_w, T, k, w.H, y_or_out, s);
+  return hipSuccess;
 }
 
 }  // namespace strata

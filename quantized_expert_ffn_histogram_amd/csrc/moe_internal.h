@@ -23,11 +23,8 @@ constexpr int kGemmRows = 128;
 constexpr int kGemmKChunk = 64;
 
 // GEMV (few pairs per expert): rows of one expert per work entry.
-constexpr int kGemvRows = 4;
 constexpr int kGemvMaxTokens = 16;        // auto path picks GEMV at or below this T
 constexpr int kGemvMaxHidden = 4096;
-constexpr int kGemvDownRowsPerWG = 8;
-constexpr int kGemvGateUpColsPerWG = 16;
 
 // One unit of grouped work: `rows` consecutive grouped rows of expert `e`
 // starting at grouped row `row0`.
@@ -49,12 +46,12 @@ size_t permute_workspace_bytes(long long pairs, int E);
 hipError_t launch_permute(const int *ids, int pairs, int E, int *counts, int *offsets,
                           int *perm, int *inv_perm, void *ws, hipStream_t s);
 
-// Workspace carving for the FFN (h, tile list, counters).
+// Workspace carving for the FFN (activations, h, fp16 y rows, tile list).
 struct FfnWorkspace {
   uint16_t *xq;      // fp16 [T][H], fragment slot order (GEMM path)
   uint16_t *h;       // fp16 [pairs][I]
-  uint16_t *y16;     // fp16 [pairs][H], pair order (GEMM path, fused combine)
-  Tile *tiles;       // grouped-work list
+  uint16_t *y16;     // fp16 [pairs][H], pair order (fused combine)
+  Tile *tiles;       // grouped-work list (GEMM path)
   int *meta;         // meta[0] = number of tiles
   size_t bytes;
 };
@@ -73,8 +70,6 @@ hipError_t launch_combine(const float *y, const int *inv_perm, const float *topk
 // out[t] = sum_j topk_w[t*k+j] * y16[t*k+j] (fp16 rows in pair order), j in order.
 hipError_t launch_combine_pairs(const uint16_t *y16, const float *topk_w, int T, int k, int H, float *out,
                                 hipStream_t s);
-hipError_t launch_plan(const int *offsets, int E, int rows_per_tile, Tile *tiles, int *meta,
-                       hipStream_t s);
 
 inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 

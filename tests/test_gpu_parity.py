@@ -6,6 +6,8 @@ sum|err| / sum|ref| <= 5e-3.  Small layers are compared element by element in
 full; the full-size layers on sampled tokens and sampled grouped rows, which
 the oracle computes one by one.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -174,6 +176,8 @@ GEMV_CFGS = [
     synth.MoEConfig("gemv_t1", T=1, H=2048, I=512, E=64, k=10, g=64, seed=42),
     synth.MoEConfig("gemv_wide", T=8, H=4096, I=1024, E=32, k=8, g=128, seed=43),
     synth.MoEConfig("gemv_shared", T=12, H=1024, I=256, E=4, k=3, g=64, seed=44),
+    # largest envelope: E=1024 experts, k=32, 512 pairs
+    synth.MoEConfig("gemv_maxk", T=16, H=256, I=128, E=1024, k=32, g=32, seed=45),
 ]
 
 
@@ -187,6 +191,25 @@ def test_ffn_decode_paths(qe, cfg, path, monkeypatch):
     check_close(_np(det["y"]), ref["y"], "y")
     fus = _run_layer(qe, inp, fused=True)
     check_close(_np(fus["out"]), ref["out"], "out (fused)")
+
+
+def test_gemv_fused_repeatable_across_calls(qe, monkeypatch):
+    """The decode path's fused output (fp16 y rows in pair order, summed in j
+    order) is bitwise repeatable, and a different step in between (other
+    experts, other rows) leaves nothing behind that changes the next call."""
+    monkeypatch.setenv("STRATA_MOE_FFN_PATH", "gemv")
+    cfg = synth.config("decode")
+    inp = inputs(cfg)
+    steps = synth.decode_steps(cfg, 2)
+    a = _run_layer(qe, inp, fused=True)
+    other = dataclasses.replace(inp, logits=steps[1][0], x_bf16=steps[1][1])
+    mid = _run_layer(qe, other, fused=True)
+    ref = oracle.moe_layer(other.logits, other.x_bf16, other.weights, cfg.k, cfg.g)
+    check_close(_np(mid["out"]), ref["out"], "decode step 1 out")
+    b = _run_layer(qe, inp, fused=True)
+    assert (_np(a["out"]) == _np(b["out"])).all()
+    ref = oracle.moe_layer(inp.logits, inp.x_bf16, inp.weights, cfg.k, cfg.g)
+    check_close(_np(b["out"]), ref["out"], "decode out")
 
 
 # ----------------------------------------------------------------------------- ffn, full-size sampled
