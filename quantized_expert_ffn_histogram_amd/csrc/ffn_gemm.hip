@@ -25,9 +25,11 @@
 // lane's accumulator holds runs of four consecutive features of one token.
 //
 // Dequant in registers: a dword holds 8 nibbles u_0..u_7 (even K low); the
-// pair (u_m, u_{m+4}) goes into the mantissas of two fp16 1024.0 values with a
-// shift and an and-or, minus 1032 gives q exactly, times the fp16 group scale
-// gives fp16(q*s) with a single rounding.  Fragment slot e therefore holds K
+// pair (u_m, u_{m+4}) goes into the mantissas of two fp16 values with one
+// and-or: the low nibbles of each half-word give 1024 + u (minus 1032 is q
+// exactly), the next nibbles give 1024 + 16u (times 1/16 minus 72 is q
+// exactly, one fma); the upper byte pair needs one shift.  Times the fp16 group
+// scale gives fp16(q*s) with a single rounding: 13 VALU ops per 8 weights.  Fragment slot e therefore holds K
 // offset (e>>1) + 4*(e&1) of its 8-block; token rows are stored in the same
 // slot order, so the contraction runs over the true K.
 //
@@ -52,13 +54,15 @@ constexpr int kKC = kGemmKChunk;            // K per pipelined chunk (64)
 constexpr int kSegs = kKC / 8;              // 16-byte segments per token row per chunk
 constexpr int kStageSegs = kGemmRows * kSegs;
 
+constexpr int kWaves = 4;  // wavefronts per workgroup
+
 template <int NB>
 struct Cfg {
-  static constexpr int kStages = 3;                // LDS ring depth
+  static constexpr int kStages = 3;                    // LDS ring depth
   static constexpr int kWgPerCu = 2;
-  static constexpr int kBRows = 4 * NB * 32;       // weight rows per workgroup
-  static constexpr int kHCols = 2 * NB * 32;       // gate/up: h columns per workgroup
-  static constexpr int kOutCols = 4 * NB * 32;     // down: output features per workgroup
+  static constexpr int kBRows = kWaves * NB * 32;      // weight rows per workgroup
+  static constexpr int kHCols = kWaves * NB * 16;      // gate/up: h columns per workgroup
+  static constexpr int kOutCols = kWaves * NB * 32;    // down: output features per workgroup
 };
 
 struct GemmArgs {
@@ -112,16 +116,26 @@ __device__ __forceinline__ void wait_vmcnt() {
 // reads on their side of the explicit waits and barriers.
 __device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
 
+// (a & m) | o as one v_and_or_b32 (m wavefront-uniform in an SGPR); written
+// out because the compiler otherwise emits a separate and + or with literals.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(o));
+  return r;
+}
 __device__ __forceinline__ half8 dequant8(uint32_t d, half2_t s2, uint32_t mask, uint32_t magic) {
   const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
-  const uint32_t r0 = (d & mask) | magic;
-  const uint32_t r1 = ((d >> 4) & mask) | magic;
-  const uint32_t r2 = ((d >> 8) & mask) | magic;
-  const uint32_t r3 = ((d >> 12) & mask) | magic;
+  const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const half2_t off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  const uint32_t d8 = d >> 8;
+  const uint32_t r0 = and_or(d, mask, magic);
+  const uint32_t r1 = and_or(d, mask << 4, magic);
+  const uint32_t r2 = and_or(d8, mask, magic);
+  const uint32_t r3 = and_or(d8, mask << 4, magic);
   const half2_t h0 = (__builtin_bit_cast(half2_t, r0) - off) * s2;
-  const half2_t h1 = (__builtin_bit_cast(half2_t, r1) - off) * s2;
+  const half2_t h1 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, r1), sixteenth, off16) * s2;
   const half2_t h2 = (__builtin_bit_cast(half2_t, r2) - off) * s2;
-  const half2_t h3 = (__builtin_bit_cast(half2_t, r3) - off) * s2;
+  const half2_t h3 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, r3), sixteenth, off16) * s2;
   return half8{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
 }
 
@@ -205,26 +219,37 @@ template <int MODE, int NB, int NMB>
 __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const Ring<NB> &R, const RowTables &rt, int e,
                                           int row0, int nrows, int slice) {
   constexpr int S_ = Cfg<NB>::kStages;
-  constexpr int V = NMB + 2 * NB;  // direct-to-LDS loads per stage per wavefront
+  // Token-row loads: 4*NMB instructions of 8 rows per stage, spread over the
+  // wavefronts; when they do not divide evenly the surplus instructions
+  // repeat earlier ones (same bytes to the same LDS place), so every
+  // wavefront issues the same count.
+  constexpr int kAInst = 4 * NMB, AI = (kAInst + kWaves - 1) / kWaves;
+  constexpr int V = AI + 2 * NB;  // direct-to-LDS loads per stage per wavefront
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
   const int col = lane & 31, half = lane >> 5;
   const int nchunks = a.K / kKC;
 
   // Load addresses: a wavefront-uniform base plus a 32-bit lane offset (bytes).
-  uint32_t aoff[NMB];
+  uint32_t aoff[AI];
+  int aseg[AI];  // first LDS segment of each token-row instruction
 #pragma unroll
-  for (int i = 0; i < NMB; ++i) {
-    const int p = (4 * i + wave) * 64 + lane;
+  for (int i = 0; i < AI; ++i) {
+    aseg[i] = ((kWaves * i + wave) % kAInst) * 64;
+    const int p = aseg[i] + lane;
     const int r = p >> 3, c = (p & 7) ^ (r & 7);
     aoff[i] = ((uint32_t)rt.src[r] * (uint32_t)a.K + 8 * c) * 2;
   }
   const int col2 = lane >> 1, hh = lane & 1;  // weight-row loads: row lane>>1 of a block, half lane&1
+  // The last slice of a matrix whose rows the slice width does not divide
+  // has wavefronts past the end: they load row 0 (in bounds), take part in
+  // the loads and barriers, and store nothing.
+  const bool wave_rows_valid = weight_row0<MODE, NB>(slice, wave, 0) < a.N;
   const char *bbase[NB];
   const char *sbase[NB];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int n0 = weight_row0<MODE, NB>(slice, wave, nb);
+    const int n0 = wave_rows_valid ? weight_row0<MODE, NB>(slice, wave, nb) : 0;
     const bool up = MODE == 0 && nb >= NB / 2;
     const uint8_t *B = up ? a.B1 : a.B0;
     const uint16_t *Sc = up ? a.S1 : a.S0;
@@ -240,8 +265,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const Ring<NB> &R, 
     const int kc = c * kKC;
     const char *ab = abase + 2 * kc;
 #pragma unroll
-    for (int i = 0; i < NMB; ++i)
-      __builtin_amdgcn_global_load_lds(ab + aoff[i], as_lds(&st.a[(4 * i + wave) * 64]), 16, 0, 0);
+    for (int i = 0; i < AI; ++i) __builtin_amdgcn_global_load_lds(ab + aoff[i], as_lds(&st.a[aseg[i]]), 16, 0, 0);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int base = brow_of<NB>(wave, nb, 0) * 2;
@@ -314,7 +338,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const Ring<NB> &R, 
         snd[3] = half ? hp[1][1] : hp[3][1];
 #pragma unroll
         for (int x = 0; x < 4; ++x) rcv[x] = __shfl_xor(snd[x], 32, kWave);
-        if (r < nrows) {
+        if (r < nrows && wave_rows_valid) {
           uint16_t *hout =
               static_cast<uint16_t *>(a.C) + (size_t)(row0 + r) * a.N + weight_row0<0, NB>(slice, wave, hb);
 #pragma unroll
@@ -331,7 +355,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const Ring<NB> &R, 
           }
         }
       }
-    } else if (r < nrows) {
+    } else if (r < nrows && wave_rows_valid) {
       const size_t row = (size_t)rt.dst[r] * a.N;
       if (a.fused) {  // fp16 y rows in pair order, summed by the combine kernel
         uint16_t *yrow = static_cast<uint16_t *>(a.C) + row;
@@ -400,7 +424,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &a, const Ring<NB
 // The ring stages are distinct LDS objects so the compiler tracks each
 // stage's direct-to-LDS loads separately instead of waiting for all of them.
 template <int MODE>  // 0: gate/up + silu*mul -> h;  1: down -> y
-__global__ __launch_bounds__(256, 2) void moe_gemm_nb2(GemmArgs a) {
+__global__ __launch_bounds__(64 * kWaves, 2) void moe_gemm_nb2(GemmArgs a) {
   __shared__ Stage<2> st0, st1, st2;
   __shared__ RowTables rt;
   const Ring<2> R{{&st0, &st1, &st2}};
@@ -467,8 +491,9 @@ int persistent_grid(long long work_upper, int wg_per_cu) {
 
 template <int MODE>
 hipError_t launch_gemm(GemmArgs args, long long tiles_upper, int matrix_rows, hipStream_t s) {
-  args.nslices = matrix_rows / (MODE == 0 ? Cfg<2>::kHCols : Cfg<2>::kOutCols);
-  moe_gemm_nb2<MODE><<<persistent_grid(tiles_upper * args.nslices, Cfg<2>::kWgPerCu), 256, 0, s>>>(args);
+  const int width = MODE == 0 ? Cfg<2>::kHCols : Cfg<2>::kOutCols;
+  args.nslices = (matrix_rows + width - 1) / width;
+  moe_gemm_nb2<MODE><<<persistent_grid(tiles_upper * args.nslices, Cfg<2>::kWgPerCu), 64 * kWaves, 0, s>>>(args);
   return hipGetLastError();
 }
 
