@@ -11,12 +11,16 @@
 //     round (ballot over the expert id's bits) plus a running per-expert
 //     counter kept in LDS and advanced in round order.
 //
-// Large inputs: one wavefront per segment of kPermuteSeg consecutive pairs.
-//   1. seg_hist:   hist[e][s] = pairs of expert e in segment s
-//   2. seg_scan:   one workgroup turns hist into the exclusive scan over the
-//                  (e-major, s-minor) order: base[e][s] = first grouped slot
-//                  of expert e's pairs from segment s; also counts/offsets
-//   3. seg_scatter: each segment walks its pairs in order from base[.][s]
+// Large inputs: one workgroup (4 wavefronts) per segment of kPermuteSeg
+// consecutive pairs.
+//   1. seg_hist:    hist[s][e] = pairs of expert e in segment s
+//   2. seg_scan:    thread e turns column e of hist into the exclusive prefix
+//                   over segments, then one block scan over experts gives
+//                   counts/offsets: the first grouped slot of expert e's pairs
+//                   from segment s is offsets[e] + hist[s][e]
+//   3. seg_scatter: each wavefront counts its quarter of the segment, the
+//                   quarters' counts are prefix-summed per expert, and every
+//                   wavefront then places its pairs in order from there
 // Small inputs (<= kPermuteSmallMax pairs): one workgroup does all three.
 #include "moe_internal.h"
 
@@ -40,26 +44,21 @@ __device__ __forceinline__ uint64_t match_any(int key, int nbits) {
 
 __device__ __forceinline__ int id_bits(int E) { return 32 - __clz(E); }  // bits of E (sentinel)
 
-// Wavefront `wave` of the block walks pairs [p0, p1) (at most kPermuteSeg) in
-// rounds of 64 and places each at running[e] + rank; running[] lives in LDS.
-// All expert ids of the segment are loaded up front so their latency overlaps.
-__device__ __forceinline__ void scatter_rounds(const int *__restrict__ ids, int p0, int p1, int E,
-                                               int *running, int *__restrict__ perm,
-                                               int *__restrict__ inv_perm) {
-  constexpr int R = kPermuteSeg / kWave;
+// The calling wavefront places pairs [p0, p1) (at most kPermuteSeg, expert
+// ids preloaded in ev: pair p0 + q*64 + lane in ev[q], -1 past p1) in rounds
+// of 64: each goes to running[e] + its rank among equal experts in the round;
+// running[] lives in LDS and is advanced by the round's last lane of each
+// expert.
+template <int R>
+__device__ __forceinline__ void scatter_rounds(const int (&ev)[R], int p0, int p1, int E, int *running,
+                                               int *__restrict__ perm, int *__restrict__ inv_perm) {
   const int lane = threadIdx.x & (kWave - 1);
   const int nbits = id_bits(E);
-  int ev[R];
-#pragma unroll
-  for (int q = 0; q < R; ++q) {
-    const int p = p0 + q * kWave + lane;
-    ev[q] = p < p1 ? ids[p] : E;  // sentinel E never matches a real expert
-  }
 #pragma unroll
   for (int q = 0; q < R; ++q) {
     if (p0 + q * kWave >= p1) break;
     const int p = p0 + q * kWave + lane;
-    const int e = ev[q];
+    const int e = ev[q] >= 0 ? ev[q] : E;  // sentinel E never matches a real expert
     const uint64_t same = match_any(e, nbits);
     const int rank = __popcll(same & lanemask_lt(lane));
     const bool last = (same >> lane) == 1ull;  // highest lane of my group
@@ -76,99 +75,98 @@ __device__ __forceinline__ void scatter_rounds(const int *__restrict__ ids, int 
 }
 
 __global__ __launch_bounds__(256) void seg_hist_kernel(const int *__restrict__ ids, int pairs, int E,
-                                                       int nseg, int *__restrict__ hist) {
-  constexpr int R = kPermuteSeg / kWave;
-  __shared__ int h[4][kMaxExperts];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int s = blockIdx.x * 4 + wave;
-  for (int e = lane; e < E; e += kWave) h[wave][e] = 0;
-  int ev[R];
+                                                       int *__restrict__ hist) {
+  constexpr int R = kPermuteSeg / 256;
+  __shared__ int h[kMaxExperts];
+  const int tid = threadIdx.x, s = blockIdx.x;
   const int p0 = s * kPermuteSeg, p1 = min(pairs, p0 + kPermuteSeg);
+  int ev[R];
 #pragma unroll
   for (int q = 0; q < R; ++q) {
-    const int p = p0 + q * kWave + lane;
-    ev[q] = (s < nseg && p < p1) ? ids[p] : -1;
+    const int p = p0 + q * 256 + tid;
+    ev[q] = p < p1 ? ids[p] : -1;
   }
+  for (int e = tid; e < E; e += 256) h[e] = 0;
   __syncthreads();
 #pragma unroll
   for (int q = 0; q < R; ++q)
-    if (ev[q] >= 0) atomicAdd(&h[wave][ev[q]], 1);
+    if (ev[q] >= 0) atomicAdd(&h[ev[q]], 1);
   __syncthreads();
-  if (s < nseg)
-    for (int e = lane; e < E; e += kWave) hist[(size_t)e * nseg + s] = h[wave][e];
+  for (int e = tid; e < E; e += 256) hist[(size_t)s * E + e] = h[e];
 }
 
-// Exclusive scan of hist (E*nseg ints, e-major) in place by one workgroup:
-// passes of 8192 ints are loaded into LDS with coalesced reads, scanned there
-// (8 contiguous values per thread, then across threads) and written back.
-__global__ __launch_bounds__(1024) void seg_scan_kernel(int *__restrict__ hist, int E, int nseg,
-                                                        int pairs, int *__restrict__ counts,
-                                                        int *__restrict__ offsets) {
-  constexpr int CH = 8192, PER = CH / 1024;
-  __shared__ int buf[CH + CH / 32];  // one pad int per 32 breaks the stride-8 bank pattern
+// One workgroup of 1024 threads (E <= 1024): thread e scans column e of hist
+// (segments in order, batches of 32 loads in flight), then the expert totals
+// are scanned across the workgroup.
+__global__ __launch_bounds__(1024) void seg_scan_kernel(int *__restrict__ hist, int E, int nseg, int pairs,
+                                                        int *__restrict__ counts, int *__restrict__ offsets) {
+  constexpr int B = 32;
   __shared__ int wsum[16];
-  const int n = E * nseg;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  auto at = [](int i) { return i + (i >> 5); };
-  int carry = 0;
-  for (int base = 0; base < n; base += CH) {
-    const int m = min(CH, n - base);
-    for (int i = tid; i < CH; i += 1024) buf[at(i)] = i < m ? hist[base + i] : 0;
-    __syncthreads();
-    int v[PER], sum = 0;
+  int total = 0;
+  if (tid < E) {
+    for (int s0 = 0; s0 < nseg; s0 += B) {
+      int v[B];
 #pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      v[q] = buf[at(tid * PER + q)];
-      sum += v[q];
-    }
-    int incl = sum;
+      for (int i = 0; i < B; ++i) v[i] = s0 + i < nseg ? hist[(size_t)(s0 + i) * E + tid] : 0;
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int t = __shfl_up(incl, off, kWave);
-      if (lane >= off) incl += t;
+      for (int i = 0; i < B; ++i) {
+        if (s0 + i < nseg) hist[(size_t)(s0 + i) * E + tid] = total;
+        total += v[i];
+      }
     }
-    if (lane == kWave - 1) wsum[wave] = incl;
-    __syncthreads();
-    int run = carry + incl - sum;
-    int total = 0;
-    for (int w2 = 0; w2 < 16; ++w2) {
-      if (w2 < wave) run += wsum[w2];
-      total += wsum[w2];
-    }
-#pragma unroll
-    for (int q = 0; q < PER; ++q) {
-      buf[at(tid * PER + q)] = run;
-      run += v[q];
-    }
-    __syncthreads();
-    for (int i = tid; i < m; i += 1024) hist[base + i] = buf[at(i)];
-    carry += total;
-    __syncthreads();
   }
-  for (int e = tid; e < E; e += 1024) {
-    const int o0 = hist[(size_t)e * nseg];
-    const int o1 = e + 1 < E ? hist[(size_t)(e + 1) * nseg] : pairs;
-    offsets[e] = o0;
-    counts[e] = o1 - o0;
+  int incl = total;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int t = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += t;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int run = incl - total;
+  for (int w2 = 0; w2 < wave; ++w2) run += wsum[w2];
+  if (tid < E) {
+    offsets[tid] = run;
+    counts[tid] = total;
   }
   if (tid == 0) offsets[E] = pairs;
 }
 
-__global__ __launch_bounds__(256) void seg_scatter_kernel(const int *__restrict__ ids, int pairs,
-                                                          int E, int nseg,
-                                                          const int *__restrict__ base,
-                                                          int *__restrict__ perm,
-                                                          int *__restrict__ inv_perm) {
-  __shared__ int running[4][kMaxExperts];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int s = blockIdx.x * 4 + wave;
-  if (s >= nseg) return;  // whole wavefront leaves together; no block barrier below
-  for (int e = lane; e < E; e += kWave) running[wave][e] = base[(size_t)e * nseg + s];
-  // LDS writes above are read back by other lanes of the same wavefront only.
+// Segment s: wavefront w owns pairs [p0 + w*Q, p0 + (w+1)*Q), Q = kPermuteSeg/4.
+__global__ __launch_bounds__(256) void seg_scatter_kernel(const int *__restrict__ ids, int pairs, int E,
+                                                          const int *__restrict__ hist,
+                                                          const int *__restrict__ offsets,
+                                                          int *__restrict__ perm, int *__restrict__ inv_perm) {
+  constexpr int Q = kPermuteSeg / 4;
+  __shared__ int cnt[4][kMaxExperts];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, s = blockIdx.x;
+  const int q0 = s * kPermuteSeg + wave * Q, q1 = min(pairs, q0 + Q);
+  int ev[Q / kWave];
+#pragma unroll
+  for (int r = 0; r < Q / kWave; ++r) {
+    const int p = q0 + r * kWave + lane;
+    ev[r] = p < q1 ? ids[p] : -1;
+  }
+  for (int e = lane; e < E; e += kWave) cnt[wave][e] = 0;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
-  const int p0 = s * kPermuteSeg, p1 = min(pairs, p0 + kPermuteSeg);
-  scatter_rounds(ids, p0, p1, E, running[wave], perm, inv_perm);
+#pragma unroll
+  for (int r = 0; r < Q / kWave; ++r)
+    if (ev[r] >= 0) atomicAdd(&cnt[wave][ev[r]], 1);
+  __syncthreads();
+  // Per expert: first slot of each quarter = offsets[e] + hist[s][e] + earlier quarters.
+  for (int e = tid; e < E; e += 256) {
+    int run = offsets[e] + hist[(size_t)s * E + e];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int c = cnt[w][e];
+      cnt[w][e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  scatter_rounds(ev, q0, q1, E, cnt[wave], perm, inv_perm);
 }
 
 // Whole grouping in one workgroup (wavefront 0 does the ordered scatter).
@@ -215,7 +213,15 @@ __global__ __launch_bounds__(256) void small_permute_kernel(const int *__restric
   }
   if (tid == 0) offsets[E] = pairs;
   __syncthreads();
-  if (wave == 0) scatter_rounds(ids, 0, pairs, E, h, perm, inv_perm);
+  if (wave == 0) {
+    int ev[kPermuteSmallMax / kWave];
+#pragma unroll
+    for (int q = 0; q < kPermuteSmallMax / kWave; ++q) {
+      const int p = q * kWave + lane;
+      ev[q] = p < pairs ? ids[p] : -1;
+    }
+    scatter_rounds(ev, 0, pairs, E, h, perm, inv_perm);
+  }
 }
 
 }  // namespace
@@ -235,10 +241,9 @@ hipError_t launch_permute(const int *ids, int pairs, int E, int *counts, int *of
   }
   const int nseg = ceil_div(pairs, kPermuteSeg);
   int *hist = static_cast<int *>(ws);
-  const int blocks = ceil_div(nseg, 4);
   {
     KernelTimer timer("permute_hist", s);
-    seg_hist_kernel<<<blocks, 256, 0, s>>>(ids, pairs, E, nseg, hist);
+    seg_hist_kernel<<<nseg, 256, 0, s>>>(ids, pairs, E, hist);
   }
   {
     KernelTimer timer("permute_scan", s);
@@ -246,7 +251,7 @@ hipError_t launch_permute(const int *ids, int pairs, int E, int *counts, int *of
   }
   {
     KernelTimer timer("permute_scatter", s);
-    seg_scatter_kernel<<<blocks, 256, 0, s>>>(ids, pairs, E, nseg, hist, perm, inv_perm);
+    seg_scatter_kernel<<<nseg, 256, 0, s>>>(ids, pairs, E, hist, offsets, perm, inv_perm);
   }
   return hipGetLastError();
 }

@@ -8,7 +8,8 @@
 // (-0.0 is canonicalised to +0.0 first, so signed zeros tie as under IEEE
 // equality).  Each of k rounds takes the wavefront maximum key and then the
 // minimum expert index among the lanes holding it (ties go to the lowest
-// index), and removes the winner.  Lane j then owns winner j, and the softmax
+// index; with a single holder that is the holder's own candidate), and
+// removes the winner.  Lane j then owns winner j, and the softmax
 // over the k selected logits is a wavefront sum in fixed order.
 #include "moe_internal.h"
 
@@ -56,8 +57,17 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict
         bi = i;
       }
     const uint32_t gmax = wave_max_u32(best);
-    const uint32_t cand = best == gmax ? (uint32_t)(bi * kWave + lane) : 0xFFFFFFFFu;
-    const int e = (int)wave_min_u32(cand);
+    // Usually one lane holds the maximum: its lowest-index candidate wins.
+    // Equal maxima in several lanes take the minimum index over those lanes.
+    const uint64_t holders = __ballot(best == gmax);
+    int e;
+    if (__popcll(holders) == 1) {
+      const int wl = __ffsll((long long)holders) - 1;
+      e = __builtin_amdgcn_readlane(bi, wl) * kWave + wl;
+    } else {
+      const uint32_t cand = best == gmax ? (uint32_t)(bi * kWave + lane) : 0xFFFFFFFFu;
+      e = (int)wave_min_u32(cand);
+    }
 #pragma unroll
     for (int i = 0; i < EPL; ++i)
       if (i * kWave + lane == e) u[i] = 0u;
