@@ -10,31 +10,39 @@
 // with the FFN projection: yfxerp.com static review §5.1).
 //
 // Work item: a tile of up to 128 grouped rows of one expert (from the plan)
-// times a slice of weight rows ("features").  Workgroup = 4 wavefronts; each
-// wavefront owns NB blocks of 32 features for all of the tile's tokens, so
-// every weight element is fetched and dequantized by exactly one wavefront:
-//   gate/up: wavefront w owns NB/2 gate blocks and the NB/2 up blocks of the
-//            same h columns (silu(g)*u is local to the lane);
-//   down:    wavefront w owns NB blocks of output features.
-// NB = 2: two workgroups per CU (accumulators plus operands fit 256 VGPRs),
-// 3-stage ring.  (NB = 4 tiles halve the LDS reads per MFMA but need the AGPR
-// file and one workgroup per CU; on gfx950 they measured slower, since a
-// single wavefront per SIMD cannot hide the dequant, LDS and barrier
-// latencies.)  Matrix cores: v_mfma_f32_32x32x16_f16
-// with the dequantized weights as the A operand and token rows as B, so each
-// lane's accumulator holds runs of four consecutive features of one token.
+// times a slice of weight rows ("features").  Each wavefront owns 2 blocks of
+// 32 weight rows for all of the tile's tokens, so every weight element is
+// fetched and dequantized by exactly one wavefront:
+//   gate/up: wavefront w owns one gate block and the up block of the same h
+//            columns (silu(g)*u is local to the lane);
+//   down:    wavefront w owns two blocks of output features.
+// 128 fp32 accumulators + operands fit 256 VGPRs: two wavefronts per SIMD.
+// Matrix cores: v_mfma_f32_32x32x16_f16 with the dequantized weights as the A
+// operand and token rows as B, so each lane's accumulator holds runs of four
+// consecutive features of one token.
+//
+// Two pipelines, both moving every operand global -> LDS with direct-to-LDS
+// loads (global_load_lds) ahead of the MFMAs:
+//   * wide (the common shapes): 8 wavefronts, one workgroup per CU, K stages
+//     of 128 in a 2-stage ring; weights are loaded 64 contiguous bytes per
+//     row, and the fp16 scales once per 8 groups (16 bytes per row) into a
+//     double-buffered window.  This halves the vector-memory instructions and
+//     cache sectors per flop of the general pipeline, which is what bounds
+//     these kernels (the per-CU load path, not HBM bandwidth).  Needs the
+//     groups per row, K/g, to be a multiple of 8.
+//   * general: 4 wavefronts, two workgroups per CU, K chunks of 64 in a
+//     3-stage ring, one 2-byte scale load per row and chunk.
 //
 // Dequant in registers: a dword holds 8 nibbles u_0..u_7 (even K low); the
 // pair (u_m, u_{m+4}) goes into the mantissas of two fp16 values with one
 // and-or: the low nibbles of each half-word give 1024 + u (minus 1032 is q
 // exactly), the next nibbles give 1024 + 16u (times 1/16 minus 72 is q
 // exactly, one fma); the upper byte pair needs one shift.  Times the fp16 group
-// scale gives fp16(q*s) with a single rounding: 13 VALU ops per 8 weights.  Fragment slot e therefore holds K
-// offset (e>>1) + 4*(e&1) of its 8-block; token rows are stored in the same
-// slot order, so the contraction runs over the true K.
+// scale gives fp16(q*s) with a single rounding: 13 VALU ops per 8 weights.
+// Fragment slot e therefore holds K offset (e>>1) + 4*(e&1) of its 8-block;
+// token rows are stored in the same slot order, so the contraction runs over
+// the true K.
 //
-// Pipeline: every operand moves global -> LDS with direct-to-LDS loads
-// (global_load_lds), kStages-1 K chunks ahead, one barrier per chunk.
 // Scheduling: persistent workgroups; workgroups reach the 8 XCDs round-robin
 // by block index, and each XCD gets a contiguous range of (tile, slice) items
 // so the slices of one tile, which share its token rows, meet in one L2.
@@ -50,19 +58,14 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kXcds = 8;
-constexpr int kKC = kGemmKChunk;            // K per pipelined chunk (64)
-constexpr int kSegs = kKC / 8;              // 16-byte segments per token row per chunk
-constexpr int kStageSegs = kGemmRows * kSegs;
+constexpr int kNB = 2;  // 32-row weight blocks per wavefront
 
-constexpr int kWaves = 4;  // wavefronts per workgroup
-
-template <int NB>
-struct Cfg {
-  static constexpr int kStages = 3;                    // LDS ring depth
-  static constexpr int kWgPerCu = 2;
-  static constexpr int kBRows = kWaves * NB * 32;      // weight rows per workgroup
-  static constexpr int kHCols = kWaves * NB * 16;      // gate/up: h columns per workgroup
-  static constexpr int kOutCols = kWaves * NB * 32;    // down: output features per workgroup
+// Workgroup shape for W wavefronts.
+template <int W>
+struct Shape {
+  static constexpr int kBRows = W * kNB * 32;    // weight rows per workgroup
+  static constexpr int kHCols = W * kNB * 16;    // gate/up: h columns per workgroup
+  static constexpr int kOutCols = W * kNB * 32;  // down: output features per workgroup
 };
 
 struct GemmArgs {
@@ -85,18 +88,6 @@ struct GemmArgs {
 struct RowTables {
   int src[kGemmRows];  // gate/up: token row of x; down: grouped row of h
   int dst[kGemmRows];  // down: output row (pair index p for the fp16 y, grouped row otherwise)
-};
-
-template <int NB>
-struct Stage {
-  uint4 a[kStageSegs];              // token rows [row][segment], XOR-swizzled (a_slot)
-  uint4 b[2 * Cfg<NB>::kBRows];     // [weight row][lane half]: 16 bytes = 32 K values
-  uint32_t s[2 * Cfg<NB>::kBRows];  // [weight row][lane half]: fp16 group scale in the low half
-};
-
-template <int NB>
-struct Ring {
-  Stage<NB> *st[Cfg<NB>::kStages];
 };
 
 // Direct-to-LDS loads take an LDS-address-space pointer; the cast makes the
@@ -123,6 +114,7 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
   asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(o));
   return r;
 }
+
 __device__ __forceinline__ half8 dequant8(uint32_t d, half2_t s2, uint32_t mask, uint32_t magic) {
   const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
   const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
@@ -148,42 +140,54 @@ __device__ __forceinline__ uint32_t dword_of(const uint4 v, int j) {
   }
 }
 
-// LDS position (16-byte units) of logical segment c of tile row r: the XOR
-// spreads the 8 rows read by one 8-lane group of a ds_read_b128 over all bank
-// quads.
-__device__ __forceinline__ int a_slot(int r, int c) { return r * kSegs + (c ^ (r & 7)); }
+// Workgroup row (0 .. W*64-1) of row `col` of block nb of wavefront `wave`.
+__device__ __forceinline__ int brow_of(int wave, int nb, int col) { return (wave * kNB + nb) * 32 + col; }
 
-template <int NB>
-__device__ __forceinline__ int brow_of(int wave, int nb, int col) { return (wave * NB + nb) * 32 + col; }
+// First weight row (within its matrix) of block nb of wavefront `wave` in a slice.
+template <int MODE, int W>
+__device__ __forceinline__ int weight_row0(int slice, int wave, int nb) {
+  if (MODE == 0) {
+    const int hb = nb % (kNB / 2);  // gate blocks first, then the up blocks of the same columns
+    return slice * Shape<W>::kHCols + (wave * (kNB / 2) + hb) * 32;
+  }
+  return slice * Shape<W>::kOutCols + (wave * kNB + nb) * 32;
+}
 
-// One K chunk of MFMAs from one stage: NMB token blocks x NB feature blocks x 4 K-steps.
-template <int NB, int NMB>
-__device__ __forceinline__ void mma_chunk(floatx16 (&acc)[NMB][NB], const Stage<NB> &st, int wave, int col,
-                                          int half) {
+// Where a wavefront's weight rows and scales start (row 0 of the expert for
+// wavefronts past the matrix end: in bounds, results not stored).
+template <int MODE, int W>
+__device__ __forceinline__ void weight_bases(const GemmArgs &a, int e, int slice, int wave, bool valid,
+                                             const char *(&bbase)[kNB], const char *(&sbase)[kNB]) {
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    const int n0 = valid ? weight_row0<MODE, W>(slice, wave, nb) : 0;
+    const bool up = MODE == 0 && nb >= kNB / 2;
+    const uint8_t *B = up ? a.B1 : a.B0;
+    const uint16_t *Sc = up ? a.S1 : a.S0;
+    bbase[nb] = reinterpret_cast<const char *>(B + ((size_t)e * a.N + n0) * (a.K / 2));
+    sbase[nb] = reinterpret_cast<const char *>(Sc + ((size_t)e * a.N + n0) * (a.K / a.g));
+  }
+}
+
+// Four K-steps (64 K) of MFMAs: token fragments from `afrag(j, mb)`, weights
+// from the packed dwords of bw (one per K-step) and the scales s2.
+template <int NMB, typename AFrag>
+__device__ __forceinline__ void mma_k64(floatx16 (&acc)[NMB][kNB], const uint4 (&bw)[kNB],
+                                        const half2_t (&s2)[kNB], AFrag &&afrag) {
   const uint32_t mask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
   const uint32_t magic = __builtin_amdgcn_readfirstlane(0x64006400u);
-  uint4 bw[NB];
-  half2_t s2[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int br = brow_of<NB>(wave, nb, col);
-    bw[nb] = st.b[br * 2 + half];
-    const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)st.s[br * 2 + half]);
-    s2[nb] = half2_t{sv, sv};
-  }
   // Token fragments are read one K-step ahead of the MFMAs that use them.
   half8 af[2][NMB];
 #pragma unroll
-  for (int mb = 0; mb < NMB; ++mb) af[0][mb] = __builtin_bit_cast(half8, st.a[a_slot(mb * 32 + col, 4 * half)]);
+  for (int mb = 0; mb < NMB; ++mb) af[0][mb] = afrag(0, mb);
 #pragma unroll
-  for (int j = 0; j < kKC / 16; ++j) {
-    if (j + 1 < kKC / 16) {
+  for (int j = 0; j < 4; ++j) {
+    if (j + 1 < 4) {
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
-        af[(j + 1) & 1][mb] = __builtin_bit_cast(half8, st.a[a_slot(mb * 32 + col, 4 * half + j + 1)]);
+      for (int mb = 0; mb < NMB; ++mb) af[(j + 1) & 1][mb] = afrag(j + 1, mb);
     }
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
+    for (int nb = 0; nb < kNB; ++nb) {
       const half8 bf = dequant8(dword_of(bw[nb], j), s2[nb], mask, magic);
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
@@ -192,130 +196,17 @@ __device__ __forceinline__ void mma_chunk(floatx16 (&acc)[NMB][NB], const Stage<
   }
 }
 
-// First weight row (within its matrix) of block nb of wavefront `wave` in a slice.
-template <int MODE, int NB>
-__device__ __forceinline__ int weight_row0(int slice, int wave, int nb) {
-  if (MODE == 0) {
-    const int hb = nb % (NB / 2);  // gate blocks first, then the up blocks of the same columns
-    return slice * Cfg<NB>::kHCols + (wave * (NB / 2) + hb) * 32;
-  }
-  return slice * Cfg<NB>::kOutCols + (wave * NB + nb) * 32;
-}
-
-// One work item: the tile's rows (NMB 32-row blocks, nrows valid) x this
-// workgroup's slice of weight rows, over all of K.  Loads, kStages-1 chunks
-// ahead, all direct-to-LDS:
-//   * token rows (fp16 slot order): wavefront instruction i fills segments
-//     [(4i + wave)*64, +64), i.e. 8 rows x 128 bytes, XOR-swizzled;
-//   * packed weights: 32 rows x 32 bytes per instruction;
-//   * scales: 32 rows x 2 halves per instruction (a 2-byte direct-to-LDS load
-//     writes one zero-extended dword per lane).
-// Per chunk: wait for this wavefront's loads of the chunk, one barrier (every
-// wavefront's loads have landed and the oldest stage is free), issue chunk
-// c+kStages-1 into it, then dequant + MFMAs.  Past the last chunk the issue
-// repeats the last chunk (loads are never skipped), so every wait counts the
-// same number of operations.
-template <int MODE, int NB, int NMB>
-__device__ __forceinline__ void gemm_tile(const GemmArgs &a, const Ring<NB> &R, const RowTables &rt, int e,
-                                          int row0, int nrows, int slice) {
-  constexpr int S_ = Cfg<NB>::kStages;
-  // Token-row loads: 4*NMB instructions of 8 rows per stage, spread over the
-  // wavefronts; when they do not divide evenly the surplus instructions
-  // repeat earlier ones (same bytes to the same LDS place), so every
-  // wavefront issues the same count.
-  constexpr int kAInst = 4 * NMB, AI = (kAInst + kWaves - 1) / kWaves;
-  constexpr int V = AI + 2 * NB;  // direct-to-LDS loads per stage per wavefront
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
-  const int col = lane & 31, half = lane >> 5;
-  const int nchunks = a.K / kKC;
-
-  // Load addresses: a wavefront-uniform base plus a 32-bit lane offset (bytes).
-  uint32_t aoff[AI];
-  int aseg[AI];  // first LDS segment of each token-row instruction
-#pragma unroll
-  for (int i = 0; i < AI; ++i) {
-    aseg[i] = ((kWaves * i + wave) % kAInst) * 64;
-    const int p = aseg[i] + lane;
-    const int r = p >> 3, c = (p & 7) ^ (r & 7);
-    aoff[i] = ((uint32_t)rt.src[r] * (uint32_t)a.K + 8 * c) * 2;
-  }
-  const int col2 = lane >> 1, hh = lane & 1;  // weight-row loads: row lane>>1 of a block, half lane&1
-  // The last slice of a matrix whose rows the slice width does not divide
-  // has wavefronts past the end: they load row 0 (in bounds), take part in
-  // the loads and barriers, and store nothing.
-  const bool wave_rows_valid = weight_row0<MODE, NB>(slice, wave, 0) < a.N;
-  const char *bbase[NB];
-  const char *sbase[NB];
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int n0 = wave_rows_valid ? weight_row0<MODE, NB>(slice, wave, nb) : 0;
-    const bool up = MODE == 0 && nb >= NB / 2;
-    const uint8_t *B = up ? a.B1 : a.B0;
-    const uint16_t *Sc = up ? a.S1 : a.S0;
-    bbase[nb] = reinterpret_cast<const char *>(B + ((size_t)e * a.N + n0) * (a.K / 2));
-    sbase[nb] = reinterpret_cast<const char *>(Sc + ((size_t)e * a.N + n0) * (a.K / a.g));
-  }
-  const uint32_t boff = (uint32_t)col2 * (a.K / 2) + 16 * hh;
-  const uint32_t soff = ((uint32_t)col2 * (a.K / a.g)) * 2;
-  const int g_shift = 31 - __clz(a.g);  // g is a power of two
-  const char *abase = reinterpret_cast<const char *>(a.A);
-
-  auto issue = [&](Stage<NB> &st, int c) {
-    const int kc = c * kKC;
-    const char *ab = abase + 2 * kc;
-#pragma unroll
-    for (int i = 0; i < AI; ++i) __builtin_amdgcn_global_load_lds(ab + aoff[i], as_lds(&st.a[aseg[i]]), 16, 0, 0);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int base = brow_of<NB>(wave, nb, 0) * 2;
-      __builtin_amdgcn_global_load_lds(bbase[nb] + kc / 2 + boff, as_lds(&st.b[base]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(sbase[nb] + 2 * ((kc + 32 * hh) >> g_shift) + soff, as_lds(&st.s[base]), 2,
-                                       0, 0);
-    }
-  };
-
-  floatx16 acc[NMB][NB];
-#pragma unroll
-  for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = floatx16{};
-
-  const int last = nchunks - 1;
-  compiler_fence();
-#pragma unroll
-  for (int st = 0; st < S_ - 1; ++st) issue(*R.st[st], min(st, last));
-
-  auto step = [&](auto stage_tag, int c) {
-    constexpr int S = decltype(stage_tag)::value;
-    if constexpr (S < S_) {
-      compiler_fence();
-      wait_vmcnt<(S_ - 2) * V>();    // this wavefront's loads of chunk c are done
-      __builtin_amdgcn_s_barrier();  // ... and every other wavefront's; stage S-1 is free
-      compiler_fence();
-      issue(*R.st[(S + S_ - 1) % S_], min(c + S_ - 1, last));
-      compiler_fence();
-      if (c < nchunks) mma_chunk<NB, NMB>(acc, *R.st[S], wave, col, half);
-    }
-  };
-  for (int c0 = 0; c0 < nchunks; c0 += S_) {
-    step(std::integral_constant<int, 0>{}, c0);
-    step(std::integral_constant<int, 1>{}, c0 + 1);
-    step(std::integral_constant<int, 2>{}, c0 + 2);
-    step(std::integral_constant<int, 3>{}, c0 + 3);
-  }
-  compiler_fence();
-  wait_vmcnt<0>();  // no load of this tile may land in the next tile's stages
-  compiler_fence();
-
-  // Epilogue.  Accumulator element v of a lane: token row mb*32 + col of the
-  // tile, feature 8*(v/4) + 4*half + v%4 of its 32-feature block.
+// Epilogue.  Accumulator element v of a lane: token row mb*32 + col of the
+// tile, feature 8*(v/4) + 4*half + v%4 of its 32-feature block.
+template <int MODE, int W, int NMB>
+__device__ __forceinline__ void epilogue(const GemmArgs &a, const RowTables &rt, const floatx16 (&acc)[NMB][kNB],
+                                         int row0, int nrows, int slice, int wave, int col, int half, bool valid) {
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
     const int r = mb * 32 + col;
     if (MODE == 0) {
 #pragma unroll
-      for (int hb = 0; hb < NB / 2; ++hb) {
+      for (int hb = 0; hb < kNB / 2; ++hb) {
         // h = silu(g) * u, fp16.  Lanes l and l^32 hold the low and high four
         // features of each 8-feature group; after one exchange each lane owns
         // two whole groups and stores them in fragment slot order (16 bytes).
@@ -325,7 +216,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const Ring<NB> &R, 
           float hv[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float gv = acc[mb][hb][4 * i + q], uv = acc[mb][hb + NB / 2][4 * i + q];
+            const float gv = acc[mb][hb][4 * i + q], uv = acc[mb][hb + kNB / 2][4 * i + q];
             hv[q] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
           }
           hp[i][0] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)hv[0], (_Float16)hv[1]});
@@ -338,9 +229,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const Ring<NB> &R, 
         snd[3] = half ? hp[1][1] : hp[3][1];
 #pragma unroll
         for (int x = 0; x < 4; ++x) rcv[x] = __shfl_xor(snd[x], 32, kWave);
-        if (r < nrows && wave_rows_valid) {
+        if (r < nrows && valid) {
           uint16_t *hout =
-              static_cast<uint16_t *>(a.C) + (size_t)(row0 + r) * a.N + weight_row0<0, NB>(slice, wave, hb);
+              static_cast<uint16_t *>(a.C) + (size_t)(row0 + r) * a.N + weight_row0<0, W>(slice, wave, hb);
 #pragma unroll
           for (int gi = 0; gi < 2; ++gi) {
             const int grp = 2 * half + gi;  // 8-feature group this lane stores
@@ -355,15 +246,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const Ring<NB> &R, 
           }
         }
       }
-    } else if (r < nrows && wave_rows_valid) {
+    } else if (r < nrows && valid) {
       const size_t row = (size_t)rt.dst[r] * a.N;
       if (a.fused) {  // fp16 y rows in pair order, summed by the combine kernel
         uint16_t *yrow = static_cast<uint16_t *>(a.C) + row;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int n = weight_row0<1, NB>(slice, wave, nb) + 8 * i + 4 * half;
+            const int n = weight_row0<1, W>(slice, wave, nb) + 8 * i + 4 * half;
             uint2 o;
             o.x = __builtin_bit_cast(uint32_t, half2_t{(_Float16)acc[mb][nb][4 * i], (_Float16)acc[mb][nb][4 * i + 1]});
             o.y = __builtin_bit_cast(uint32_t,
@@ -373,10 +264,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const Ring<NB> &R, 
       } else {  // fp32 y rows in grouped order
         float *yrow = static_cast<float *>(a.C) + row;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int n = weight_row0<1, NB>(slice, wave, nb) + 8 * i + 4 * half;
+            const int n = weight_row0<1, W>(slice, wave, nb) + 8 * i + 4 * half;
             *reinterpret_cast<float4 *>(yrow + n) =
                 float4{acc[mb][nb][4 * i], acc[mb][nb][4 * i + 1], acc[mb][nb][4 * i + 2], acc[mb][nb][4 * i + 3]};
           }
@@ -385,8 +276,9 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs &a, const Ring<NB> &R, 
   }
 }
 
-template <int MODE, int NB>
-__device__ __forceinline__ void gemm_persistent(const GemmArgs &a, const Ring<NB> &R, RowTables &rt) {
+// Persistent loop over (tile, slice) items; `run_tile(nmb, tile, slice)` does one.
+template <int MODE, typename RunTile>
+__device__ __forceinline__ void gemm_persistent(const GemmArgs &a, RowTables &rt, RunTile &&run_tile) {
   const int tid = threadIdx.x;
   const int total = a.meta[0] * a.nslices;
   const int xcd = blockIdx.x % kXcds, lb = blockIdx.x / kXcds, per_xcd_wgs = gridDim.x / kXcds;
@@ -398,7 +290,6 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &a, const Ring<NB
     const int item = start + local;
     const int entry = item / a.nslices, slice = item - entry * a.nslices;
     const Tile tile = a.tiles[entry];
-    const int nmb = (tile.rows + 31) >> 5;
 
     __syncthreads();  // previous work item is done with LDS and the row tables
     if (tid < kGemmRows) {
@@ -412,23 +303,294 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &a, const Ring<NB
       }
     }
     __syncthreads();
-    switch (nmb) {
-      case 1: gemm_tile<MODE, NB, 1>(a, R, rt, tile.e, tile.row0, tile.rows, slice); break;
-      case 2: gemm_tile<MODE, NB, 2>(a, R, rt, tile.e, tile.row0, tile.rows, slice); break;
-      case 3: gemm_tile<MODE, NB, 3>(a, R, rt, tile.e, tile.row0, tile.rows, slice); break;
-      default: gemm_tile<MODE, NB, 4>(a, R, rt, tile.e, tile.row0, tile.rows, slice); break;
-    }
+    run_tile((tile.rows + 31) >> 5, tile, slice);
   }
 }
 
-// The ring stages are distinct LDS objects so the compiler tracks each
-// stage's direct-to-LDS loads separately instead of waiting for all of them.
+template <typename F>
+__device__ __forceinline__ void dispatch_nmb(int nmb, F &&f) {
+  switch (nmb) {
+    case 1: f(std::integral_constant<int, 1>{}); break;
+    case 2: f(std::integral_constant<int, 2>{}); break;
+    case 3: f(std::integral_constant<int, 3>{}); break;
+    default: f(std::integral_constant<int, 4>{}); break;
+  }
+}
+
+// =========================================================================
+// Wide pipeline: 8 wavefronts, K stages of 128, 2-stage ring, scale windows.
+// =========================================================================
+constexpr int kWideW = 8;
+constexpr int kKS = 128;  // K per stage
+
+struct WideStage {
+  uint4 a[kGemmRows * 16];             // token rows [row][16-byte segment], XOR-swizzled (wa_slot)
+  uint4 b[Shape<kWideW>::kBRows * 4];  // weight rows [row][16-byte quarter], XOR-swizzled (wb_slot)
+};
+struct ScaleWindow {
+  uint4 s[Shape<kWideW>::kBRows];  // weight rows: fp16 scales of 8 consecutive groups
+};
+
+// Segment c (0..15) of token row r: 16 consecutive rows read by a ds_read_b128
+// lane group land on 16 different bank quads.
+__device__ __forceinline__ int wa_slot(int r, int c) { return r * 16 + (c ^ (r & 15)); }
+// Quarter q (0..3, 32 K values) of weight row br: 16 consecutive rows spread
+// over all 64 banks.
+__device__ __forceinline__ int wb_slot(int br, int q) { return br * 4 + (q ^ ((br >> 2) & 3)); }
+
+// One work item on the wide pipeline.  Per stage (128 K) a wavefront issues:
+//   * token rows: NMB instructions of 4 rows x 256 bytes (instruction wave+8i);
+//   * packed weights: 2 per block, 16 rows x 64 bytes each;
+//   * on the first stage of every 8-group window: one 16-byte scale load per
+//     weight row of the wavefront (64 rows), into the window buffer of the
+//     window's parity.
+// Step c: wait for this wavefront's loads, one barrier (every wavefront's
+// loads of stage c landed, and everyone is done with stage c-1, whose buffer
+// is next), read this stage's scales, issue stage c+1, dequant + MFMAs.
+template <int MODE, int NMB>
+__device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0, WideStage &st1, ScaleWindow &sw0,
+                                               ScaleWindow &sw1, const RowTables &rt, int e, int row0, int nrows,
+                                               int slice) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
+  const int col = lane & 31, half = lane >> 5;
+  const int nst = a.K / kKS;
+  const int per_win = a.g / 16;  // stages per 8-group scale window
+  const int ngr = a.K / a.g;     // groups per weight row (a multiple of 8)
+
+  uint32_t aoff[NMB];
+#pragma unroll
+  for (int i = 0; i < NMB; ++i) {
+    const int p = (wave + kWideW * i) * 64 + lane;
+    const int r = p >> 4, c = (p & 15) ^ (r & 15);
+    aoff[i] = ((uint32_t)rt.src[r] * (uint32_t)a.K + 8 * c) * 2;
+  }
+  const bool valid = weight_row0<MODE, kWideW>(slice, wave, 0) < a.N;
+  const char *bbase[kNB];
+  const char *sbase[kNB];
+  weight_bases<MODE, kWideW>(a, e, slice, wave, valid, bbase, sbase);
+  uint32_t boff[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int rr = 16 * t + (lane >> 2);
+    boff[t] = (uint32_t)rr * (a.K / 2) + 16 * ((lane & 3) ^ ((rr >> 2) & 3));
+  }
+  // Scale loads: lanes 0-31 the rows of block 0, lanes 32-63 those of block 1.
+  const char *sptr = (half ? sbase[1] : sbase[0]) + (size_t)col * ngr * 2;
+  const char *abase = reinterpret_cast<const char *>(a.A);
+
+  auto issue = [&](WideStage &st, int c) {
+    const int kc = c * kKS;
+#pragma unroll
+    for (int i = 0; i < NMB; ++i)
+      __builtin_amdgcn_global_load_lds(abase + aoff[i] + 2 * kc, as_lds(&st.a[(wave + kWideW * i) * 64]), 16, 0, 0);
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        __builtin_amdgcn_global_load_lds(bbase[nb] + boff[t] + kc / 2, as_lds(&st.b[(brow_of(wave, nb, 0) + 16 * t) * 4]),
+                                         16, 0, 0);
+    if (c % per_win == 0) {
+      const int win = c / per_win;
+      if (win & 1)
+        __builtin_amdgcn_global_load_lds(sptr + 16 * win, as_lds(&sw1.s[wave * 64]), 16, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(sptr + 16 * win, as_lds(&sw0.s[wave * 64]), 16, 0, 0);
+    }
+  };
+
+  floatx16 acc[NMB][kNB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = floatx16{};
+
+  auto step = [&](const WideStage &cur, WideStage &nxt, int c) {
+    compiler_fence();
+    wait_vmcnt<0>();               // this wavefront's loads of stage c are done
+    __builtin_amdgcn_s_barrier();  // ... and everyone's; stage c-1's buffer is free
+    compiler_fence();
+    // Scales of this stage's two 64-K halves (group of K offset kc + 32*half).
+    const int win = c / per_win;
+    const ScaleWindow &sw = (win & 1) ? sw1 : sw0;
+    half2_t s2[2][kNB];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int grp = (c * kKS + 64 * s + 32 * half) / a.g - 8 * win;
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        const uint16_t bits = reinterpret_cast<const uint16_t *>(&sw.s[brow_of(wave, nb, col)])[grp];
+        const _Float16 sv = __builtin_bit_cast(_Float16, bits);
+        s2[s][nb] = half2_t{sv, sv};
+      }
+    }
+    compiler_fence();
+    if (c + 1 < nst) issue(nxt, c + 1);
+    compiler_fence();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      uint4 bw[kNB];
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) bw[nb] = cur.b[wb_slot(brow_of(wave, nb, col), 2 * s + half)];
+      mma_k64<NMB>(acc, bw, s2[s], [&](int j, int mb) {
+        return __builtin_bit_cast(half8, cur.a[wa_slot(mb * 32 + col, 8 * s + 4 * half + j)]);
+      });
+    }
+  };
+
+  compiler_fence();
+  issue(st0, 0);
+  for (int c = 0; c < nst; c += 2) {
+    step(st0, st1, c);
+    if (c + 1 < nst) step(st1, st0, c + 1);
+  }
+  // The last step issued nothing: no load of this tile is in flight.
+  epilogue<MODE, kWideW, NMB>(a, rt, acc, row0, nrows, slice, wave, col, half, valid);
+}
+
+// The ring stages and scale windows are distinct LDS objects so the compiler
+// tracks each one's direct-to-LDS loads separately.
 template <int MODE>  // 0: gate/up + silu*mul -> h;  1: down -> y
-__global__ __launch_bounds__(64 * kWaves, 2) void moe_gemm_nb2(GemmArgs a) {
-  __shared__ Stage<2> st0, st1, st2;
+__global__ __launch_bounds__(64 * kWideW, 1) void moe_gemm_wide(GemmArgs a) {
+  __shared__ WideStage st0, st1;
+  __shared__ ScaleWindow sw0, sw1;
   __shared__ RowTables rt;
-  const Ring<2> R{{&st0, &st1, &st2}};
-  gemm_persistent<MODE, 2>(a, R, rt);
+  gemm_persistent<MODE>(a, rt, [&](int nmb, const Tile &tile, int slice) {
+    dispatch_nmb(nmb, [&](auto n) {
+      gemm_tile_wide<MODE, decltype(n)::value>(a, st0, st1, sw0, sw1, rt, tile.e, tile.row0, tile.rows, slice);
+    });
+  });
+}
+
+// =========================================================================
+// General pipeline: 4 wavefronts, K chunks of 64, 3-stage ring.
+// =========================================================================
+constexpr int kGenW = 4;
+constexpr int kKC = kGemmKChunk;  // K per pipelined chunk (64)
+constexpr int kGenStages = 3;
+
+struct GenStage {
+  uint4 a[kGemmRows * 8];                // token rows [row][segment], XOR-swizzled (ga_slot)
+  uint4 b[2 * Shape<kGenW>::kBRows];     // [weight row][lane half]: 16 bytes = 32 K values
+  uint32_t s[2 * Shape<kGenW>::kBRows];  // [weight row][lane half]: fp16 group scale in the low half
+};
+struct GenRing {
+  GenStage *st[kGenStages];
+};
+
+// Segment c (0..7) of token row r: the 8 rows read by one 8-lane group of a
+// ds_read_b128 hit distinct bank quads.
+__device__ __forceinline__ int ga_slot(int r, int c) { return r * 8 + (c ^ (r & 7)); }
+
+// One work item on the general pipeline.  Per chunk a wavefront issues:
+//   * token rows (fp16 slot order): instruction i fills segments
+//     [(4i + wave)*64, +64), i.e. 8 rows x 128 bytes;
+//   * packed weights: 32 rows x 32 bytes per block;
+//   * scales: 32 rows x 2 halves per block (a 2-byte direct-to-LDS load
+//     writes one zero-extended dword per lane).
+// Step c: wait for this wavefront's loads of chunk c, one barrier (every
+// wavefront's loads landed and the oldest stage is free), issue chunk c+2
+// into it, then dequant + MFMAs.  Past the last chunk the issue repeats the
+// last chunk (loads are never skipped), so every wait counts the same number
+// of operations.
+template <int MODE, int NMB>
+__device__ __forceinline__ void gemm_tile_general(const GemmArgs &a, const GenRing &R, const RowTables &rt, int e,
+                                                  int row0, int nrows, int slice) {
+  constexpr int S_ = kGenStages;
+  constexpr int V = NMB + 2 * kNB;  // direct-to-LDS loads per stage per wavefront
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
+  const int col = lane & 31, half = lane >> 5;
+  const int nchunks = a.K / kKC;
+
+  uint32_t aoff[NMB];
+#pragma unroll
+  for (int i = 0; i < NMB; ++i) {
+    const int p = (kGenW * i + wave) * 64 + lane;
+    const int r = p >> 3, c = (p & 7) ^ (r & 7);
+    aoff[i] = ((uint32_t)rt.src[r] * (uint32_t)a.K + 8 * c) * 2;
+  }
+  const int col2 = lane >> 1, hh = lane & 1;  // weight-row loads: row lane>>1 of a block, half lane&1
+  const bool valid = weight_row0<MODE, kGenW>(slice, wave, 0) < a.N;
+  const char *bbase[kNB];
+  const char *sbase[kNB];
+  weight_bases<MODE, kGenW>(a, e, slice, wave, valid, bbase, sbase);
+  const uint32_t boff = (uint32_t)col2 * (a.K / 2) + 16 * hh;
+  const uint32_t soff = ((uint32_t)col2 * (a.K / a.g)) * 2;
+  const int g_shift = 31 - __clz(a.g);  // g is a power of two
+  const char *abase = reinterpret_cast<const char *>(a.A);
+
+  auto issue = [&](GenStage &st, int c) {
+    const int kc = c * kKC;
+    const char *ab = abase + 2 * kc;
+#pragma unroll
+    for (int i = 0; i < NMB; ++i)
+      __builtin_amdgcn_global_load_lds(ab + aoff[i], as_lds(&st.a[(kGenW * i + wave) * 64]), 16, 0, 0);
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      const int base = brow_of(wave, nb, 0) * 2;
+      __builtin_amdgcn_global_load_lds(bbase[nb] + kc / 2 + boff, as_lds(&st.b[base]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(sbase[nb] + 2 * ((kc + 32 * hh) >> g_shift) + soff, as_lds(&st.s[base]), 2,
+                                       0, 0);
+    }
+  };
+
+  floatx16 acc[NMB][kNB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = floatx16{};
+
+  const int last = nchunks - 1;
+  compiler_fence();
+#pragma unroll
+  for (int st = 0; st < S_ - 1; ++st) issue(*R.st[st], min(st, last));
+
+  auto step = [&](auto stage_tag, int c) {
+    constexpr int S = decltype(stage_tag)::value;
+    compiler_fence();
+    wait_vmcnt<(S_ - 2) * V>();    // this wavefront's loads of chunk c are done
+    __builtin_amdgcn_s_barrier();  // ... and every other wavefront's; stage S-1 is free
+    compiler_fence();
+    issue(*R.st[(S + S_ - 1) % S_], min(c + S_ - 1, last));
+    compiler_fence();
+    if (c < nchunks) {
+      const GenStage &st = *R.st[S];
+      uint4 bw[kNB];
+      half2_t s2[kNB];
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        const int br = brow_of(wave, nb, col);
+        bw[nb] = st.b[br * 2 + half];
+        const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)st.s[br * 2 + half]);
+        s2[nb] = half2_t{sv, sv};
+      }
+      mma_k64<NMB>(acc, bw, s2, [&](int j, int mb) {
+        return __builtin_bit_cast(half8, st.a[ga_slot(mb * 32 + col, 4 * half + j)]);
+      });
+    }
+  };
+  for (int c0 = 0; c0 < nchunks; c0 += S_) {
+    step(std::integral_constant<int, 0>{}, c0);
+    step(std::integral_constant<int, 1>{}, c0 + 1);
+    step(std::integral_constant<int, 2>{}, c0 + 2);
+  }
+  compiler_fence();
+  wait_vmcnt<0>();  // no load of this tile may land in the next tile's stages
+  compiler_fence();
+  epilogue<MODE, kGenW, NMB>(a, rt, acc, row0, nrows, slice, wave, col, half, valid);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(64 * kGenW, 2) void moe_gemm_general(GemmArgs a) {
+  __shared__ GenStage st0, st1, st2;
+  __shared__ RowTables rt;
+  const GenRing R{{&st0, &st1, &st2}};
+  gemm_persistent<MODE>(a, rt, [&](int nmb, const Tile &tile, int slice) {
+    dispatch_nmb(nmb, [&](auto n) {
+      gemm_tile_general<MODE, decltype(n)::value>(a, R, rt, tile.e, tile.row0, tile.rows, slice);
+    });
+  });
 }
 
 // Tile list from the expert offsets: expert e gets ceil(count_e / rows_per_tile)
@@ -489,11 +651,24 @@ int persistent_grid(long long work_upper, int wg_per_cu) {
   return (int)(g < kXcds ? kXcds : g);
 }
 
+#ifndef STRATA_GEMM_WIDE
+#define STRATA_GEMM_WIDE 1
+#endif
+
+// The wide pipeline when the scale windows align with the rows (K/g a
+// multiple of 8), the general one otherwise.
 template <int MODE>
 hipError_t launch_gemm(GemmArgs args, long long tiles_upper, int matrix_rows, hipStream_t s) {
-  const int width = MODE == 0 ? Cfg<2>::kHCols : Cfg<2>::kOutCols;
-  args.nslices = (matrix_rows + width - 1) / width;
-  moe_gemm_nb2<MODE><<<persistent_grid(tiles_upper * args.nslices, Cfg<2>::kWgPerCu), 64 * kWaves, 0, s>>>(args);
+  const bool wide = STRATA_GEMM_WIDE && args.K % kKS == 0 && (args.K / args.g) % 8 == 0;
+  if (wide) {
+    const int width = MODE == 0 ? Shape<kWideW>::kHCols : Shape<kWideW>::kOutCols;
+    args.nslices = (matrix_rows + width - 1) / width;
+    moe_gemm_wide<MODE><<<persistent_grid(tiles_upper * args.nslices, 1), 64 * kWideW, 0, s>>>(args);
+  } else {
+    const int width = MODE == 0 ? Shape<kGenW>::kHCols : Shape<kGenW>::kOutCols;
+    args.nslices = (matrix_rows + width - 1) / width;
+    moe_gemm_general<MODE><<<persistent_grid(tiles_upper * args.nslices, 2), 64 * kGenW, 0, s>>>(args);
+  }
   return hipGetLastError();
 }
 
