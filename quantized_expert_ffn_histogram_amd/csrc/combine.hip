@@ -6,6 +6,8 @@
 
 namespace strata {
 namespace {
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ y,
                                                       const int *__restrict__ inv_perm,
@@ -28,8 +30,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
   reinterpret_cast<float4 *>(out + (size_t)t * H)[n4] = acc;
 }
 
-// Fused-combine finish of the GEMM path: fp16 y rows in pair order, so the k
-// rows of token t are contiguous.  One thread: 8 consecutive features.
+// Fused-combine finish: fp16 y rows in pair order, so the k rows of token t
+// are contiguous.  One thread: 8 consecutive features.  The rows are read
+// once and out is not read back here, so both go through non-temporal
+// accesses (they do not displace other data in the caches).
 __global__ __launch_bounds__(256) void combine_pairs_kernel(const uint4 *__restrict__ y16,
                                                             const float *__restrict__ topk_w, int T, int k,
                                                             int H, float4 *__restrict__ out) {
@@ -40,7 +44,8 @@ __global__ __launch_bounds__(256) void combine_pairs_kernel(const uint4 *__restr
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int j = 0; j < k; ++j) {
     const float w = topk_w[(size_t)t * k + j];
-    const uint4 v = y16[((size_t)t * k + j) * groups + c];
+    const u32x4_t vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(&y16[((size_t)t * k + j) * groups + c]));
+    const uint4 v = {vv.x, vv.y, vv.z, vv.w};
     const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -49,8 +54,8 @@ __global__ __launch_bounds__(256) void combine_pairs_kernel(const uint4 *__restr
       acc[2 * q + 1] += w * (float)h2.y;
     }
   }
-  out[g * 2] = float4{acc[0], acc[1], acc[2], acc[3]};
-  out[g * 2 + 1] = float4{acc[4], acc[5], acc[6], acc[7]};
+  __builtin_nontemporal_store(f32x4_t{acc[0], acc[1], acc[2], acc[3]}, reinterpret_cast<f32x4_t *>(&out[g * 2]));
+  __builtin_nontemporal_store(f32x4_t{acc[4], acc[5], acc[6], acc[7]}, reinterpret_cast<f32x4_t *>(&out[g * 2 + 1]));
 }
 
 }  // namespace
