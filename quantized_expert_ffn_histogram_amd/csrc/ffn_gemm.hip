@@ -249,18 +249,36 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const RowTables &rt,
     } else if (r < nrows && valid) {
       const size_t row = (size_t)rt.dst[r] * a.N;
       if (a.fused) {  // fp16 y rows in pair order, summed by the combine kernel
+        // As for h: one exchange with lane l^32 gives each lane two whole
+        // 8-feature groups per block, stored as 16 bytes each.
         uint16_t *yrow = static_cast<uint16_t *>(a.C) + row;
 #pragma unroll
-        for (int nb = 0; nb < kNB; ++nb)
+        for (int nb = 0; nb < kNB; ++nb) {
+          uint32_t yp[4][2];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int n = weight_row0<1, W>(slice, wave, nb) + 8 * i + 4 * half;
-            uint2 o;
-            o.x = __builtin_bit_cast(uint32_t, half2_t{(_Float16)acc[mb][nb][4 * i], (_Float16)acc[mb][nb][4 * i + 1]});
-            o.y = __builtin_bit_cast(uint32_t,
-                                     half2_t{(_Float16)acc[mb][nb][4 * i + 2], (_Float16)acc[mb][nb][4 * i + 3]});
-            *reinterpret_cast<uint2 *>(yrow + n) = o;
+            yp[i][0] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)acc[mb][nb][4 * i], (_Float16)acc[mb][nb][4 * i + 1]});
+            yp[i][1] =
+                __builtin_bit_cast(uint32_t, half2_t{(_Float16)acc[mb][nb][4 * i + 2], (_Float16)acc[mb][nb][4 * i + 3]});
           }
+          uint32_t snd[4], rcv[4];
+          snd[0] = half ? yp[0][0] : yp[2][0];
+          snd[1] = half ? yp[0][1] : yp[2][1];
+          snd[2] = half ? yp[1][0] : yp[3][0];
+          snd[3] = half ? yp[1][1] : yp[3][1];
+#pragma unroll
+          for (int x = 0; x < 4; ++x) rcv[x] = __shfl_xor(snd[x], 32, kWave);
+#pragma unroll
+          for (int gi = 0; gi < 2; ++gi) {
+            const int grp = 2 * half + gi;  // 8-feature group this lane stores
+            uint4 o;
+            o.x = half ? rcv[2 * gi] : yp[grp][0];      // features 0-1 of the group (from the half-0 lane)
+            o.y = half ? rcv[2 * gi + 1] : yp[grp][1];  // 2-3
+            o.z = half ? yp[grp][0] : rcv[2 * gi];      // 4-5 (from the half-1 lane)
+            o.w = half ? yp[grp][1] : rcv[2 * gi + 1];  // 6-7
+            *reinterpret_cast<uint4 *>(yrow + weight_row0<1, W>(slice, wave, nb) + 8 * grp) = o;
+          }
+        }
       } else {  // fp32 y rows in grouped order
         float *yrow = static_cast<float *>(a.C) + row;
 #pragma unroll
