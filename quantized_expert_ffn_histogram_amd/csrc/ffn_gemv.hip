@@ -27,7 +27,7 @@
 //
 //   gemv_gateup: workgroup = (entry, 16 h columns); wavefront = 4 columns,
 //                gate and up rows; lane 0 writes h = silu(g)*u (fp16).
-//   gemv_down:   workgroup = (entry, 2048/(I/32) output rows); each output
+//   gemv_down:   workgroup = (entry, 1024/(I/32) output rows); each output
 //                row is reduced over I/32 lanes.  Fused combine: y goes to
 //                fp16 rows in pair order and the combine kernel of the
 //                matrix-core path sums each token's k rows in j order
@@ -39,8 +39,11 @@ namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kGateUpCols = 16;  // h columns per workgroup (4 per wavefront)
-constexpr int kDownIter = 8;     // 16-byte weight loads per lane in gemv_down
+// Tile sizes measured best on the decode shape (T=4, H=2048, I=512, E=512,
+// k=10) among 2/4/8 columns per wavefront and 1/2/4/8/16 down loads per lane.
+constexpr int kColsPerWave = 4;                // h columns per wavefront
+constexpr int kGateUpCols = 4 * kColsPerWave;  // h columns per workgroup
+constexpr int kDownIter = 4;   // 16-byte weight loads per lane in gemv_down
 constexpr int kMaxChunks = kGemvMaxHidden / 2048;
 
 __device__ __forceinline__ half2_t magic_pair(uint32_t d, int m) {
@@ -169,16 +172,16 @@ __global__ __launch_bounds__(256, NCH == 1 ? 4 : 2) void gemv_gateup_kernel(Gemv
   const bool active = 32 * lane < a.H;
   const int kl = active ? 32 * lane : 0;
   const int kb = a.H / 2, ng = a.H / a.g;
-  const int n0 = cs * kGateUpCols + wave * 4;
+  const int n0 = cs * kGateUpCols + wave * kColsPerWave;
 
   // The first row's pair index is loaded before the weights: vector loads
   // complete in order, so the x loads that depend on it wait only for it.
   int p_first = a.perm[en.row0];
   // This wavefront's gate and up rows (4 columns) and their scales (fp16 bits).
-  uint4 wg[4][NCH], wu[4][NCH];
-  uint32_t sgb[4][NCH], sub_[4][NCH];
+  uint4 wg[kColsPerWave][NCH], wu[kColsPerWave][NCH];
+  uint32_t sgb[kColsPerWave][NCH], sub_[kColsPerWave][NCH];
 #pragma unroll
-  for (int cc = 0; cc < 4; ++cc)
+  for (int cc = 0; cc < kColsPerWave; ++cc)
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const size_t row = (size_t)en.e * a.I + n0 + cc;
@@ -205,14 +208,16 @@ __global__ __launch_bounds__(256, NCH == 1 ? 4 : 2) void gemv_gateup_kernel(Gemv
 #pragma unroll
       for (int q = 0; q < 4; ++q) opaque(xv[c][q]);
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc)
+    for (int cc = 0; cc < kColsPerWave; ++cc)
 #pragma unroll
       for (int c = 0; c < NCH; ++c) {
         opaque(wg[cc][c]);
         opaque(wu[cc][c]);
         asm volatile("" : "+v"(sgb[cc][c]), "+v"(sub_[cc][c]));
       }
-    float gs[4] = {0.f, 0.f, 0.f, 0.f}, us[4] = {0.f, 0.f, 0.f, 0.f};
+    float gs[kColsPerWave], us[kColsPerWave];
+#pragma unroll
+    for (int cc = 0; cc < kColsPerWave; ++cc) gs[cc] = us[cc] = 0.0f;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       half2_t xp[16];
@@ -222,13 +227,13 @@ __global__ __launch_bounds__(256, NCH == 1 ? 4 : 2) void gemv_gateup_kernel(Gemv
 #pragma unroll
       for (int i = 0; i < 16; ++i) xs += pair_sum(xp[i]);
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) {
+      for (int cc = 0; cc < kColsPerWave; ++cc) {
         gs[cc] += dot32(wg[cc][c], xp, xs, on * half_bits_to_float((uint16_t)sgb[cc][c]));
         us[cc] += dot32(wu[cc][c], xp, xs, on * half_bits_to_float((uint16_t)sub_[cc][c]));
       }
     }
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
+    for (int cc = 0; cc < kColsPerWave; ++cc) {
       const float gv = group_sum<kWave>(gs[cc]);
       const float uv = group_sum<kWave>(us[cc]);
       if (lane == 0) {
@@ -268,7 +273,7 @@ __global__ __launch_bounds__(256, 4) void gemv_down_kernel(GemvArgs a) {
   int dst;
   load_row(0, hv, dst);
 
-  // Rows past H (only when H < 2048/(I/32)*32) load row 0 and are not stored.
+  // Rows past H (only when H is below the workgroup's row count) load row 0 and are not stored.
   uint4 wq[kDownIter];
   uint32_t sdb[kDownIter];
 #pragma unroll
