@@ -171,6 +171,27 @@ __device__ __forceinline__ void weight_bases(const GemmArgs &a, int e, int slice
 
 // Four K-steps (64 K) of MFMAs: token fragments from `afrag(j, mb)`, weights
 // from the packed dwords of bw (one per K-step) and the scales s2.
+template <int NMB, typename AFrag, typename Pre>
+__device__ __forceinline__ void mma_k64_cb(floatx16 (&acc)[NMB][kNB], const uint4 (&bw)[kNB],
+                                        const half2_t (&s2)[kNB], AFrag &&afrag, Pre &&pre) {
+  const uint32_t mask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
+  const uint32_t magic = __builtin_amdgcn_readfirstlane(0x64006400u);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    half8 af[NMB];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) af[mb] = afrag(j, mb);
+    pre(j);
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      const half8 bf = dequant8(dword_of(bw[nb], j), s2[nb], mask, magic);
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf, af[mb], acc[mb][nb], 0, 0, 0);
+    }
+  }
+}
+
 template <int NMB, typename AFrag>
 __device__ __forceinline__ void mma_k64(floatx16 (&acc)[NMB][kNB], const uint4 (&bw)[kNB],
                                         const half2_t (&s2)[kNB], AFrag &&afrag) {
@@ -364,7 +385,10 @@ __device__ __forceinline__ int wb_slot(int br, int q) { return br * 4 + (q ^ ((b
 //     window's parity.
 // Step c: wait for this wavefront's loads, one barrier (every wavefront's
 // loads of stage c landed, and everyone is done with stage c-1, whose buffer
-// is next), read this stage's scales, issue stage c+1, dequant + MFMAs.
+// is next), read this stage's scales, then dequant + MFMAs, with the loads of
+// stage c+1 issued one per K-step between the MFMA groups (a wavefront's
+// load issue then overlaps the other wavefronts' MFMAs instead of all
+// wavefronts issuing together after the barrier).
 template <int MODE, int NMB>
 __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0, WideStage &st1, ScaleWindow &sw0,
                                                ScaleWindow &sw1, const RowTables &rt, int e, int row0, int nrows,
@@ -397,18 +421,19 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
   const char *sptr = (half ? sbase[1] : sbase[0]) + (size_t)col * ngr * 2;
   const char *abase = reinterpret_cast<const char *>(a.A);
 
-  auto issue = [&](WideStage &st, int c) {
+  // Part k (0..7) of the loads of stage c: token rows first, then weights,
+  // the scale window with the last part.
+  auto issue_part = [&](WideStage &st, int c, int k) {
     const int kc = c * kKS;
-#pragma unroll
-    for (int i = 0; i < NMB; ++i)
-      __builtin_amdgcn_global_load_lds(abase + aoff[i] + 2 * kc, as_lds(&st.a[(wave + kWideW * i) * 64]), 16, 0, 0);
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        __builtin_amdgcn_global_load_lds(bbase[nb] + boff[t] + kc / 2, as_lds(&st.b[(brow_of(wave, nb, 0) + 16 * t) * 4]),
-                                         16, 0, 0);
-    if (c % per_win == 0) {
+    if (k < NMB) {
+      __builtin_amdgcn_global_load_lds(abase + aoff[k < NMB ? k : 0] + 2 * kc,
+                                       as_lds(&st.a[(wave + kWideW * k) * 64]), 16, 0, 0);
+    } else if (k < NMB + 4) {
+      const int q = k - NMB, nb = q >> 1, t = q & 1;
+      __builtin_amdgcn_global_load_lds(bbase[nb] + boff[t] + kc / 2, as_lds(&st.b[(brow_of(wave, nb, 0) + 16 * t) * 4]),
+                                       16, 0, 0);
+    }
+    if (k == 7 && c % per_win == 0) {
       const int win = c / per_win;
       if (win & 1)
         __builtin_amdgcn_global_load_lds(sptr + 16 * win, as_lds(&sw1.s[wave * 64]), 16, 0, 0);
@@ -443,21 +468,23 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
       }
     }
     compiler_fence();
-    if (c + 1 < nst) issue(nxt, c + 1);
-    compiler_fence();
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       uint4 bw[kNB];
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) bw[nb] = cur.b[wb_slot(brow_of(wave, nb, col), 2 * s + half)];
-      mma_k64<NMB>(acc, bw, s2[s], [&](int j, int mb) {
+      mma_k64_cb<NMB>(acc, bw, s2[s], [&](int j, int mb) {
         return __builtin_bit_cast(half8, cur.a[wa_slot(mb * 32 + col, 8 * s + 4 * half + j)]);
+      }, [&](int j) {
+        if (c + 1 < nst) issue_part(nxt, c + 1, 4 * s + j);
+        __builtin_amdgcn_sched_barrier(0);
       });
     }
   };
 
   compiler_fence();
-  issue(st0, 0);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) issue_part(st0, 0, k);
   for (int c = 0; c < nst; c += 2) {
     step(st0, st1, c);
     if (c + 1 < nst) step(st1, st0, c + 1);
