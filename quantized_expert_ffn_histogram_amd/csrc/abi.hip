@@ -101,11 +101,11 @@ long long max_tiles(long long pairs, int E) {
 }
 }  // namespace
 
-// Regions: xq, h, y16, tiles, meta (256 B).
+// Regions: xq, h, y16, tiles (two lists), meta (256 B).
 size_t ffn_workspace_bytes(long long T, int k, int E, int H, int I) {
   const long long pairs = T * k;
   return up256((size_t)T * H * 2) + up256((size_t)pairs * I * 2) + up256((size_t)pairs * H * 2) +
-         up256((size_t)max_tiles(pairs, E) * sizeof(Tile)) + 256;
+         up256((size_t)2 * max_tiles(pairs, E) * sizeof(Tile)) + 256;
 }
 
 FfnWorkspace carve_ffn_workspace(void *base, long long T, int k, int E, int H, int I) {
@@ -119,7 +119,8 @@ FfnWorkspace carve_ffn_workspace(void *base, long long T, int k, int E, int H, i
   w.y16 = reinterpret_cast<uint16_t *>(p);
   p += up256((size_t)pairs * H * 2);
   w.tiles = reinterpret_cast<Tile *>(p);
-  p += up256((size_t)max_tiles(pairs, E) * sizeof(Tile));
+  w.tile_cap = max_tiles(pairs, E);
+  p += up256((size_t)2 * w.tile_cap * sizeof(Tile));
   w.meta = reinterpret_cast<int *>(p);
   w.bytes = ffn_workspace_bytes(T, k, E, H, I);
   return w;

@@ -51,7 +51,8 @@ struct FfnWorkspace {
   uint16_t *xq;      // fp16 [T][H], fragment slot order (GEMM path)
   uint16_t *h;       // fp16 [pairs][I]
   uint16_t *y16;     // fp16 [pairs][H], pair order (fused combine)
-  Tile *tiles;       // grouped-work list (GEMM path)
+  Tile *tiles;       // GEMM path work lists, [2][tile_cap]: sorted by cost, then in expert order
+  long long tile_cap;
   int *meta;         // meta[0] = number of tiles
   size_t bytes;
 };
