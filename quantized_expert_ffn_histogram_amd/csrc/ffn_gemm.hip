@@ -50,6 +50,10 @@
 
 #include "moe_internal.h"
 
+#ifndef STRATA_PIPE_MMA
+#define STRATA_PIPE_MMA 1
+#endif
+
 namespace strata {
 namespace {
 
@@ -82,7 +86,9 @@ struct GemmArgs {
   int by_cost;
   void *C;             // gate/up: h fp16 [pairs][N] (slot order); down: fp16 y [pairs][N] in pair
                        // order (fused combine follows) or fp32 y [pairs][N] in grouped order
-  int nslices;
+  int a_rows;          // rows of A (T for gate/up, pairs for down)
+  int nslices;         // weight-row slices per tile
+  int spi;             // slices per work item (consecutive slices of one tile)
   int fused;
 };
 
@@ -95,6 +101,22 @@ struct RowTables {
 // conversion from the generic pointer of a __shared__ object explicit.
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 __device__ __forceinline__ lds_ptr_t as_lds(void *p) { return (lds_ptr_t)p; }
+// LDS address `byte_off` bytes into object `p`, with the offset hidden from
+// the optimizer until this point (see gemm_tile_wide: it keeps the compiler
+// from holding every load destination in its own SGPR).
+__device__ __forceinline__ lds_ptr_t lds_at(void *p, uint32_t byte_off) {
+  return (lds_ptr_t)((__attribute__((address_space(3))) char *)as_lds(p) + byte_off);
+}
+
+// Raw buffer resource over `bytes` bytes at `base` (offsets past the end read
+// zeros).  Direct-to-LDS loads through a buffer resource are plain vector-
+// memory operations to the compiler's wait-count tracking, so LDS reads that
+// follow them keep exact lgkmcnt waits; the global-address form is treated as
+// possibly touching LDS through its address as well and turns every later
+// LDS wait of the stage into a full one.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, (int)bytes, 0x00020000);
+}
 
 // Wait until at most N vector-memory operations of this wavefront are
 // outstanding (expcnt and lgkmcnt left unconstrained), N < 64.
@@ -167,6 +189,116 @@ __device__ __forceinline__ void weight_bases(const GemmArgs &a, int e, int slice
     const uint16_t *Sc = up ? a.S1 : a.S0;
     bbase[nb] = reinterpret_cast<const char *>(B + ((size_t)e * a.N + n0) * (a.K / 2));
     sbase[nb] = reinterpret_cast<const char *>(Sc + ((size_t)e * a.N + n0) * (a.K / a.g));
+  }
+}
+
+// Dequant constants held in registers the compiler cannot see through: the
+// nibble masks in SGPRs, the fp16 exponent pattern in a VGPR, so that each
+// masked insert is one v_and_or_b32 written as plain C (which the scheduler
+// can then place like any other VALU instruction).
+struct DequantRegs {
+  uint32_t mask, mask4, magic;
+};
+__device__ __forceinline__ DequantRegs dequant_regs() {
+  DequantRegs r;
+  asm("s_mov_b32 %0, 0xf000f" : "=s"(r.mask));
+  asm("s_mov_b32 %0, 0xf000f0" : "=s"(r.mask4));
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(r.magic));
+  return r;
+}
+// Same arithmetic as dequant8: q = (1024 + u) - 1032 for the low nibble of a
+// half-word, q = (1024 + 16u) / 16 - 72 for the next one, both exact in fp16,
+// then one multiply by the group scale.
+__device__ __forceinline__ half8 dequant8_c(uint32_t d, half2_t s2, const DequantRegs &k) {
+  const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const half2_t off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  const uint32_t d8 = d >> 8;
+  const uint32_t r0 = (d & k.mask) | k.magic;
+  const uint32_t r1 = (d & k.mask4) | k.magic;
+  const uint32_t r2 = (d8 & k.mask) | k.magic;
+  const uint32_t r3 = (d8 & k.mask4) | k.magic;
+  const half2_t h0 = (__builtin_bit_cast(half2_t, r0) - off) * s2;
+  const half2_t h1 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, r1), sixteenth, off16) * s2;
+  const half2_t h2 = (__builtin_bit_cast(half2_t, r2) - off) * s2;
+  const half2_t h3 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, r3), sixteenth, off16) * s2;
+  return half8{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
+}
+
+// Piece q (0..3) of the dequantization of one packed dword for both weight
+// blocks: fp16 pair q of the eight weights (see dequant8_c), for block 0 and
+// block 1 side by side so that no two dependent packed operations are
+// adjacent.
+__device__ __forceinline__ void dequant_piece(int q, const uint32_t (&d)[kNB], const half2_t (&s2)[kNB],
+                                              const DequantRegs &k, uint32_t (&out)[kNB][4]) {
+  const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
+  const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const half2_t off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  uint32_t r[kNB];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    const uint32_t src = q < 2 ? d[nb] : d[nb] >> 8;
+    r[nb] = (src & ((q & 1) ? k.mask4 : k.mask)) | k.magic;
+  }
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) {
+    const half2_t v = __builtin_bit_cast(half2_t, r[nb]);
+    const half2_t qv = (q & 1) ? __builtin_elementwise_fma(v, sixteenth, off16) : v - off;
+    out[nb][q] = __builtin_bit_cast(uint32_t, qv * s2[nb]);
+  }
+}
+
+// One 128-K stage (8 K-steps of 16) of MFMAs, software-pipelined by hand:
+// during the MFMAs of K-step j the weights of K-step j+1 are dequantized (in
+// four pieces) and each token block's fragment of K-step j+1 is read from LDS
+// right after the last MFMA that uses the current one.  `bread(h, nb)` gives
+// the packed weights of 64-K half h, block nb; `afrag(j, mb)` token block
+// mb's fragment of K-step j; `pre(j)` runs at the start of K-step j.  Each
+// token block's group (two MFMAs, one fragment read, its dequant pieces) is
+// closed by a scheduling barrier, so the order is the source order.
+template <int NMB, typename BRead, typename AFrag, typename Pre>
+__device__ __forceinline__ void mma_stage_pipelined(floatx16 (&acc)[NMB][kNB], BRead &&bread,
+                                                    const half2_t (&s2)[2][kNB], AFrag &&afrag, Pre &&pre) {
+  const DequantRegs k = dequant_regs();
+  uint4 bw[kNB];
+#pragma unroll
+  for (int nb = 0; nb < kNB; ++nb) bw[nb] = bread(0, nb);
+  half8 af[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) af[mb] = afrag(0, mb);
+  uint32_t bf[2][kNB][4];
+  {
+    uint32_t d[kNB];
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) d[nb] = dword_of(bw[nb], 0);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dequant_piece(q, d, s2[0], k, bf[0]);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    pre(j);
+    const int cur = j & 1, jn = j + 1;
+    uint32_t d[kNB];
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) d[nb] = dword_of(bw[nb], jn & 3);
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) {
+        const half8 w = __builtin_bit_cast(half8, uint4{bf[cur][nb][0], bf[cur][nb][1], bf[cur][nb][2], bf[cur][nb][3]});
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(w, af[mb], acc[mb][nb], 0, 0, 0);
+      }
+      if (j < 7) {
+        af[mb] = afrag(jn, mb);
+#pragma unroll
+        for (int q = mb * 4 / NMB; q < (mb + 1) * 4 / NMB; ++q) dequant_piece(q, d, s2[jn >> 2], k, bf[cur ^ 1]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (j == 2) {  // half 0's packed weights are dead after K-step 3's dequant
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) bw[nb] = bread(1, nb);
+    }
   }
 }
 
@@ -316,41 +448,44 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const RowTables &rt,
   }
 }
 
-// Persistent loop over (tile, slice) items; `run_tile(nmb, tile, slice)` does one.
-// Workgroups are dispatched to the XCDs round-robin, so blockIdx % 8 names
-// the XCD; the slices of one tile always run side by side in one XCD's L2.
-// by_cost: the list is sorted by cost (number of 32-row token blocks, largest
-// first); tile j belongs to XCD j % 8 and the XCD's workgroups take its items
-// round-robin in that order, so the cheap tiles fill the gaps of the last
-// round (longest-first list scheduling).  Otherwise (expert order) each XCD
-// takes a contiguous range of items, so the tiles of one expert share its
-// weights in L2.
+// Persistent loop over work items; `run_tile(nmb, tile, slice0, nsl)` does
+// one: slices slice0 .. slice0+nsl-1 (spi of them, fewer at the end) of one
+// tile.  Workgroups are dispatched to the XCDs round-robin, so blockIdx % 8
+// names the XCD; the items of one tile always run side by side in one XCD's
+// L2.  by_cost: the list is sorted by cost (number of 32-row token blocks,
+// largest first); tile j belongs to XCD j % 8 and the XCD's workgroups take
+// its items round-robin in that order, so the cheap tiles fill the gaps of
+// the last round (longest-first list scheduling).  Otherwise (expert order)
+// each XCD takes a contiguous range of items, so the tiles of one expert
+// share its weights in L2.
 template <int MODE, typename RunTile>
 __device__ __forceinline__ void gemm_persistent(const GemmArgs &a, RowTables &rt, RunTile &&run_tile) {
   const int tid = threadIdx.x;
   const int ntiles = a.meta[0];
+  const int ipt = (a.nslices + a.spi - 1) / a.spi;  // items per tile
   const int xcd = blockIdx.x % kXcds, lb = blockIdx.x / kXcds, per_xcd_wgs = gridDim.x / kXcds;
   int cnt, start;
   if (a.by_cost) {
-    cnt = (ntiles > xcd ? (ntiles - xcd + kXcds - 1) / kXcds : 0) * a.nslices;
+    cnt = (ntiles > xcd ? (ntiles - xcd + kXcds - 1) / kXcds : 0) * ipt;
     start = 0;
   } else {
-    const int total = ntiles * a.nslices, base = total / kXcds, rem = total % kXcds;
+    const int total = ntiles * ipt, base = total / kXcds, rem = total % kXcds;
     cnt = base + (xcd < rem ? 1 : 0);
     start = xcd * base + min(xcd, rem);
   }
 
   for (int q = lb; q < cnt; q += per_xcd_wgs) {
-    int entry, slice;
+    int entry, part;
     if (a.by_cost) {
-      const int lt = q / a.nslices;
-      slice = q - lt * a.nslices;
+      const int lt = q / ipt;
+      part = q - lt * ipt;
       entry = lt * kXcds + xcd;
     } else {
       const int item = start + q;
-      entry = item / a.nslices;
-      slice = item - entry * a.nslices;
+      entry = item / ipt;
+      part = item - entry * ipt;
     }
+    const int slice0 = part * a.spi, nsl = min(a.spi, a.nslices - slice0);
     const Tile tile = a.tiles[entry];
 
     __syncthreads();  // previous work item is done with LDS and the row tables
@@ -365,7 +500,7 @@ __device__ __forceinline__ void gemm_persistent(const GemmArgs &a, RowTables &rt
       }
     }
     __syncthreads();
-    run_tile((tile.rows + 31) >> 5, tile, slice);
+    run_tile((tile.rows + 31) >> 5, tile, slice0, nsl);
   }
 }
 
@@ -412,18 +547,23 @@ __device__ __forceinline__ int wb_slot(int br, int q) { return br * 4 + (q ^ ((b
 // stage c+1 issued one per K-step between the MFMA groups (a wavefront's
 // load issue then overlaps the other wavefronts' MFMAs instead of all
 // wavefronts issuing together after the barrier).
+// One work item of the wide pipeline: slices slice0 .. slice0+nsl-1 of one
+// tile.  The K stages of consecutive slices form one pipeline: while the last
+// stage of a slice is computed the first stage of the next is already in
+// flight, and the slice's epilogue runs while it lands.
 template <int MODE, int NMB>
 __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0, WideStage &st1, ScaleWindow &sw0,
                                                ScaleWindow &sw1, const RowTables &rt, int e, int row0, int nrows,
-                                               int slice) {
+                                               int slice0, int nsl) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
   const int col = lane & 31, half = lane >> 5;
-  const int nst = a.K / kKS;
+  const int nst = a.K / kKS;  // K stages per slice
   // g is 32, 64 or 128: group and window indexes are shifts.
   const int lg = 31 - __builtin_clz(a.g);  // log2(g)
   const int lpw = lg - 4;                  // log2(stages per 8-group scale window)
   const int ngr = a.K >> lg;               // groups per weight row (a multiple of 8)
+  const int nwin = ngr >> 3;               // scale windows per slice
 
   uint32_t aoff[NMB];
 #pragma unroll
@@ -432,50 +572,87 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
     const int r = p >> 4, c = (p & 15) ^ (r & 15);
     aoff[i] = ((uint32_t)rt.src[r] * (uint32_t)a.K + 8 * c) * 2;
   }
-  const bool valid = weight_row0<MODE, kWideW>(slice, wave, 0) < a.N;
-  const char *bbase[kNB];
-  const char *sbase[kNB];
-  weight_bases<MODE, kWideW>(a, e, slice, wave, valid, bbase, sbase);
   uint32_t boff[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int rr = 16 * t + (lane >> 2);
     boff[t] = (uint32_t)rr * (a.K / 2) + 16 * ((lane & 3) ^ ((rr >> 2) & 3));
   }
-  // Scale loads: lanes 0-31 the rows of block 0, lanes 32-63 those of block 1.
-  const char *sptr = (half ? sbase[1] : sbase[0]) + (size_t)col * ngr * 2;
-  const char *abase = reinterpret_cast<const char *>(a.A);
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(a.A, (uint32_t)a.a_rows * (uint32_t)a.K * 2u);
 
-  auto issue_a = [&](WideStage &st, int c, int i) {
-    __builtin_amdgcn_global_load_lds(abase + aoff[i] + 2 * (c * kKS), as_lds(&st.a[(wave + kWideW * i) * 64]), 16,
-                                     0, 0);
-  };
-  auto issue_b = [&](WideStage &st, int c, int q) {
-    const int nb = q >> 1, t = q & 1;
-    __builtin_amdgcn_global_load_lds(bbase[nb] + boff[t] + c * (kKS / 2),
-                                     as_lds(&st.b[(brow_of(wave, nb, 0) + 16 * t) * 4]), 16, 0, 0);
-  };
-  auto issue_s = [&](int c) {
-    if ((c & ((1 << lpw) - 1)) == 0) {
-      const int win = c >> lpw;
-      if (win & 1)
-        __builtin_amdgcn_global_load_lds(sptr + 16 * win, as_lds(&sw1.s[wave * 64]), 16, 0, 0);
-      else
-        __builtin_amdgcn_global_load_lds(sptr + 16 * win, as_lds(&sw0.s[wave * 64]), 16, 0, 0);
+  // Load cursor: slice lsl, stage lc is the next stage whose loads are issued;
+  // rb / rs are buffer resources over that slice's weight rows and scale rows
+  // of this wavefront's two blocks (32 rows each).
+  constexpr int kRes = kNB;
+  int lsl = slice0, lc = 0;
+  __amdgpu_buffer_rsrc_t rb[kRes], rs[kRes];
+  // This lane's scale row in its block.
+  const uint32_t soff = (uint32_t)col * ngr * 2;
+  auto bases = [&](int sl) {
+    const bool v = weight_row0<MODE, kWideW>(sl, wave, 0) < a.N;
+    const char *bb[kNB];
+    const char *sb[kNB];
+    weight_bases<MODE, kWideW>(a, e, sl, wave, v, bb, sb);
+#pragma unroll
+    for (int r = 0; r < kRes; ++r) {
+      rb[r] = buffer_rsrc(bb[r], 32u * (uint32_t)a.K / 2);
+      rs[r] = buffer_rsrc(sb[r], 32u * (uint32_t)ngr * 2);
     }
   };
-  // Loads of stage c, spread over the 8 K-steps (kk) of the stage before:
-  // the weight rows (from HBM, the longest latency) all at its first K-step,
-  // the token rows (mostly L2 hits) one per K-step after that, the scale
-  // window with the last.
-  auto issue_part = [&](WideStage &st, int c, int kk) {
+  bases(lsl);
+  // Scale windows alternate between sw0 and sw1 in load order.
+  auto window_odd = [&](int sl, int win) { return (((sl - slice0) * nwin + win) & 1) != 0; };
+
+  // Per-wavefront LDS offsets of the load destinations (token rows and scale
+  // windows: 1 KB per wavefront; weight rows: 4 KB), re-derived through an
+  // empty asm once per stage so that each destination is one scalar add from
+  // them instead of a loop-invariant register of its own.
+  uint32_t lds_w1k = 0, lds_w4k = 0;
+  auto refresh_lds_offsets = [&]() {
+    lds_w1k = (uint32_t)wave * 1024u;
+    lds_w4k = (uint32_t)wave * 4096u;
+    asm volatile("" : "+s"(lds_w1k), "+s"(lds_w4k));
+  };
+  auto issue_a = [&](WideStage &st, int i) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, lds_at(st.a, lds_w1k + (uint32_t)(kWideW * i) * 1024u), 16,
+                                             aoff[i] + 2u * (uint32_t)(lc * kKS), 0, 0, 0);
+  };
+  auto issue_b = [&](WideStage &st, int q) {
+    const int nb = q >> 1, t = q & 1;
+    const uint32_t so = (uint32_t)lc * (kKS / 2);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[nb], lds_at(st.b, lds_w4k + (uint32_t)(nb * 2048 + t * 1024)), 16,
+                                             boff[t], so, 0, 0);
+  };
+  // Scale window of the cursor's stage, if it starts one: lanes 0-31 load the
+  // rows of block 0, lanes 32-63 those of block 1 (16 bytes = 8 groups each).
+  auto issue_s = [&]() {
+    if ((lc & ((1 << lpw) - 1)) == 0) {
+      const int win = lc >> lpw;
+      const lds_ptr_t dst = window_odd(lsl, win) ? lds_at(sw1.s, lds_w1k) : lds_at(sw0.s, lds_w1k);
+      if (half == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[0], dst, 16, soff, 16u * win, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[1], dst, 16, soff, 16u * win, 0, 0);
+    }
+  };
+  // The loads of the cursor's stage, spread over the 8 K-steps (kk) of the
+  // stage computed meanwhile: the weight rows (from HBM, the longest latency)
+  // all at the first K-step, so their latency has the whole stage to land,
+  // and the token rows (mostly L2 hits) one per K-step after that.  kk is a
+  // compile-time constant in every caller: no branch splits a K-step.
+  auto issue_part = [&](WideStage &st, int kk) {
     if (kk == 0) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) issue_b(st, c, q);
+      for (int q = 0; q < 4; ++q) issue_b(st, q);
     } else if (kk <= NMB) {
-      issue_a(st, c, kk - 1 < NMB ? kk - 1 : 0);
+      issue_a(st, kk - 1 < NMB ? kk - 1 : 0);
     }
-    if (kk == 7) issue_s(c);
+  };
+  auto advance_loads = [&]() {
+    if (++lc == nst) {
+      lc = 0;
+      if (++lsl < slice0 + nsl) bases(lsl);
+    }
   };
 
   floatx16 acc[NMB][kNB];
@@ -484,14 +661,28 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = floatx16{};
 
-  auto step = [&](const WideStage &cur, WideStage &nxt, int c) {
+  // Compute stage c of slice sl from `cur` while issuing the cursor's loads
+  // into `nxt`.
+  auto slice_epilogue = [&](int esl) {
+    const bool valid = weight_row0<MODE, kWideW>(esl, wave, 0) < a.N;
+    epilogue<MODE, kWideW, NMB>(a, rt, acc, row0, nrows, esl, wave, col, half, valid);
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) acc[mb][nb] = floatx16{};
+  };
+  // Compute stage c of slice sl from `cur`; with MORE (a compile-time flag:
+  // this is not the item's last stage) issue the cursor's loads into `nxt`.
+  auto step = [&](const WideStage &cur, WideStage &nxt, int sl, int c, auto more_c) {
+    constexpr bool MORE = decltype(more_c)::value;
     compiler_fence();
-    wait_vmcnt<0>();               // this wavefront's loads of stage c are done
-    __builtin_amdgcn_s_barrier();  // ... and everyone's; stage c-1's buffer is free
+    wait_vmcnt<0>();               // this wavefront's loads of this stage are done
+    __builtin_amdgcn_s_barrier();  // ... and everyone's; the other stage buffer is free
     compiler_fence();
+    refresh_lds_offsets();
     // Scales of this stage's two 64-K halves (group of K offset kc + 32*half).
     const int win = c >> lpw;
-    const ScaleWindow &sw = (win & 1) ? sw1 : sw0;
+    const ScaleWindow &sw = window_odd(sl, win) ? sw1 : sw0;
     half2_t s2[2][kNB];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -504,6 +695,20 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
       }
     }
     compiler_fence();
+    // The scale window of the cursor's stage, if it starts one (the buffer it
+    // fills was last read two windows ago).
+    if constexpr (MORE) issue_s();
+#if STRATA_PIPE_MMA
+    mma_stage_pipelined<NMB>(
+        acc, [&](int h, int nb) { return cur.b[wb_slot(brow_of(wave, nb, col), 2 * h + half)]; }, s2,
+        [&](int j, int mb) {
+          return __builtin_bit_cast(half8, cur.a[wa_slot(mb * 32 + col, 8 * (j >> 2) + 4 * half + (j & 3))]);
+        },
+        [&](int j) {
+          if constexpr (MORE) issue_part(nxt, j);
+          __builtin_amdgcn_sched_barrier(0);
+        });
+#else
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       uint4 bw[kNB];
@@ -512,21 +717,46 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
       mma_k64_cb<NMB>(acc, bw, s2[s], [&](int j, int mb) {
         return __builtin_bit_cast(half8, cur.a[wa_slot(mb * 32 + col, 8 * s + 4 * half + j)]);
       }, [&](int j) {
-        if (c + 1 < nst) issue_part(nxt, c + 1, 4 * s + j);
+        if constexpr (MORE) issue_part(nxt, 4 * s + j);
         __builtin_amdgcn_sched_barrier(0);
       });
     }
+#endif
+    if constexpr (MORE) advance_loads();
+  };
+  // After stage c of slice sl: the slice's epilogue once its last stage is in.
+  int sl = slice0, c = 0;
+  auto finish = [&]() {
+    if (++c < nst) return;
+    slice_epilogue(sl);
+    c = 0;
+    ++sl;
   };
 
   compiler_fence();
+  refresh_lds_offsets();
+  issue_s();  // the first scale window
 #pragma unroll
-  for (int k = 0; k < 8; ++k) issue_part(st0, 0, k);
-  for (int c = 0; c < nst; c += 2) {
-    step(st0, st1, c);
-    if (c + 1 < nst) step(st1, st0, c + 1);
+  for (int kk = 0; kk < 8; ++kk) issue_part(st0, kk);
+  advance_loads();
+  const std::true_type more;
+  const std::false_type last;
+  const int total = nsl * nst;
+  int gs = 0;
+  for (; gs + 2 < total; gs += 2) {
+    step(st0, st1, sl, c, more);
+    finish();
+    step(st1, st0, sl, c, more);
+    finish();
   }
-  // The last step issued nothing: no load of this tile is in flight.
-  epilogue<MODE, kWideW, NMB>(a, rt, acc, row0, nrows, slice, wave, col, half, valid);
+  const bool two = gs + 1 < total;
+  if (two) {
+    step(st0, st1, sl, c, more);
+    finish();
+  }
+  step(two ? st1 : st0, st0, sl, c, last);
+  finish();
+  // The last step issued nothing: no load of this item is in flight.
 }
 
 // The ring stages and scale windows are distinct LDS objects so the compiler
@@ -536,9 +766,10 @@ __global__ __launch_bounds__(64 * kWideW, 1) void moe_gemm_wide(GemmArgs a) {
   __shared__ WideStage st0, st1;
   __shared__ ScaleWindow sw0, sw1;
   __shared__ RowTables rt;
-  gemm_persistent<MODE>(a, rt, [&](int nmb, const Tile &tile, int slice) {
+  gemm_persistent<MODE>(a, rt, [&](int nmb, const Tile &tile, int slice0, int nsl) {
     dispatch_nmb(nmb, [&](auto n) {
-      gemm_tile_wide<MODE, decltype(n)::value>(a, st0, st1, sw0, sw1, rt, tile.e, tile.row0, tile.rows, slice);
+      gemm_tile_wide<MODE, decltype(n)::value>(a, st0, st1, sw0, sw1, rt, tile.e, tile.row0, tile.rows, slice0,
+                                               nsl);
     });
   });
 }
@@ -667,9 +898,10 @@ __global__ __launch_bounds__(64 * kGenW, 2) void moe_gemm_general(GemmArgs a) {
   __shared__ GenStage st0, st1, st2;
   __shared__ RowTables rt;
   const GenRing R{{&st0, &st1, &st2}};
-  gemm_persistent<MODE>(a, rt, [&](int nmb, const Tile &tile, int slice) {
+  gemm_persistent<MODE>(a, rt, [&](int nmb, const Tile &tile, int slice0, int nsl) {
     dispatch_nmb(nmb, [&](auto n) {
-      gemm_tile_general<MODE, decltype(n)::value>(a, R, rt, tile.e, tile.row0, tile.rows, slice);
+      for (int sl = slice0; sl < slice0 + nsl; ++sl)
+        gemm_tile_general<MODE, decltype(n)::value>(a, R, rt, tile.e, tile.row0, tile.rows, sl);
     });
   });
 }
@@ -756,19 +988,30 @@ int persistent_grid(long long work_upper, int wg_per_cu) {
 #ifndef STRATA_GEMM_WIDE
 #define STRATA_GEMM_WIDE 1
 #endif
+#ifndef STRATA_WIDE_MIN_STAGES
+#define STRATA_WIDE_MIN_STAGES 8
+#endif
 
 // The wide pipeline when the scale windows align with the rows (K/g a
 // multiple of 8), the general one otherwise.
 template <int MODE>
 hipError_t launch_gemm(GemmArgs args, long long tiles_upper, int matrix_rows, hipStream_t s) {
-  const bool wide = STRATA_GEMM_WIDE && args.K % kKS == 0 && (args.K / args.g) % 8 == 0;
+  // The wide pipeline addresses A through a buffer resource: 32-bit offsets.
+  const bool wide = STRATA_GEMM_WIDE && args.K % kKS == 0 && (args.K / args.g) % 8 == 0 &&
+                    (long long)args.a_rows * args.K * 2 < (1LL << 32);
   if (wide) {
     const int width = MODE == 0 ? Shape<kWideW>::kHCols : Shape<kWideW>::kOutCols;
     args.nslices = (matrix_rows + width - 1) / width;
-    moe_gemm_wide<MODE><<<persistent_grid(tiles_upper * args.nslices, 1), 64 * kWideW, 0, s>>>(args);
+    // Items of fewer than 8 K stages pay the pipeline fill too often; join
+    // consecutive slices of a tile until an item has 8 or more.
+    const int nst = args.K / kKS;
+    args.spi = std::max(1, std::min(args.nslices, (STRATA_WIDE_MIN_STAGES + nst - 1) / nst));
+    const long long items = tiles_upper * ((args.nslices + args.spi - 1) / args.spi);
+    moe_gemm_wide<MODE><<<persistent_grid(items, 1), 64 * kWideW, 0, s>>>(args);
   } else {
     const int width = MODE == 0 ? Shape<kGenW>::kHCols : Shape<kGenW>::kOutCols;
     args.nslices = (matrix_rows + width - 1) / width;
+    args.spi = 1;
     moe_gemm_general<MODE><<<persistent_grid(tiles_upper * args.nslices, 2), 64 * kGenW, 0, s>>>(args);
   }
   return hipGetLastError();
@@ -794,6 +1037,7 @@ hipError_t launch_ffn_gemm(const uint16_t *x, int T, int k, const FfnWeights &w,
 
   GemmArgs g{};
   g.A = ws.xq;
+  g.a_rows = T;
   g.B0 = w.gate;
   g.S0 = w.gate_s;
   g.B1 = w.up;
@@ -815,6 +1059,7 @@ hipError_t launch_ffn_gemm(const uint16_t *x, int T, int k, const FfnWeights &w,
 
   GemmArgs d = g;
   d.A = ws.h;
+  d.a_rows = (int)pairs;
   d.B0 = w.down;
   d.S0 = w.down_s;
   d.B1 = nullptr;
