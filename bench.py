@@ -151,6 +151,22 @@ def time_region(fn, steps: int):
     return a.elapsed_time(b) / 1e3  # seconds
 
 
+def step_percentiles(fn, steps: int) -> dict:
+    """Per-step device time (HIP events around each step): p10 / p50 / p90 in us."""
+    import torch
+
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    return {"p10_us": round(float(np.percentile(t, 10)), 2), "p50_us": round(float(np.percentile(t, 50)), 2),
+            "p90_us": round(float(np.percentile(t, 90)), 2)}
+
+
 def kernel_table(qe):
     rows = {}
     for name in qe.timing_kernels():
@@ -253,16 +269,96 @@ def bench_decode(qe, args):
             r = roofline_of(name, table[name]["avg_us"], cfg, cfg.T * cfg.k, avg_distinct, cfg.name)
             kern[name] = {k_: r[k_] for k_ in ("avg_us", "achieved", "frac", "traffic")}
     device_us = sum(v["total_ms"] for v in table.values()) * 1e3 / K
+    pct = step_percentiles(lambda i: run(L[i % n], X[i % n]), min(K, 500))
+
+    # The same steps replayed from HIP graphs, one captured per pre-drawn step
+    # (launch cost off the host); each graph's output is checked against the
+    # eager step first.
+    graph = None
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for i in range(3):
+                run(L[i], X[i])
+        torch.cuda.current_stream().wait_stream(side)
+        graphs = []
+        for i in range(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run(L[i], X[i])
+            graphs.append(g)
+        for i in (0, n // 2, n - 1):
+            ref = run(L[i], X[i]).clone()
+            graphs[i].replay()
+            torch.cuda.synchronize()
+            if not torch.equal(run.out, ref):
+                raise RuntimeError(f"graph replay of step {i} differs from the eager step")
+        for i in range(args.warmup):
+            graphs[i % n].replay()
+        gsecs = time_region(lambda i: graphs[i % n].replay(), K)
+        graph = {"us_per_step": round(gsecs / K * 1e6, 2),
+                 "hbm_frac_step": round(step_bytes / gsecs * K / 1e9 / PEAK_HBM_GBS, 4)}
+        del graphs
+    except Exception as exc:  # reported, not hidden
+        graph = {"error": str(exc)}
     return {
         "workload": "decode: T=4 (1 token + 3 drafts) H=2048 I=512 E=512 k=10 g=64, 64 rotating steps",
         "us_per_step": round(us, 2),
         "device_us_per_step": round(device_us, 2),
+        "step_percentiles": pct,
+        "graph_replay": graph,
         "steps": K,
         "alg_bytes_per_step": int(step_bytes),
         "hbm_frac_step": round(step_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
         "kernels_us": {n: round(v["avg_us"], 2) for n, v in table.items()},
         "roofline": kern,
     }
+
+
+def layer_work(cfg, distinct: int):
+    """Algorithmic work of one whole layer call: (flops, bytes)."""
+    flops = 6.0 * cfg.T * cfg.k * cfg.H * cfg.I
+    nbytes = distinct * expert_weight_bytes(cfg) + cfg.T * (cfg.H * 2 + cfg.E * 4 + cfg.k * 8 + cfg.H * 4)
+    return flops, nbytes
+
+
+def bench_secondary(qe, args):
+    """The other configurations, each timed the same way as the headline one
+    (whole layer, inputs resident, HIP events), against the roofline that
+    bounds it: HBM for small-batch prefill, the matrix cores for the skewed
+    large-chunk prefill; the tiny case is launch-latency bound."""
+    import torch
+
+    import synth
+
+    out = {}
+    dev = torch.device("cuda:0")
+    for name, bound, steps in (("tiny", None, 200), ("prefill512", "hbm", 50), ("zipf6144", "mfma", 10)):
+        cfg = synth.config(name)
+        inp = synth.make_inputs(cfg)
+        logits = torch.from_numpy(inp.logits).to(dev)
+        x = torch.from_numpy(inp.x_bf16.view(np.int16)).to(dev).view(torch.bfloat16)
+        experts = qe.QuantizedExperts.from_numpy(inp.weights, cfg.g, dev)
+        run = qe.LayerRunner(experts, cfg.T, cfg.E, cfg.k, fused=True, device=dev)
+        for _ in range(max(args.warmup, 3)):
+            run(logits, x)
+        secs = time_region(lambda i: run(logits, x), steps)
+        distinct = int((run.counts > 0).sum().item())
+        flops, nbytes = layer_work(cfg, distinct)
+        us = secs / steps * 1e6
+        rec = {"workload": f"{cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} g={cfg.g}",
+               "us_per_step": round(us, 2), "tokens_per_s": round(cfg.T / (us * 1e-6), 1), "steps": steps,
+               "distinct_experts": distinct, "alg_flops": flops, "alg_bytes": int(nbytes)}
+        if bound == "hbm":
+            rec["roofline"] = {"bound": "hbm", "frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        elif bound == "mfma":
+            rec["roofline"] = {"bound": "mfma", "frac": round(flops / (us * 1e-6) / 1e12 / PEAK_MFMA_TFLOPS, 4)}
+        out[name] = rec
+        log(f"[bench] {name}: {us:.1f} us/step")
+        del experts, run, logits, x, inp
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(cfg, inp):
@@ -298,6 +394,7 @@ def main(argv=None) -> int:
     ap.add_argument("--decode-steps", type=int, default=2000)
     ap.add_argument("--workload", default="prefill6144")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the tiny / prefill512 / zipf6144 lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fused", type=int, default=1, help="1: fused weighted scatter-add; 0: y rows + combine")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -363,6 +460,8 @@ def main(argv=None) -> int:
     }
     if not args.no_decode:
         result["decode"] = bench_decode(qe, args)
+    if not args.no_secondary:
+        result["secondary"] = bench_secondary(qe, args)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp)
     print(json.dumps(result), flush=True)
