@@ -36,11 +36,14 @@ METRIC = "MoE-layer prefill tokens/s @6144-tok chunk; decode µs/step; % rooflin
 PEAK_MFMA_TFLOPS = 2500.0  # MI355X dense fp16/bf16 matrix peak
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+_CSRC = "quantized_expert_ffn_histogram_amd/csrc/"
 KERNEL_SOURCES = {
-    "gemm_gateup": "quantized_expert_ffn_histogram_amd/csrc/ffn_gemm.hip",
-    "gemm_down": "quantized_expert_ffn_histogram_amd/csrc/ffn_gemm.hip",
-    "gemv_gateup": "quantized_expert_ffn_histogram_amd/csrc/ffn_gemv.hip",
-    "gemv_down": "quantized_expert_ffn_histogram_amd/csrc/ffn_gemv.hip",
+    "gemm_gateup": [_CSRC + "ffn_gemm.hip"],
+    "gemm_down": [_CSRC + "ffn_gemm.hip"],
+    "gemv_gateup": [_CSRC + "ffn_gemv.hip", _CSRC + "gemv_dev.h"],
+    "gemv_down": [_CSRC + "ffn_gemv.hip", _CSRC + "gemv_dev.h"],
+    "decode_route_gateup": [_CSRC + f for f in ("decode.hip", "gemv_dev.h", "route_dev.h", "permute_dev.h")],
+    "decode_down_combine": [_CSRC + f for f in ("decode.hip", "gemv_dev.h", "route_dev.h", "permute_dev.h")],
 }
 
 
@@ -49,11 +52,14 @@ def log(*a):
 
 
 def source_sha(kernel: str) -> str | None:
-    rel = KERNEL_SOURCES.get(kernel)
-    if rel is None:
+    rels = KERNEL_SOURCES.get(kernel)
+    if rels is None:
         return None
-    with open(os.path.join(ROOT, rel), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for rel in rels:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def counted_traffic(kernel: str, workload: str):
@@ -78,6 +84,8 @@ COUNTED_KERNELS = {
     "moe_gemm_general<1>": ("gemm_down", "prefill"),
     "gemv_gateup_kernel": ("gemv_gateup", "decode"),
     "gemv_down_kernel": ("gemv_down", "decode"),
+    "decode_route_gateup_kernel": ("decode_route_gateup", "decode"),
+    "decode_down_combine_kernel": ("decode_down_combine", "decode"),
 }
 
 
@@ -133,6 +141,10 @@ def kernel_work(kernel: str, cfg, pairs: int, distinct: int):
     if kernel == "gemv_gateup":  # gate + up weights of the selected experts, plus x
         return float(distinct * expert_weight_bytes(cfg, 2) + cfg.T * H * 2), "byte", "hbm"
     if kernel == "gemv_down":  # down weights of the selected experts, plus out
+        return float(distinct * expert_weight_bytes(cfg, 1) + cfg.T * H * 4), "byte", "hbm"
+    if kernel == "decode_route_gateup":  # gate + up weights of the selected experts, x and logits
+        return float(distinct * expert_weight_bytes(cfg, 2) + cfg.T * (H * 2 + cfg.E * 4)), "byte", "hbm"
+    if kernel == "decode_down_combine":  # down weights of the selected experts, plus out
         return float(distinct * expert_weight_bytes(cfg, 1) + cfg.T * H * 4), "byte", "hbm"
     return None, None, None
 
@@ -246,7 +258,10 @@ def bench_decode(qe, args):
     experts = qe.QuantizedExperts.from_numpy(inp.weights, cfg.g, dev)
     L = [torch.from_numpy(lg).to(dev) for lg, _ in steps]
     X = [torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16) for _, xb in steps]
-    run = qe.LayerRunner(experts, cfg.T, cfg.E, cfg.k, fused=True, device=dev)
+    # The step is one strata_moe_layer call (two kernels at this size); the
+    # four separate calls are timed beside it for reference.
+    run = qe.LayerRunner(experts, cfg.T, cfg.E, cfg.k, fused=True, device=dev, single_call=True)
+    run4 = qe.LayerRunner(experts, cfg.T, cfg.E, cfg.k, fused=True, device=dev)
     n = len(steps)
     distinct = []
     for i in range(n):  # also counts the experts each pre-drawn step touches
@@ -264,12 +279,19 @@ def bench_decode(qe, args):
     step_bytes = avg_distinct * expert_weight_bytes(cfg) + cfg.T * (cfg.H * 2 + cfg.E * 4 + cfg.k * 8 + cfg.H * 4)
     us = secs / K * 1e6
     kern = {}
-    for name in ("gemv_gateup", "gemv_down"):
+    for name in ("decode_route_gateup", "decode_down_combine"):
         if name in table:
             r = roofline_of(name, table[name]["avg_us"], cfg, cfg.T * cfg.k, avg_distinct, cfg.name)
             kern[name] = {k_: r[k_] for k_ in ("avg_us", "achieved", "frac", "traffic")}
     device_us = sum(v["total_ms"] for v in table.values()) * 1e3 / K
     pct = step_percentiles(lambda i: run(L[i % n], X[i % n]), min(K, 500))
+    for i in range(args.warmup):
+        run4(L[i % n], X[i % n])
+    secs4 = time_region(lambda i: run4(L[i % n], X[i % n]), K)
+    qe.timing_enable(True)
+    time_region(lambda i: run4(L[i % n], X[i % n]), min(K, 500))
+    table4 = kernel_table(qe)
+    qe.timing_enable(False)
 
     # The same steps replayed from HIP graphs, one captured per pre-drawn step
     # (launch cost off the host); each graph's output is checked against the
@@ -313,6 +335,8 @@ def bench_decode(qe, args):
         "hbm_frac_step": round(step_bytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
         "kernels_us": {n: round(v["avg_us"], 2) for n, v in table.items()},
         "roofline": kern,
+        "four_calls": {"us_per_step": round(secs4 / K * 1e6, 2),
+                       "kernels_us": {n: round(v["avg_us"], 2) for n, v in table4.items()}},
     }
 
 

@@ -166,8 +166,40 @@ int strata_moe_combine(const float *y, const int32_t *inv_perm, const float *top
                        int32_t T, int32_t k, int32_t H, float *out, void *stream);
 
 /*
- * Bytes of device workspace that strata_moe_permute and strata_moe_ffn need
- * for this shape (the larger of the two).  Returns 0 for invalid sizes.
+ * strata_moe_layer - the whole routed FFN layer in one call: routing,
+ * grouping, the expert FFN and the weighted combine, i.e. strata_moe_route,
+ * strata_moe_permute and strata_moe_ffn (with topk_w) in order on one
+ * workspace.  (The layer as a whole: "两天移植，预填充提速8倍：Strata引擎实测"
+ * (kongchang.com), section "Strata快在哪：不是魔法，是物流".)
+ *
+ *   logits, x_bf16, T, k, w  in  as for strata_moe_route and strata_moe_ffn.
+ *   topk_ids, topk_w         out as from strata_moe_route (bit-identical).
+ *   counts, offsets, perm, inv_perm
+ *                            out as from strata_moe_permute (bit-identical).
+ *   out        out float32 [T][H], the layer output (overwritten).
+ *   workspace  device scratch, at least strata_moe_workspace_size() bytes,
+ *              256-byte aligned.
+ *
+ * Decode batches (T <= 16, k <= 16, k * inter <= 16384, hidden in {256, ...,
+ * 4096}, inter a power of two in [128, 2048]; STRATA_MOE_FFN_PATH auto or
+ * gemv) run as two kernels: every expert row block re-selects its token's
+ * expert itself while dedicated blocks write the routing outputs, and the
+ * down projection is token-major: out[t][n] = sum_j topk_w[t][j] *
+ * (W_down[e_j][n] . h(t, j)) in fp32, summed in j order (deterministic, and
+ * without the fp16 rounding of y that the three-call path stores).  Other
+ * shapes, or STRATA_MOE_FFN_PATH=gemm, run the three calls' kernels.
+ * Argument errors are those of the three calls; T = 0 writes counts and
+ * offsets (zeros) only.
+ */
+int strata_moe_layer(const float *logits, const uint16_t *x_bf16, int32_t T, int32_t k,
+                     const strata_moe_weights *w, int32_t *topk_ids, float *topk_w,
+                     int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm,
+                     float *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of device workspace that strata_moe_permute, strata_moe_ffn and
+ * strata_moe_layer need for this shape (the larger of the permute and ffn
+ * needs).  Returns 0 for invalid sizes.
  */
 size_t strata_moe_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H,
                                  int32_t I, int32_t g);
@@ -194,7 +226,7 @@ const char *strata_moe_last_error(void);
  *                               returns how many there are.
  * Kernel names: route_topk, permute_small, permute_hist, permute_scan,
  * permute_scatter, ffn_prep, gemm_gateup, gemm_down, gemv_gateup, gemv_down,
- * combine.
+ * combine, decode_route_gateup, decode_down_combine.
  */
 int strata_moe_timing_enable(int32_t on);
 int strata_moe_timing_query(const char *kernel, int32_t *launches, double *total_ms);

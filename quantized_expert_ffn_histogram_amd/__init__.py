@@ -27,6 +27,7 @@ __all__ = [
     "ffn",
     "combine",
     "moe_layer",
+    "layer",
     "LayerRunner",
     "workspace_size",
     "timing_enable",
@@ -194,6 +195,28 @@ def moe_layer(logits: torch.Tensor, x: torch.Tensor, experts: QuantizedExperts, 
     return res
 
 
+def layer(logits: torch.Tensor, x: torch.Tensor, experts: QuantizedExperts, k: int,
+          workspace: torch.Tensor | None = None) -> dict:
+    """The whole layer in one C-ABI call (strata_moe_layer) on the current stream."""
+    E = experts.num_experts
+    T = x.shape[0]
+    dev = x.device
+    if workspace is None:
+        workspace = _workspace(dev, workspace_size(T, E, k, experts.hidden, experts.inter, experts.group), None)
+    res = dict(ids=torch.empty((T, k), dtype=torch.int32, device=dev),
+               w=torch.empty((T, k), dtype=torch.float32, device=dev),
+               counts=torch.empty(E, dtype=torch.int32, device=dev),
+               offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+               perm=torch.empty(T * k, dtype=torch.int32, device=dev),
+               inv_perm=torch.empty(T * k, dtype=torch.int32, device=dev),
+               out=torch.empty((T, experts.hidden), dtype=torch.float32, device=dev))
+    desc = experts.descriptor()
+    check(load().strata_moe_layer(_p(logits), _p(x), T, k, ctypes.byref(desc), _p(res["ids"]), _p(res["w"]),
+                                  _p(res["counts"]), _p(res["offsets"]), _p(res["perm"]), _p(res["inv_perm"]),
+                                  _p(res["out"]), _p(workspace), workspace.numel(), _stream(x)))
+    return res
+
+
 def timing_enable(on: bool = True) -> None:
     """Start (or stop) per-kernel event timing inside the library; clears old records."""
     check(load().strata_moe_timing_enable(1 if on else 0))
@@ -216,12 +239,14 @@ def timing_kernels() -> list[str]:
 
 
 class LayerRunner:
-    """One layer invocation (route, permute, ffn[, combine]) with preallocated
-    outputs and workspace, for timing loops.  Marshalling only: each call is
-    the same three or four C-ABI calls as ``moe_layer``."""
+    """One layer invocation with preallocated outputs and workspace, for
+    timing loops.  Marshalling only: ``single_call`` runs strata_moe_layer,
+    otherwise the same three or four C-ABI calls as ``moe_layer``."""
 
-    def __init__(self, experts: QuantizedExperts, T: int, E: int, k: int, fused: bool = True, device="cuda"):
+    def __init__(self, experts: QuantizedExperts, T: int, E: int, k: int, fused: bool = True, device="cuda",
+                 single_call: bool = False):
         self.experts, self.T, self.E, self.k, self.fused = experts, T, E, k, fused
+        self.single_call = single_call and fused
         H = experts.hidden
         dev = torch.device(device)
         self.ids = torch.empty((T, k), dtype=torch.int32, device=dev)
@@ -240,6 +265,11 @@ class LayerRunner:
     def __call__(self, logits: torch.Tensor, x: torch.Tensor) -> torch.Tensor:
         lib, T, E, k = self.lib, self.T, self.E, self.k
         s = _stream(x)
+        if self.single_call:
+            check(lib.strata_moe_layer(_p(logits), _p(x), T, k, ctypes.byref(self.desc), _p(self.ids), _p(self.w),
+                                       _p(self.counts), _p(self.offsets), _p(self.perm), _p(self.inv), _p(self.out),
+                                       _p(self.ws), self.ws.numel(), s))
+            return self.out
         check(lib.strata_moe_route(_p(logits), T, E, k, _p(self.ids), _p(self.w), s))
         check(lib.strata_moe_permute(_p(self.ids), T, E, k, _p(self.counts), _p(self.offsets), _p(self.perm),
                                      _p(self.inv), _p(self.ws), self.ws.numel(), s))

@@ -46,6 +46,10 @@ SIGNATURES = {
         [_vp, _i32, _i32, ctypes.POINTER(StrataMoeWeights), _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     ),
     "strata_moe_combine": (ctypes.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
+    "strata_moe_layer": (
+        ctypes.c_int,
+        [_vp, _vp, _i32, _i32, ctypes.POINTER(StrataMoeWeights), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    ),
     "strata_moe_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "strata_moe_last_error": (ctypes.c_char_p, []),
     "strata_moe_timing_enable": (ctypes.c_int, [_i32]),

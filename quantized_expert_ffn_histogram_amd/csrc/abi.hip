@@ -12,10 +12,6 @@
 #include "strata_moe.h"
 #include "moe_internal.h"
 
-namespace strata {
-bool gemv_supported(int T, int H, int I);
-}
-
 using namespace strata;
 
 namespace {
@@ -225,6 +221,69 @@ int strata_moe_ffn(const uint16_t *x_bf16, int32_t T, int32_t k, const strata_mo
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = use_gemv ? launch_ffn_gemv(x_bf16, T, k, fw, offsets, perm, topk_w, y_or_out, ws, s)
                                 : launch_ffn_gemm(x_bf16, T, k, fw, offsets, perm, topk_w, y_or_out, ws, s);
+  return e == hipSuccess ? ok() : hip_fail(fn, e);
+}
+
+int strata_moe_layer(const float *logits, const uint16_t *x_bf16, int32_t T, int32_t k, const strata_moe_weights *w,
+                     int32_t *topk_ids, float *topk_w, int32_t *counts, int32_t *offsets, int32_t *perm,
+                     int32_t *inv_perm, float *out, void *workspace, size_t workspace_bytes, void *stream) {
+  static const char *fn = "strata_moe_layer";
+  if (w == nullptr) return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "w is NULL");
+  const int E = w->num_experts, H = w->hidden, I = w->inter, g = w->group;
+  if (int rc = check_tek(fn, T, E, k)) return rc;
+  if (int rc = check_shape(fn, H, I, g)) return rc;
+  if (!ffn_path_env_valid())
+    return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "STRATA_MOE_FFN_PATH=%s is not one of auto, gemm, gemv",
+                std::getenv("STRATA_MOE_FFN_PATH"));
+  REQUIRE_PTR(fn, counts);
+  REQUIRE_PTR(fn, offsets);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T == 0) {  // counts = 0 and offsets = 0, as strata_moe_permute defines them
+    const hipError_t e = launch_permute(nullptr, 0, E, counts, offsets, nullptr, nullptr, nullptr, s);
+    return e == hipSuccess ? ok() : hip_fail(fn, e);
+  }
+  REQUIRE_PTR(fn, logits);
+  REQUIRE_PTR(fn, x_bf16);
+  REQUIRE_PTR(fn, topk_ids);
+  REQUIRE_PTR(fn, topk_w);
+  REQUIRE_PTR(fn, perm);
+  REQUIRE_PTR(fn, inv_perm);
+  REQUIRE_PTR(fn, out);
+  REQUIRE_PTR(fn, w->gate);
+  REQUIRE_PTR(fn, w->gate_scale);
+  REQUIRE_PTR(fn, w->up);
+  REQUIRE_PTR(fn, w->up_scale);
+  REQUIRE_PTR(fn, w->down);
+  REQUIRE_PTR(fn, w->down_scale);
+  const long long pairs = (long long)T * k;
+  const size_t need = std::max(permute_workspace_bytes(pairs, E), ffn_workspace_bytes(T, k, E, H, I));
+  if (workspace == nullptr)
+    return fail(STRATA_ERR_WORKSPACE, fn, "workspace is NULL but %zu bytes are required", need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "workspace=%p is not 256-byte aligned", workspace);
+  if (workspace_bytes < need)
+    return fail(STRATA_ERR_WORKSPACE, fn, "workspace_bytes=%zu is smaller than the required %zu", workspace_bytes, need);
+
+  const FfnPath forced = ffn_path_env();
+  const bool gemv_ok = gemv_supported(T, H, I);
+  if (forced == FfnPath::Gemv && !gemv_ok)
+    return fail(STRATA_ERR_UNSUPPORTED, fn,
+                "STRATA_MOE_FFN_PATH=gemv needs T <= %d, hidden in {256,512,1024,2048,4096} and inter a power of two "
+                "in [128, 2048] (T=%d, hidden=%d, inter=%d)",
+                kGemvMaxTokens, T, H, I);
+  FfnWeights fw{w->gate, w->up, w->down, w->gate_scale, w->up_scale, w->down_scale, E, H, I, g};
+  const FfnWorkspace ws = carve_ffn_workspace(workspace, T, k, E, H, I);
+  hipError_t e;
+  if (forced != FfnPath::Gemm && decode_layer_supported(T, E, k, H, I)) {
+    e = launch_decode_layer(logits, x_bf16, T, k, fw, topk_ids, topk_w, counts, offsets, perm, inv_perm, out, ws, s);
+  } else {
+    e = launch_route(logits, T, E, k, topk_ids, topk_w, s);
+    if (e == hipSuccess) e = launch_permute(topk_ids, (int)pairs, E, counts, offsets, perm, inv_perm, workspace, s);
+    const bool use_gemv = forced == FfnPath::Gemv || (forced == FfnPath::Auto && gemv_ok);
+    if (e == hipSuccess)
+      e = use_gemv ? launch_ffn_gemv(x_bf16, T, k, fw, offsets, perm, topk_w, out, ws, s)
+                   : launch_ffn_gemm(x_bf16, T, k, fw, offsets, perm, topk_w, out, ws, s);
+  }
   return e == hipSuccess ? ok() : hip_fail(fn, e);
 }
 

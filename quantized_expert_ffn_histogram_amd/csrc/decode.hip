@@ -1,0 +1,284 @@
+// The whole routed FFN layer for a decode batch (T <= 16 tokens: one token
+// plus drafts) in two kernels instead of route / group / gate-up / down /
+// combine one after another.  At this size every kernel is a few
+// microseconds of launch, first-load latency and drain around very little
+// work, so the step time is set by the number of dependent kernels; each
+// decode token is a fresh pass over its experts' weights ("两天移植，预填充
+// 提速8倍：Strata引擎实测" (kongchang.com), section "Strata快在哪：不是魔法，
+// 是物流"), bounded by memory bandwidth over the bytes read (lqnn.cn static
+// review §4.1).
+//
+//   decode_route_gateup (grid: ceil(T/4) routing blocks + T*k*(I/16) others)
+//     routing blocks: one wavefront per token selects its top-k and writes
+//       topk_ids / topk_w exactly as the routing kernel does (same code);
+//     the others: block (pair p = t*k + j, 16 h columns) re-selects the j-th
+//       expert of token t in one wavefront (same code, so the same expert),
+//       then streams that expert's gate and up rows for its columns and
+//       writes h[p] = silu(gate . x_t) * (up . x_t) in fp16, pair order.
+//       The token's activations are loaded before the selection finishes.
+//   decode_down_combine (grid: 1 grouping block + T * H/rows blocks)
+//     grouping block: counts / offsets / perm / inv_perm from topk_ids with
+//       the single-workgroup grouping of the grouping step (same code);
+//     the others: block (token t, rows) stages h of the token's k pairs in
+//       LDS, streams row n of each of its k experts' down weights and writes
+//       out[t][n] = sum_j w[t][j] * (W_down[e_j][n] . h[t*k+j]), summed in j
+//       order: deterministic, with no y round trip and no combine kernel.
+//
+// Dot products are those of the GEMV path (ffn_gemv.hip): fp16 pairs
+// (1024 + u) against fp16 activations with v_dot2_f32_f16 and the exact
+// offset correction per lane.
+#include "gemv_dev.h"
+#include "permute_dev.h"
+#include "route_dev.h"
+
+namespace strata {
+namespace {
+
+constexpr int kDecColsPerWave = 4;                 // h columns per wavefront
+constexpr int kDecCols = 4 * kDecColsPerWave;      // h columns per workgroup
+constexpr int kDecMaxChunks = kGemvMaxHidden / 2048;
+
+struct DecodeArgs {
+  const float *logits;  // fp32 [T][E]
+  const uint16_t *x;    // bf16 [T][H]
+  const uint8_t *gate, *up, *down;
+  const uint16_t *gate_s, *up_s, *down_s;
+  int T, H, I, g, k, E;
+  int *ids;        // [T*k]
+  float *w;        // [T*k]
+  int *counts, *offsets, *perm, *inv_perm;
+  uint16_t *h;     // fp16 [T*k][I], pair order
+  float *out;      // fp32 [T][H]
+};
+
+template <int EPL, int NCH>
+__global__ __launch_bounds__(256) void decode_route_gateup_kernel(DecodeArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nroute = (a.T + 3) / 4;
+  if ((int)blockIdx.x < nroute) {
+    const int t = blockIdx.x * 4 + wave;
+    if (t < a.T) wave_route_token<EPL>(a.logits + (size_t)t * a.E, a.E, a.k, a.ids + t * a.k, a.w + t * a.k);
+    return;
+  }
+  const int colsets = a.I / kDecCols;
+  const int item = blockIdx.x - nroute, p = item / colsets, cs = item - p * colsets;
+  const int t = p / a.k, j = p - t * a.k;
+
+  // Lanes past H (H < 2048) load lane 0's data and get a zero scale.
+  const bool active = 32 * lane < a.H;
+  const int kl = active ? 32 * lane : 0;
+  uint4 xv[NCH][4];
+#pragma unroll
+  for (int c = 0; c < NCH; ++c)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) xv[c][q] = reinterpret_cast<const uint4 *>(a.x + (size_t)t * a.H + 2048 * c + kl)[q];
+
+  __shared__ int e_s;
+  if (wave == 0) {
+    int my_id;
+    float my_val;
+    wave_topk<EPL>(a.logits + (size_t)t * a.E, a.E, j + 1, my_id, my_val);
+    if (lane == j) e_s = my_id;
+  }
+  __syncthreads();
+  const int e = e_s;
+
+  const int kb = a.H / 2, ng = a.H / a.g;
+  const int n0 = cs * kDecCols + wave * kDecColsPerWave;
+  uint4 wg[kDecColsPerWave][NCH], wu[kDecColsPerWave][NCH];
+  uint32_t sgb[kDecColsPerWave][NCH], sub_[kDecColsPerWave][NCH];
+#pragma unroll
+  for (int cc = 0; cc < kDecColsPerWave; ++cc)
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const size_t row = (size_t)e * a.I + n0 + cc;
+      const int kk = 2048 * c + kl;
+      wg[cc][c] = *reinterpret_cast<const uint4 *>(a.gate + row * kb + kk / 2);
+      wu[cc][c] = *reinterpret_cast<const uint4 *>(a.up + row * kb + kk / 2);
+      sgb[cc][c] = a.gate_s[row * ng + kk / a.g];
+      sub_[cc][c] = a.up_s[row * ng + kk / a.g];
+    }
+  const float on = active ? 1.0f : 0.0f;
+  float gs[kDecColsPerWave], us[kDecColsPerWave];
+#pragma unroll
+  for (int cc = 0; cc < kDecColsPerWave; ++cc) gs[cc] = us[cc] = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    half2_t xp[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) bf16x8_pairs(xv[c][q], &xp[4 * q]);
+    float xs = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xs += pair_sum(xp[i]);
+#pragma unroll
+    for (int cc = 0; cc < kDecColsPerWave; ++cc) {
+      gs[cc] += dot32(wg[cc][c], xp, xs, on * half_bits_to_float((uint16_t)sgb[cc][c]));
+      us[cc] += dot32(wu[cc][c], xp, xs, on * half_bits_to_float((uint16_t)sub_[cc][c]));
+    }
+  }
+#pragma unroll
+  for (int cc = 0; cc < kDecColsPerWave; ++cc) {
+    const float gv = group_sum<kWave>(gs[cc]);
+    const float uv = group_sum<kWave>(us[cc]);
+    if (lane == 0) {
+      const float hv = gv / (1.0f + __expf(-gv)) * uv;
+      reinterpret_cast<_Float16 *>(a.h)[(size_t)p * a.I + n0 + cc] = (_Float16)hv;
+    }
+  }
+}
+
+template <int LPR, int KMAX>  // lanes per down row = I / 32; KMAX >= k
+__global__ __launch_bounds__(256) void decode_down_combine_kernel(DecodeArgs a) {
+  constexpr int RPW = kWave / LPR;  // rows per wavefront
+  constexpr int kRowsWG = 4 * RPW;  // output rows per workgroup
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (blockIdx.x == 0) {
+    group_small(a.ids, a.T * a.k, a.E, a.counts, a.offsets, a.perm, a.inv_perm);
+    return;
+  }
+  const int sub = lane % LPR, rsel = lane / LPR;
+  const int rowsets = (a.H + kRowsWG - 1) / kRowsWG;
+  const int item = blockIdx.x - 1, t = item / rowsets, rs = item - t * rowsets;
+  const int n = rs * kRowsWG + wave * RPW + rsel;  // this lane's output row
+  const int nc = n < a.H ? n : 0;                  // rows past H load row 0 and are not stored
+
+  // Lane j (< k) holds pair j's expert and routing weight.
+  const int pj = t * a.k + (lane < a.k ? lane : 0);
+  const int eid = a.ids[pj];
+  const float wj = lane < a.k ? a.w[pj] : 0.0f;
+
+  // h of the token's k pairs (fp16, k * I <= kDecodeMaxKI values) does not
+  // depend on the routing: it goes straight to LDS with direct-to-LDS loads
+  // through a buffer resource (range-checked: slots past k * I read zeros),
+  // issued right after the routing loads (so waiting for those does not wait
+  // for h) and in flight with the weight loads.
+  constexpr int kHLoads = kDecodeMaxKI / 8 / 256;  // 16-byte loads per thread
+  __shared__ uint4 hs[kDecodeMaxKI / 8];
+  {
+    const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.h + (size_t)t * a.k * a.I), 0, a.k * a.I * 2, 0x00020000);
+#pragma unroll
+    for (int i = 0; i < kHLoads; ++i) {
+      const int slot = 256 * i + 64 * wave;  // first uint4 slot of this wavefront's load
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (__attribute__((address_space(3))) void *)&hs[slot], 16,
+                                               (uint32_t)(slot + lane) * 16u, 0, 0, 0);
+    }
+  }
+
+  // Row n of each pair's expert: this lane's 32 K values (16 bytes) and their scale.
+  const int kb = a.I / 2, ng = a.I / a.g;
+  uint4 wq[KMAX];
+  uint32_t sdb[KMAX];
+#pragma unroll
+  for (int jj = 0; jj < KMAX; ++jj) {
+    const int e = __builtin_amdgcn_readlane(eid, jj < a.k ? jj : a.k - 1);  // past k: repeat the last row
+    const size_t row = (size_t)e * a.H + nc;
+    wq[jj] = *reinterpret_cast<const uint4 *>(a.down + row * kb + 16 * sub);
+    sdb[jj] = a.down_s[row * ng + (32 * sub) / a.g];
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wavefront's h loads have landed
+  __syncthreads();                                 // ... and everyone's
+
+  float acc = 0.0f;
+#pragma unroll
+  for (int jj = 0; jj < KMAX; ++jj) {
+    if (jj < a.k) {
+      const uint4 *hrow = hs + (jj * a.I + 32 * sub) / 8;
+      half2_t hp[16];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) f16x8_pairs(hrow[q], &hp[4 * q]);
+      float hsum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) hsum += pair_sum(hp[i]);
+      const float wsel = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), jj));
+      acc += wsel * dot32(wq[jj], hp, hsum, half_bits_to_float((uint16_t)sdb[jj]));
+    }
+  }
+  const float y = group_sum<LPR>(acc);
+  if (sub == 0 && n < a.H) a.out[(size_t)t * a.H + n] = y;
+}
+
+template <int LPR>
+void launch_down_combine(const DecodeArgs &a, int grid, hipStream_t s) {
+  if (a.k <= 4)
+    decode_down_combine_kernel<LPR, 4><<<grid, 256, 0, s>>>(a);
+  else if (a.k <= 8)
+    decode_down_combine_kernel<LPR, 8><<<grid, 256, 0, s>>>(a);
+  else
+    decode_down_combine_kernel<LPR, 16><<<grid, 256, 0, s>>>(a);
+}
+
+template <int NCH>
+void launch_route_gateup(const DecodeArgs &a, int grid, hipStream_t s) {
+  if (a.E <= 64)
+    decode_route_gateup_kernel<1, NCH><<<grid, 256, 0, s>>>(a);
+  else if (a.E <= 128)
+    decode_route_gateup_kernel<2, NCH><<<grid, 256, 0, s>>>(a);
+  else if (a.E <= 256)
+    decode_route_gateup_kernel<4, NCH><<<grid, 256, 0, s>>>(a);
+  else if (a.E <= 512)
+    decode_route_gateup_kernel<8, NCH><<<grid, 256, 0, s>>>(a);
+  else
+    decode_route_gateup_kernel<16, NCH><<<grid, 256, 0, s>>>(a);
+}
+
+}  // namespace
+
+bool decode_layer_supported(int T, int E, int k, int H, int I) {
+  return T >= 1 && T <= kGemvMaxTokens && k <= kDecodeMaxK && E <= kMaxExperts && (long long)k * I <= kDecodeMaxKI &&
+         gemv_supported(T, H, I);
+}
+
+hipError_t launch_decode_layer(const float *logits, const uint16_t *x, int T, int k, const FfnWeights &w,
+                               int *ids, float *topk_w, int *counts, int *offsets, int *perm, int *inv_perm,
+                               float *out, const FfnWorkspace &ws, hipStream_t s) {
+  DecodeArgs a{};
+  a.logits = logits;
+  a.x = x;
+  a.gate = w.gate;
+  a.up = w.up;
+  a.down = w.down;
+  a.gate_s = w.gate_s;
+  a.up_s = w.up_s;
+  a.down_s = w.down_s;
+  a.T = T;
+  a.H = w.H;
+  a.I = w.I;
+  a.g = w.g;
+  a.k = k;
+  a.E = w.E;
+  a.ids = ids;
+  a.w = topk_w;
+  a.counts = counts;
+  a.offsets = offsets;
+  a.perm = perm;
+  a.inv_perm = inv_perm;
+  a.h = ws.h;
+  a.out = out;
+  {
+    KernelTimer timer("decode_route_gateup", s);
+    const int grid = (T + 3) / 4 + T * k * (w.I / kDecCols);
+    if (w.H <= 2048)
+      launch_route_gateup<1>(a, grid, s);
+    else
+      launch_route_gateup<kDecMaxChunks>(a, grid, s);
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  {
+    KernelTimer timer("decode_down_combine", s);
+    const int lpr = w.I / 32;
+    const int rows_wg = 4 * (kWave / lpr);
+    const int grid = 1 + T * ((w.H + rows_wg - 1) / rows_wg);
+    switch (lpr) {
+      case 4: launch_down_combine<4>(a, grid, s); break;
+      case 8: launch_down_combine<8>(a, grid, s); break;
+      case 16: launch_down_combine<16>(a, grid, s); break;
+      case 32: launch_down_combine<32>(a, grid, s); break;
+      default: launch_down_combine<64>(a, grid, s); break;
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace strata

@@ -26,6 +26,11 @@ constexpr int kGemmKChunk = 64;
 constexpr int kGemvMaxTokens = 16;        // auto path picks GEMV at or below this T
 constexpr int kGemvMaxHidden = 4096;
 
+// Fused decode layer (strata_moe_layer at T <= kGemvMaxTokens): top-k per
+// token and h of a token's k pairs staged in LDS (k * I fp16 values).
+constexpr int kDecodeMaxK = 16;
+constexpr int kDecodeMaxKI = 16384;
+
 // One unit of grouped work: `rows` consecutive grouped rows of expert `e`
 // starting at grouped row `row0`.
 struct Tile {
@@ -65,6 +70,15 @@ hipError_t launch_ffn_gemm(const uint16_t *x, int T, int k, const FfnWeights &w,
 hipError_t launch_ffn_gemv(const uint16_t *x, int T, int k, const FfnWeights &w,
                            const int *offsets, const int *perm, const float *topk_w,
                            float *y_or_out, const FfnWorkspace &ws, hipStream_t s);
+
+bool gemv_supported(int T, int H, int I);
+
+// Whole layer for a decode batch in two kernels (route + gate/up, grouping +
+// down + combine); fills every output of route, permute and the fused ffn.
+bool decode_layer_supported(int T, int E, int k, int H, int I);
+hipError_t launch_decode_layer(const float *logits, const uint16_t *x, int T, int k, const FfnWeights &w,
+                               int *ids, float *topk_w, int *counts, int *offsets, int *perm, int *inv_perm,
+                               float *out, const FfnWorkspace &ws, hipStream_t s);
 
 hipError_t launch_combine(const float *y, const int *inv_perm, const float *topk_w, int T,
                           int k, int H, float *out, hipStream_t s);

@@ -157,6 +157,31 @@ def test_ffn_path_override_is_checked(monkeypatch):
     assert "gemv" in _err(lib)
 
 
+def test_layer_rejects_bad_arguments_before_launch(monkeypatch):
+    abi, lib = _lib()
+    fake = ctypes.c_void_p(0x10000)
+    w = _weights(abi)
+
+    def call(T=4, k=2, wp=ctypes.byref(w), counts=fake, logits=fake, ws_bytes=1 << 30):
+        return lib.strata_moe_layer(logits, fake, T, k, wp, fake, fake, counts, fake, fake, fake, fake, fake,
+                                    ws_bytes, None)
+
+    assert call(wp=None) == 1 and "w is NULL" in _err(lib)
+    assert call(k=17) == 1 and "k=17 exceeds E=16" in _err(lib)
+    assert call(T=-1) == 1 and "T=-1" in _err(lib)
+    assert call(counts=None) == 1 and "counts is NULL" in _err(lib)
+    assert call(logits=None) == 1 and "logits is NULL" in _err(lib)
+    assert call(logits=ctypes.c_void_p(0x10004)) == 1 and "not 16-byte aligned" in _err(lib)
+    assert call(ws_bytes=64) == 3 and "workspace_bytes=64" in _err(lib)
+    bad = _weights(abi, g=48)
+    assert call(wp=ctypes.byref(bad)) == 2 and "group=48" in _err(lib)
+    assert _err(lib).startswith("strata_moe_layer")
+    monkeypatch.setenv("STRATA_MOE_FFN_PATH", "fastest")
+    assert call() == 1 and "STRATA_MOE_FFN_PATH=fastest" in _err(lib)
+    monkeypatch.setenv("STRATA_MOE_FFN_PATH", "gemv")
+    assert call(T=64) == 2 and "gemv" in _err(lib)
+
+
 def test_combine_rejects_bad_h():
     _, lib = _lib()
     fake = ctypes.c_void_p(0x10000)

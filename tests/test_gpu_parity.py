@@ -277,8 +277,9 @@ def test_one_hot_routing_layer(qe):
 
 
 # ----------------------------------------------------------------------------- graph replay
+@pytest.mark.parametrize("single", [False, True], ids=["four_calls", "layer_call"])
 @pytest.mark.parametrize("name", ["tiny", "decode", "prefill512"])
-def test_layer_graph_replay(qe, name):
+def test_layer_graph_replay(qe, name, single):
     """A whole layer call (route, permute, fused ffn) captured in a HIP graph
     gives the eager result on every replay.  Between replays the same buffers
     are overwritten by an eager call on other logits and the stream is
@@ -288,7 +289,7 @@ def test_layer_graph_replay(qe, name):
     inp = inputs(name)
     cfg = inp.cfg
     logits, x, experts = to_device(inp)
-    run = qe.LayerRunner(experts, cfg.T, cfg.E, cfg.k, fused=True)
+    run = qe.LayerRunner(experts, cfg.T, cfg.E, cfg.k, fused=True, single_call=single)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -314,3 +315,61 @@ def test_layer_graph_replay(qe, name):
         torch.cuda.synchronize()
         for k_, v in ref.items():
             assert torch.equal(getattr(run, k_), v), f"replay {rep}: {k_} differs from the eager call"
+
+
+# ----------------------------------------------------------------------------- whole-layer call
+LAYER_CFGS = [synth.config("decode")] + GEMV_CFGS + [
+    synth.MoEConfig("layer_e1024", T=3, H=512, I=256, E=1024, k=16, g=64, seed=46),
+    # k * inter at the two-kernel path's limit, one down row per wavefront
+    synth.MoEConfig("layer_i2048", T=2, H=256, I=2048, E=8, k=8, g=128, seed=47),
+    SMALL_CFGS[1],
+]
+
+
+def _two_kernel_shape(cfg):
+    pow2 = lambda v: v & (v - 1) == 0
+    return (cfg.T <= 16 and cfg.k <= 16 and cfg.k * cfg.I <= 16384 and cfg.H <= 4096 and pow2(cfg.H)
+            and 128 <= cfg.I <= 2048 and pow2(cfg.I))
+
+
+@pytest.mark.parametrize("path", ["auto", "gemm"])
+@pytest.mark.parametrize("cfg", LAYER_CFGS, ids=lambda c: c.name)
+def test_layer_call(qe, cfg, path, monkeypatch):
+    """strata_moe_layer: routing and grouping outputs bit-exact against the
+    oracle and identical to the routing call's, out within the tolerance; the
+    decode shapes run as the two fused kernels under the automatic path."""
+    import torch
+
+    monkeypatch.setenv("STRATA_MOE_FFN_PATH", path)
+    inp = inputs(cfg)
+    logits, x, ex = to_device(inp)
+    qe.timing_enable(True)
+    res = qe.layer(logits, x, ex, cfg.k)
+    names = qe.timing_kernels()
+    qe.timing_enable(False)
+    assert ("decode_route_gateup" in names) == (path == "auto" and _two_kernel_shape(cfg)), names
+    ref = oracle.moe_layer(inp.logits, inp.x_bf16, inp.weights, cfg.k, cfg.g)
+    for key in ("ids", "counts", "offsets", "perm", "inv_perm"):
+        assert (_np(res[key]) == ref[key]).all(), key
+    assert np.abs(_np(res["w"]).astype(np.float64) - ref["w"]).max() <= W_ATOL
+    check_close(_np(res["out"]), ref["out"], f"{cfg.name} out")
+    ids, w = qe.route(logits, cfg.k)
+    assert torch.equal(ids, res["ids"]) and torch.equal(w, res["w"])
+
+
+def test_layer_call_repeatable_and_zero_tokens(qe):
+    """The two-kernel decode output is bitwise repeatable across calls with a
+    different step in between; T = 0 writes zero counts and offsets."""
+    import torch
+
+    cfg = synth.config("decode")
+    inp = inputs(cfg)
+    logits, x, ex = to_device(inp)
+    a = qe.layer(logits, x, ex, cfg.k)
+    other = torch.roll(logits, shifts=3, dims=1)
+    qe.layer(other, x, ex, cfg.k)
+    b = qe.layer(logits, x, ex, cfg.k)
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+    z = qe.layer(logits[:0], x[:0], ex, cfg.k)
+    assert int(z["counts"].abs().sum()) == 0 and int(z["offsets"].abs().sum()) == 0
