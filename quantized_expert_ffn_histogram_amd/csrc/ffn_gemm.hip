@@ -376,21 +376,27 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const RowTables &rt,
           hp[i][0] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)hv[0], (_Float16)hv[1]});
           hp[i][1] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)hv[2], (_Float16)hv[3]});
         }
-        uint32_t snd[4], rcv[4];
-        snd[0] = half ? hp[0][0] : hp[2][0];
-        snd[1] = half ? hp[0][1] : hp[2][1];
-        snd[2] = half ? hp[1][0] : hp[3][0];
-        snd[3] = half ? hp[1][1] : hp[3][1];
+        // Half-wave swaps (v_permlane32_swap): for gi = 0, 1 the lanes of
+        // half 0 receive the high four features of group gi from half 1 and
+        // give it the low four of group gi + 2, so afterwards every lane
+        // holds both halves (lo: from half 0, hi: from half 1) of the group
+        // it stores, 2 * half + gi.
+        uint32_t lo[2][2], hi[2][2];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) rcv[x] = __shfl_xor(snd[x], 32, kWave);
+        for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+          for (int d = 0; d < 2; ++d) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(hp[gi][d], hp[gi + 2][d], false, false);
+            lo[gi][d] = sw[0];
+            hi[gi][d] = sw[1];
+          }
         if (r < nrows && valid) {
           uint16_t *hout =
               static_cast<uint16_t *>(a.C) + (size_t)(row0 + r) * a.N + weight_row0<0, W>(slice, wave, hb);
 #pragma unroll
           for (int gi = 0; gi < 2; ++gi) {
             const int grp = 2 * half + gi;  // 8-feature group this lane stores
-            const uint32_t lo0 = half ? rcv[2 * gi] : hp[grp][0], lo1 = half ? rcv[2 * gi + 1] : hp[grp][1];
-            const uint32_t hi0 = half ? hp[grp][0] : rcv[2 * gi], hi1 = half ? hp[grp][1] : rcv[2 * gi + 1];
+            const uint32_t lo0 = lo[gi][0], lo1 = lo[gi][1], hi0 = hi[gi][0], hi1 = hi[gi][1];
             uint4 o;
             o.x = __builtin_amdgcn_perm(hi0, lo0, 0x05040100u);
             o.y = __builtin_amdgcn_perm(hi0, lo0, 0x07060302u);
@@ -415,21 +421,17 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const RowTables &rt,
             yp[i][1] =
                 __builtin_bit_cast(uint32_t, half2_t{(_Float16)acc[mb][nb][4 * i + 2], (_Float16)acc[mb][nb][4 * i + 3]});
           }
-          uint32_t snd[4], rcv[4];
-          snd[0] = half ? yp[0][0] : yp[2][0];
-          snd[1] = half ? yp[0][1] : yp[2][1];
-          snd[2] = half ? yp[1][0] : yp[3][0];
-          snd[3] = half ? yp[1][1] : yp[3][1];
-#pragma unroll
-          for (int x = 0; x < 4; ++x) rcv[x] = __shfl_xor(snd[x], 32, kWave);
+          // The same half-wave swaps as for h.
 #pragma unroll
           for (int gi = 0; gi < 2; ++gi) {
             const int grp = 2 * half + gi;  // 8-feature group this lane stores
+            const auto s0 = __builtin_amdgcn_permlane32_swap(yp[gi][0], yp[gi + 2][0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(yp[gi][1], yp[gi + 2][1], false, false);
             uint4 o;
-            o.x = half ? rcv[2 * gi] : yp[grp][0];      // features 0-1 of the group (from the half-0 lane)
-            o.y = half ? rcv[2 * gi + 1] : yp[grp][1];  // 2-3
-            o.z = half ? yp[grp][0] : rcv[2 * gi];      // 4-5 (from the half-1 lane)
-            o.w = half ? yp[grp][1] : rcv[2 * gi + 1];  // 6-7
+            o.x = s0[0];  // features 0-1 of the group (from the half-0 lane)
+            o.y = s1[0];  // 2-3
+            o.z = s0[1];  // 4-5 (from the half-1 lane)
+            o.w = s1[1];  // 6-7
             *reinterpret_cast<uint4 *>(yrow + weight_row0<1, W>(slice, wave, nb) + 8 * grp) = o;
           }
         }
