@@ -187,7 +187,10 @@ int strata_moe_combine(const float *y, const int32_t *inv_perm, const float *top
  * down projection is token-major: out[t][n] = sum_j topk_w[t][j] *
  * (W_down[e_j][n] . h(t, j)) in fp32, summed in j order (deterministic, and
  * without the fp16 rounding of y that the three-call path stores).  Other
- * shapes, or STRATA_MOE_FFN_PATH=gemm, run the three calls' kernels.
+ * shapes, or STRATA_MOE_FFN_PATH=gemm, run the three calls' kernels; on the
+ * grouped-GEMM path with more than 1024 pairs the routing kernel also
+ * converts x for the GEMM and the grouping scan also builds the GEMM's tile
+ * lists, so the ffn's prologue kernel is not launched (same results).
  * Argument errors are those of the three calls; T = 0 writes counts and
  * offsets (zeros) only.
  */
@@ -198,8 +201,9 @@ int strata_moe_layer(const float *logits, const uint16_t *x_bf16, int32_t T, int
 
 /*
  * Bytes of device workspace that strata_moe_permute, strata_moe_ffn and
- * strata_moe_layer need for this shape (the larger of the permute and ffn
- * needs).  Returns 0 for invalid sizes.
+ * strata_moe_layer need for this shape (the ffn's regions plus the grouping
+ * histogram's, which strata_moe_layer keeps apart).  Returns 0 for invalid
+ * sizes.
  */
 size_t strata_moe_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H,
                                  int32_t I, int32_t g);
@@ -224,9 +228,9 @@ const char *strata_moe_last_error(void);
  *                               writes up to max_names distinct kernel names
  *                               (static strings) in first-launch order and
  *                               returns how many there are.
- * Kernel names: route_topk, permute_small, permute_hist, permute_scan,
- * permute_scatter, ffn_prep, gemm_gateup, gemm_down, gemv_gateup, gemv_down,
- * combine, decode_route_gateup, decode_down_combine.
+ * Kernel names: route_topk, route_xconv, permute_small, permute_hist,
+ * permute_scan, permute_scatter, ffn_prep, gemm_gateup, gemm_down,
+ * gemv_gateup, gemv_down, combine, decode_route_gateup, decode_down_combine.
  */
 int strata_moe_timing_enable(int32_t on);
 int strata_moe_timing_query(const char *kernel, int32_t *launches, double *total_ms);

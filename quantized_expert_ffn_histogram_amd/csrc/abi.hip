@@ -122,6 +122,13 @@ FfnWorkspace carve_ffn_workspace(void *base, long long T, int k, int E, int H, i
   return w;
 }
 
+// What strata_moe_workspace_size reports: the ffn regions, then the grouping
+// histogram in a region of its own (the layer call's routing kernel writes
+// the ffn's fp16 x before the grouping runs).
+size_t layer_workspace_bytes(long long T, int E, int k, int H, int I) {
+  return up256(ffn_workspace_bytes(T, k, E, H, I)) + up256(permute_workspace_bytes(T * k, E));
+}
+
 }  // namespace strata
 
 extern "C" {
@@ -131,8 +138,7 @@ const char *strata_moe_last_error(void) { return g_last_error.c_str(); }
 size_t strata_moe_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t I, int32_t g) {
   if (check_tek("strata_moe_workspace_size", T, E, k) != STRATA_OK) return 0;
   if (check_shape("strata_moe_workspace_size", H, I, g) != STRATA_OK) return 0;
-  const long long pairs = (long long)T * k;
-  return std::max(permute_workspace_bytes(pairs, E), ffn_workspace_bytes(T, k, E, H, I));
+  return layer_workspace_bytes(T, E, k, H, I);
 }
 
 int strata_moe_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *topk_ids,
@@ -256,7 +262,7 @@ int strata_moe_layer(const float *logits, const uint16_t *x_bf16, int32_t T, int
   REQUIRE_PTR(fn, w->down);
   REQUIRE_PTR(fn, w->down_scale);
   const long long pairs = (long long)T * k;
-  const size_t need = std::max(permute_workspace_bytes(pairs, E), ffn_workspace_bytes(T, k, E, H, I));
+  const size_t need = layer_workspace_bytes(T, E, k, H, I);
   if (workspace == nullptr)
     return fail(STRATA_ERR_WORKSPACE, fn, "workspace is NULL but %zu bytes are required", need);
   if (reinterpret_cast<uintptr_t>(workspace) & 255u)
@@ -277,12 +283,23 @@ int strata_moe_layer(const float *logits, const uint16_t *x_bf16, int32_t T, int
   if (forced != FfnPath::Gemm && decode_layer_supported(T, E, k, H, I)) {
     e = launch_decode_layer(logits, x_bf16, T, k, fw, topk_ids, topk_w, counts, offsets, perm, inv_perm, out, ws, s);
   } else {
-    e = launch_route(logits, T, E, k, topk_ids, topk_w, s);
-    if (e == hipSuccess) e = launch_permute(topk_ids, (int)pairs, E, counts, offsets, perm, inv_perm, workspace, s);
     const bool use_gemv = forced == FfnPath::Gemv || (forced == FfnPath::Auto && gemv_ok);
-    if (e == hipSuccess)
-      e = use_gemv ? launch_ffn_gemv(x_bf16, T, k, fw, offsets, perm, topk_w, out, ws, s)
-                   : launch_ffn_gemm(x_bf16, T, k, fw, offsets, perm, topk_w, out, ws, s);
+    if (!use_gemv && pairs > kPermuteSmallMax) {
+      // Grouped-GEMM path in six kernels: the routing kernel also converts x,
+      // the grouping scan also builds the tile lists (no prologue kernel).
+      void *hist = static_cast<char *>(workspace) + (ffn_workspace_bytes(T, k, E, H, I) + 255) / 256 * 256;
+      e = launch_route_convert(logits, T, E, k, topk_ids, topk_w, x_bf16, ws.xq, (size_t)T * H / 8, s);
+      if (e == hipSuccess)
+        e = launch_permute(topk_ids, (int)pairs, E, counts, offsets, perm, inv_perm, hist, s, ws.tiles,
+                           ws.tiles + ws.tile_cap, ws.meta);
+      if (e == hipSuccess) e = launch_ffn_gemm(x_bf16, T, k, fw, offsets, perm, topk_w, out, ws, s, true);
+    } else {
+      e = launch_route(logits, T, E, k, topk_ids, topk_w, s);
+      if (e == hipSuccess) e = launch_permute(topk_ids, (int)pairs, E, counts, offsets, perm, inv_perm, workspace, s);
+      if (e == hipSuccess)
+        e = use_gemv ? launch_ffn_gemv(x_bf16, T, k, fw, offsets, perm, topk_w, out, ws, s)
+                     : launch_ffn_gemm(x_bf16, T, k, fw, offsets, perm, topk_w, out, ws, s);
+    }
   }
   return e == hipSuccess ? ok() : hip_fail(fn, e);
 }

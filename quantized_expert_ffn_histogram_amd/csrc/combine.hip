@@ -31,9 +31,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
 }
 
 // Fused-combine finish: fp16 y rows in pair order, so the k rows of token t
-// are contiguous.  One thread: 8 consecutive features.  The rows are read
-// once and out is not read back here, so both go through non-temporal
-// accesses (they do not displace other data in the caches).
+// are contiguous.  One thread: 8 consecutive features.  All of a thread's
+// row loads are issued before the first is used (KMAX >= k of them, rows past
+// k repeat row k-1 with weight 0), so that each thread keeps k loads in
+// flight.  The rows are read once and out is not read back here, so both go
+// through non-temporal accesses (they do not displace other data in the
+// caches).  Sum in j order, in fp32.
+template <int KMAX>
 __global__ __launch_bounds__(256) void combine_pairs_kernel(const uint4 *__restrict__ y16,
                                                             const float *__restrict__ topk_w, int T, int k,
                                                             int H, float4 *__restrict__ out) {
@@ -41,17 +45,23 @@ __global__ __launch_bounds__(256) void combine_pairs_kernel(const uint4 *__restr
   const long long g = (long long)blockIdx.x * 256 + threadIdx.x;
   if (g >= (long long)T * groups) return;
   const int t = (int)(g / groups), c = (int)(g - (long long)t * groups);
+  u32x4_t v[KMAX];
+  float w[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const int jj = j < k ? j : k - 1;
+    v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(&y16[((size_t)t * k + jj) * groups + c]));
+    w[j] = j < k ? topk_w[(size_t)t * k + jj] : 0.0f;
+  }
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const float w = topk_w[(size_t)t * k + j];
-    const u32x4_t vv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(&y16[((size_t)t * k + j) * groups + c]));
-    const uint4 v = {vv.x, vv.y, vv.z, vv.w};
-    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int j = 0; j < KMAX; ++j) {
+    const uint32_t d[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const auto h2 = __builtin_bit_cast(_Float16 __attribute__((ext_vector_type(2))), d[q]);
-      acc[2 * q] += w * (float)h2.x;
-      acc[2 * q + 1] += w * (float)h2.y;
+      acc[2 * q] += w[j] * (float)h2.x;
+      acc[2 * q + 1] += w[j] * (float)h2.y;
     }
   }
   __builtin_nontemporal_store(f32x4_t{acc[0], acc[1], acc[2], acc[3]}, reinterpret_cast<f32x4_t *>(&out[g * 2]));
@@ -64,8 +74,21 @@ hipError_t launch_combine_pairs(const uint16_t *y16, const float *topk_w, int T,
                                 hipStream_t s) {
   const long long groups = (long long)T * (H / 8);
   KernelTimer timer("combine", s);
-  combine_pairs_kernel<<<dim3((unsigned)((groups + 255) / 256)), 256, 0, s>>>(
-      reinterpret_cast<const uint4 *>(y16), topk_w, T, k, H, reinterpret_cast<float4 *>(out));
+  const dim3 grid((unsigned)((groups + 255) / 256));
+  const uint4 *y = reinterpret_cast<const uint4 *>(y16);
+  float4 *o = reinterpret_cast<float4 *>(out);
+  if (k <= 2)
+    combine_pairs_kernel<2><<<grid, 256, 0, s>>>(y, topk_w, T, k, H, o);
+  else if (k <= 4)
+    combine_pairs_kernel<4><<<grid, 256, 0, s>>>(y, topk_w, T, k, H, o);
+  else if (k <= 8)
+    combine_pairs_kernel<8><<<grid, 256, 0, s>>>(y, topk_w, T, k, H, o);
+  else if (k <= 12)
+    combine_pairs_kernel<12><<<grid, 256, 0, s>>>(y, topk_w, T, k, H, o);
+  else if (k <= 16)
+    combine_pairs_kernel<16><<<grid, 256, 0, s>>>(y, topk_w, T, k, H, o);
+  else
+    combine_pairs_kernel<kMaxTopK><<<grid, 256, 0, s>>>(y, topk_w, T, k, H, o);
   return hipGetLastError();
 }
 

@@ -49,6 +49,7 @@
 #include <type_traits>
 
 #include "moe_internal.h"
+#include "tiles_dev.h"
 
 #ifndef STRATA_PIPE_MMA
 #define STRATA_PIPE_MMA 1
@@ -908,54 +909,6 @@ __global__ __launch_bounds__(64 * kGenW, 2) void moe_gemm_general(GemmArgs a) {
   });
 }
 
-// Tile list from the expert offsets, one workgroup of 1024 threads (E <= 1024).
-// Expert e's rows split into count_e / 128 full tiles and, if a remainder is
-// left, one partial tile of ceil(rem / 32) token blocks.  Tiles are listed by
-// cost class (4 blocks, then 3, 2, 1), each class in expert order, so the
-// list is sorted by cost for the scheduler; `by_expert` gets the same tiles
-// in expert order.  Positions come from one scan of
-// a packed 64-bit count: bits 0-30 hold the 4-block tiles, then three 11-bit
-// fields the 3-, 2- and 1-block ones (at most one per expert, so < 2048).
-__device__ __forceinline__ void plan_tiles(const int *__restrict__ offsets, int E, Tile *__restrict__ tiles,
-                                           Tile *__restrict__ by_expert, int *__restrict__ meta,
-                                           unsigned long long *part) {
-  const int e = threadIdx.x;
-  const int lo = e < E ? offsets[e] : 0;
-  const int c = e < E ? offsets[e + 1] - lo : 0;
-  const int full = c / kGemmRows, rem = c - full * kGemmRows;
-  const int cls = (rem + 31) >> 5;  // blocks of the partial tile, 0 if none
-  auto field = [](int cl) { return 31 + 11 * (3 - cl); };
-  const unsigned long long mine = (unsigned long long)(full + (cls == 4)) |
-                                  (cls >= 1 && cls <= 3 ? 1ull << field(cls) : 0ull);
-  part[e] = mine;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const unsigned long long v = e >= off ? part[e - off] : 0ull;
-    __syncthreads();
-    part[e] += v;
-    __syncthreads();
-  }
-  const unsigned long long tot = part[1023], ex = part[e] - mine;
-  auto count = [](unsigned long long v, int cl) {
-    return cl == 4 ? (int)(v & 0x7FFFFFFFull) : (int)((v >> (31 + 11 * (3 - cl))) & 0x7FFull);
-  };
-  const int pos4 = count(ex, 4);
-  const int epos = pos4 + count(ex, 3) + count(ex, 2) + count(ex, 1);
-  for (int i = 0; i < full; ++i) {
-    const Tile t{e, lo + i * kGemmRows, kGemmRows, 0};
-    tiles[pos4 + i] = t;
-    by_expert[epos + i] = t;
-  }
-  if (cls > 0) {
-    int pos = cls == 4 ? pos4 + full : count(ex, cls);
-    for (int cl = 4; cl > cls; --cl) pos += count(tot, cl);
-    const Tile t{e, lo + full * kGemmRows, rem, 0};
-    tiles[pos] = t;
-    by_expert[epos + full] = t;
-  }
-  if (e == 0) meta[0] = count(tot, 4) + count(tot, 3) + count(tot, 2) + count(tot, 1);
-}
-
 // Prologue of the GEMM path: block 0 builds the tile list; every block
 // converts x (bf16) to fp16 in fragment slot order (grid-stride, 8 elements
 // per thread).
@@ -965,18 +918,7 @@ __global__ __launch_bounds__(1024) void prep_kernel(const int *__restrict__ offs
                                                     uint4 *__restrict__ xq, size_t n8) {
   __shared__ unsigned long long part[1024];
   if (blockIdx.x == 0) plan_tiles(offsets, E, tiles, by_expert, meta, part);
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n8; i += stride) {
-    const uint4 v = x[i];
-    auto lo = [](uint32_t d) { return __uint_as_float(d << 16); };
-    auto hi = [](uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); };
-    uint4 o;
-    o.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo(v.x), lo(v.z)));
-    o.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi(v.x), hi(v.z)));
-    o.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo(v.y), lo(v.w)));
-    o.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(hi(v.y), hi(v.w)));
-    xq[i] = o;
-  }
+  convert_x_slots(x, xq, n8, blockIdx.x, gridDim.x);
 }
 
 // Persistent grid: wg_per_cu workgroups per CU (256 CUs), whole XCD rounds.
@@ -1023,12 +965,12 @@ hipError_t launch_gemm(GemmArgs args, long long tiles_upper, int matrix_rows, hi
 
 hipError_t launch_ffn_gemm(const uint16_t *x, int T, int k, const FfnWeights &w, const int *offsets,
                            const int *perm, const float *topk_w, float *y_or_out,
-                           const FfnWorkspace &ws, hipStream_t s) {
+                           const FfnWorkspace &ws, hipStream_t s, bool prepared) {
   const long long pairs = (long long)T * k;
   const long long tiles_upper = (pairs + kGemmRows - 1) / kGemmRows + std::min<long long>(w.E, pairs);
   const bool fused = topk_w != nullptr;
   hipError_t err;
-  {
+  if (!prepared) {
     KernelTimer timer("ffn_prep", s);
     const size_t n8 = (size_t)T * w.H / 8;
     const int blocks = (int)std::max<size_t>(1, std::min<size_t>(1024, (n8 + 1023) / 1024));

@@ -46,10 +46,18 @@ struct FfnWeights {
 // ---------------------------------------------------------------- launchers
 hipError_t launch_route(const float *logits, int T, int E, int k, int *ids, float *w,
                         hipStream_t s);
+// Routing plus the conversion of x (bf16 [T][H], n8 = T*H/8) to the grouped
+// GEMM's fp16 slot order in xq, in one launch (layer call, GEMM path).
+hipError_t launch_route_convert(const float *logits, int T, int E, int k, int *ids, float *w, const uint16_t *x,
+                                uint16_t *xq, size_t n8, hipStream_t s);
 
 size_t permute_workspace_bytes(long long pairs, int E);
+// With `tiles` non-null (multi-block path only, pairs > kPermuteSmallMax) the
+// scan also writes the grouped-GEMM tile lists: tiles sorted by cost,
+// by_expert in expert order, meta[0] = their number.
 hipError_t launch_permute(const int *ids, int pairs, int E, int *counts, int *offsets,
-                          int *perm, int *inv_perm, void *ws, hipStream_t s);
+                          int *perm, int *inv_perm, void *ws, hipStream_t s, Tile *tiles = nullptr,
+                          Tile *by_expert = nullptr, int *meta = nullptr);
 
 // Workspace carving for the FFN (activations, h, fp16 y rows, tile list).
 struct FfnWorkspace {
@@ -64,9 +72,12 @@ struct FfnWorkspace {
 size_t ffn_workspace_bytes(long long T, int k, int E, int H, int I);
 FfnWorkspace carve_ffn_workspace(void *base, long long T, int k, int E, int H, int I);
 
+// prepared: xq and the tile lists are already in the workspace (the layer
+// call's routing and grouping kernels wrote them); otherwise a prologue
+// kernel makes them from x and offsets.
 hipError_t launch_ffn_gemm(const uint16_t *x, int T, int k, const FfnWeights &w,
                            const int *offsets, const int *perm, const float *topk_w,
-                           float *y_or_out, const FfnWorkspace &ws, hipStream_t s);
+                           float *y_or_out, const FfnWorkspace &ws, hipStream_t s, bool prepared = false);
 hipError_t launch_ffn_gemv(const uint16_t *x, int T, int k, const FfnWeights &w,
                            const int *offsets, const int *perm, const float *topk_w,
                            float *y_or_out, const FfnWorkspace &ws, hipStream_t s);

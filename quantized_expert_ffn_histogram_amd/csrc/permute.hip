@@ -23,6 +23,7 @@
 //                   wavefront then places its pairs in order from there
 // Small inputs (<= kPermuteSmallMax pairs): one workgroup does all three.
 #include "permute_dev.h"
+#include "tiles_dev.h"
 
 namespace strata {
 namespace {
@@ -51,10 +52,16 @@ __global__ __launch_bounds__(256) void seg_hist_kernel(const int *__restrict__ i
 // One workgroup of 1024 threads (E <= 1024): thread e scans column e of hist
 // (segments in order, batches of 32 loads in flight), then the expert totals
 // are scanned across the workgroup.
+// With `tiles` non-null it also builds the grouped-GEMM tile lists from the
+// offsets (the layer call's GEMM path, which then needs no prologue kernel).
 __global__ __launch_bounds__(1024) void seg_scan_kernel(int *__restrict__ hist, int E, int nseg, int pairs,
-                                                        int *__restrict__ counts, int *__restrict__ offsets) {
+                                                        int *__restrict__ counts, int *__restrict__ offsets,
+                                                        Tile *__restrict__ tiles, Tile *__restrict__ by_expert,
+                                                        int *__restrict__ meta) {
   constexpr int B = 32;
   __shared__ int wsum[16];
+  __shared__ int soff[kMaxExperts + 1];
+  __shared__ unsigned long long part[1024];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int total = 0;
   if (tid < E) {
@@ -82,8 +89,16 @@ __global__ __launch_bounds__(1024) void seg_scan_kernel(int *__restrict__ hist, 
   if (tid < E) {
     offsets[tid] = run;
     counts[tid] = total;
+    soff[tid] = run;
   }
-  if (tid == 0) offsets[E] = pairs;
+  if (tid == 0) {
+    offsets[E] = pairs;
+    soff[E] = pairs;
+  }
+  if (tiles != nullptr) {
+    __syncthreads();
+    plan_tiles(soff, E, tiles, by_expert, meta, part);
+  }
 }
 
 // Segment s: wavefront w owns pairs [p0 + w*Q, p0 + (w+1)*Q), Q = kPermuteSeg/4.
@@ -140,8 +155,9 @@ size_t permute_workspace_bytes(long long pairs, int E) {
 }
 
 hipError_t launch_permute(const int *ids, int pairs, int E, int *counts, int *offsets, int *perm,
-                          int *inv_perm, void *ws, hipStream_t s) {
+                          int *inv_perm, void *ws, hipStream_t s, Tile *tiles, Tile *by_expert, int *meta) {
   if (pairs <= kPermuteSmallMax) {
+    if (tiles != nullptr) return hipErrorInvalidValue;  // the tile lists come from the multi-block scan only
     KernelTimer timer("permute_small", s);
     small_permute_kernel<<<1, 256, 0, s>>>(ids, pairs, E, counts, offsets, perm, inv_perm);
     return hipGetLastError();
@@ -154,7 +170,7 @@ hipError_t launch_permute(const int *ids, int pairs, int E, int *counts, int *of
   }
   {
     KernelTimer timer("permute_scan", s);
-    seg_scan_kernel<<<1, 1024, 0, s>>>(hist, E, nseg, pairs, counts, offsets);
+    seg_scan_kernel<<<1, 1024, 0, s>>>(hist, E, nseg, pairs, counts, offsets, tiles, by_expert, meta);
   }
   {
     KernelTimer timer("permute_scatter", s);
