@@ -323,6 +323,10 @@ LAYER_CFGS = [synth.config("decode")] + GEMV_CFGS + [
     # k * inter at the two-kernel path's limit, one down row per wavefront
     synth.MoEConfig("layer_i2048", T=2, H=256, I=2048, E=8, k=8, g=128, seed=47),
     SMALL_CFGS[1],
+    # grouped-GEMM path above 1024 pairs (routing kernel converts x, the scan
+    # builds the tile lists): ragged tiles, and 1024 experts of ~1 pair each
+    synth.MoEConfig("layer_fold", T=600, H=512, I=256, E=8, k=3, g=64, seed=48),
+    synth.MoEConfig("layer_fold_e1024", T=150, H=256, I=128, E=1024, k=8, g=32, seed=49),
 ]
 
 
@@ -347,7 +351,12 @@ def test_layer_call(qe, cfg, path, monkeypatch):
     res = qe.layer(logits, x, ex, cfg.k)
     names = qe.timing_kernels()
     qe.timing_enable(False)
-    assert ("decode_route_gateup" in names) == (path == "auto" and _two_kernel_shape(cfg)), names
+    decode = path == "auto" and _two_kernel_shape(cfg)
+    assert ("decode_route_gateup" in names) == decode, names
+    # The grouped-GEMM path above 1024 pairs runs without the ffn prologue.
+    fold = not decode and cfg.T * cfg.k > 1024
+    assert ("route_xconv" in names) == fold, names
+    assert not (fold and "ffn_prep" in names), names
     ref = oracle.moe_layer(inp.logits, inp.x_bf16, inp.weights, cfg.k, cfg.g)
     for key in ("ids", "counts", "offsets", "perm", "inv_perm"):
         assert (_np(res[key]) == ref[key]).all(), key
