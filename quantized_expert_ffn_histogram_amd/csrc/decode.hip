@@ -204,6 +204,8 @@ void launch_down_combine(const DecodeArgs &a, int grid, hipStream_t s) {
     decode_down_combine_kernel<LPR, 4><<<grid, 256, 0, s>>>(a);
   else if (a.k <= 8)
     decode_down_combine_kernel<LPR, 8><<<grid, 256, 0, s>>>(a);
+  else if (a.k <= 12)  // k = 10: 2 repeated row loads per lane instead of 6
+    decode_down_combine_kernel<LPR, 12><<<grid, 256, 0, s>>>(a);
   else
     decode_down_combine_kernel<LPR, 16><<<grid, 256, 0, s>>>(a);
 }
