@@ -26,15 +26,25 @@ __device__ __forceinline__ void plan_tiles(const int *__restrict__ offsets, int 
   auto field = [](int cl) { return 31 + 11 * (3 - cl); };
   const unsigned long long mine = (unsigned long long)(full + (cls == 4)) |
                                   (cls >= 1 && cls <= 3 ? 1ull << field(cls) : 0ull);
-  part[e] = mine;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const unsigned long long v = e >= off ? part[e - off] : 0ull;
-    __syncthreads();
-    part[e] += v;
-    __syncthreads();
+  // Inclusive scan of the packed counts: within each wavefront by shuffles,
+  // then the 16 wavefront totals through LDS (one barrier).
+  const int lane = e & (kWave - 1), wv = e / kWave;
+  unsigned long long incl = mine;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const unsigned long long t = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += t;
   }
-  const unsigned long long tot = part[1023], ex = part[e] - mine;
+  if (lane == kWave - 1) part[wv] = incl;
+  __syncthreads();
+  unsigned long long tot = 0;
+#pragma unroll
+  for (int w = 0; w < 1024 / kWave; ++w) {
+    const unsigned long long pw = part[w];
+    if (w < wv) incl += pw;
+    tot += pw;
+  }
+  const unsigned long long ex = incl - mine;
   auto count = [](unsigned long long v, int cl) {
     return cl == 4 ? (int)(v & 0x7FFFFFFFull) : (int)((v >> (31 + 11 * (3 - cl))) & 0x7FFull);
   };
