@@ -51,9 +51,6 @@
 #include "moe_internal.h"
 #include "tiles_dev.h"
 
-#ifndef STRATA_PIPE_MMA
-#define STRATA_PIPE_MMA 1
-#endif
 
 namespace strata {
 namespace {
@@ -303,29 +300,9 @@ __device__ __forceinline__ void mma_stage_pipelined(floatx16 (&acc)[NMB][kNB], B
   }
 }
 
-// Four K-steps (64 K) of MFMAs: token fragments from `afrag(j, mb)`, weights
-// from the packed dwords of bw (one per K-step) and the scales s2.
-template <int NMB, typename AFrag, typename Pre>
-__device__ __forceinline__ void mma_k64_cb(floatx16 (&acc)[NMB][kNB], const uint4 (&bw)[kNB],
-                                        const half2_t (&s2)[kNB], AFrag &&afrag, Pre &&pre) {
-  const uint32_t mask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
-  const uint32_t magic = __builtin_amdgcn_readfirstlane(0x64006400u);
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    half8 af[NMB];
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) af[mb] = afrag(j, mb);
-    pre(j);
-#pragma unroll
-    for (int nb = 0; nb < kNB; ++nb) {
-      const half8 bf = dequant8(dword_of(bw[nb], j), s2[nb], mask, magic);
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf, af[mb], acc[mb][nb], 0, 0, 0);
-    }
-  }
-}
-
+// Four K-steps (64 K) of MFMAs (general pipeline): token fragments from
+// `afrag(j, mb)`, weights from the packed dwords of bw (one per K-step) and
+// the scales s2.
 template <int NMB, typename AFrag>
 __device__ __forceinline__ void mma_k64(floatx16 (&acc)[NMB][kNB], const uint4 (&bw)[kNB],
                                         const half2_t (&s2)[kNB], AFrag &&afrag) {
@@ -701,7 +678,6 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
     // The scale window of the cursor's stage, if it starts one (the buffer it
     // fills was last read two windows ago).
     if constexpr (MORE) issue_s();
-#if STRATA_PIPE_MMA
     mma_stage_pipelined<NMB>(
         acc, [&](int h, int nb) { return cur.b[wb_slot(brow_of(wave, nb, col), 2 * h + half)]; }, s2,
         [&](int j, int mb) {
@@ -711,20 +687,6 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
           if constexpr (MORE) issue_part(nxt, j);
           __builtin_amdgcn_sched_barrier(0);
         });
-#else
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      uint4 bw[kNB];
-#pragma unroll
-      for (int nb = 0; nb < kNB; ++nb) bw[nb] = cur.b[wb_slot(brow_of(wave, nb, col), 2 * s + half)];
-      mma_k64_cb<NMB>(acc, bw, s2[s], [&](int j, int mb) {
-        return __builtin_bit_cast(half8, cur.a[wa_slot(mb * 32 + col, 8 * s + 4 * half + j)]);
-      }, [&](int j) {
-        if constexpr (MORE) issue_part(nxt, 4 * s + j);
-        __builtin_amdgcn_sched_barrier(0);
-      });
-    }
-#endif
     if constexpr (MORE) advance_loads();
   };
   // After stage c of slice sl: the slice's epilogue once its last stage is in.
