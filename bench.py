@@ -392,7 +392,56 @@ def bench_secondary(qe, args):
         log(f"[bench] {name}: {us:.1f} us/step")
         del experts, run, logits, x, inp
         torch.cuda.empty_cache()
+    out["router6144"] = bench_router(qe, args)
     return out
+
+
+def bench_router(qe, args):
+    """The router projection in front of the top-k (strata_moe_router) at the
+    prefill chunk's shape: T=6144 tokens, H=2048, E=512 router rows, k=10.
+    Work: 2*T*H*E flops of bf16 matmul; bytes: x and W_r read once, fp32
+    logits written, ids and weights written."""
+    import torch
+
+    import synth
+
+    T, H, E, k = 6144, 2048, 512, 10
+    dev = torch.device("cuda:0")
+    xb, wb = synth.make_router(T, H, E, seed=61)
+    x = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+    w = torch.from_numpy(wb.view(np.int16)).to(dev).view(torch.bfloat16)
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+    lib = qe.load()
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def call(_i):
+        rc = lib.strata_moe_router(x.data_ptr(), T, H, w.data_ptr(), E, k, logits.data_ptr(), ids.data_ptr(),
+                                   wts.data_ptr(), stream)
+        if rc != 0:
+            raise RuntimeError(lib.strata_moe_last_error().decode())
+
+    steps = 50
+    for i in range(max(args.warmup, 3)):
+        call(i)
+    secs = time_region(call, steps)
+    qe.timing_enable(True)
+    for i in range(10):
+        call(i)
+    torch.cuda.synchronize()
+    kern = {n: round(qe.timing_query(n)[1] / max(qe.timing_query(n)[0], 1) * 1e3, 2) for n in qe.timing_kernels()}
+    qe.timing_enable(False)
+    us = secs / steps * 1e6
+    flops = 2.0 * T * H * E
+    nbytes = T * H * 2 + E * H * 2 + T * E * 4 + T * k * 8
+    proj_us = kern.get("router_logits")
+    log(f"[bench] router6144: {us:.1f} us/call {kern}")
+    return {"workload": f"router6144: T={T} H={H} E={E} k={k} (bf16 projection, then top-k)",
+            "us_per_call": round(us, 2), "steps": steps, "kernels_us": kern, "alg_flops": flops, "alg_bytes": nbytes,
+            "roofline_projection": None if not proj_us else {
+                "mfma_frac": round(flops / (proj_us * 1e-6) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+                "hbm_frac": round((T * H * 2 + E * H * 2 + T * E * 4) / (proj_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}}
 
 
 def cpu_baseline(cfg, inp):
@@ -431,6 +480,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-secondary", action="store_true", help="skip the tiny / prefill512 / zipf6144 lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fused", type=int, default=1, help="1: fused weighted scatter-add; 0: y rows + combine")
+    ap.add_argument("--router-only", action="store_true",
+                    help="time only the router projection + top-k call (router6144) and print its record")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -458,6 +509,9 @@ def main(argv=None) -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     qe.load()
+    if args.router_only:
+        print(json.dumps(bench_router(qe, args)), flush=True)
+        return 0
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

@@ -96,6 +96,25 @@ int strata_moe_route(const float *logits, int32_t T, int32_t E, int32_t k,
                      int32_t *topk_ids, float *topk_w, void *stream);
 
 /*
+ * strata_moe_router - the router projection in front of the top-k selection:
+ * logits = x . W_r^T, then exactly strata_moe_route on those logits.  (The
+ * router that scores the experts of each token before a few are picked:
+ * "两天移植，预填充提速8倍：Strata引擎实测" (kongchang.com), section
+ * "Strata快在哪：不是魔法，是物流", MoE note.)
+ *
+ *   x_bf16         in  bf16 bits [T][H], row-major.
+ *   w_router_bf16  in  bf16 bits [E][H], row-major (one row per expert).
+ *   logits         out float32 [T][E]: sum_h x[t][h] * W_r[e][h], products
+ *                  exact in fp32, accumulated in fp32 (MFMA order).
+ *   topk_ids, topk_w  out as from strata_moe_route on `logits`.
+ *
+ * H must be a multiple of 64 in [64, 16384], T*H and E*H below 2^30; E and
+ * k as for strata_moe_route.  T = 0 does nothing.  Pointers 16-byte aligned.
+ */
+int strata_moe_router(const uint16_t *x_bf16, int32_t T, int32_t H, const uint16_t *w_router_bf16, int32_t E,
+                      int32_t k, float *logits, int32_t *topk_ids, float *topk_w, void *stream);
+
+/*
  * strata_moe_permute - group the T*k (token, slot) pairs by expert.
  * (Tokens routed to one expert are batched together: kongchang.com hands-on,
  * section "Strata快在哪".)
@@ -228,7 +247,7 @@ const char *strata_moe_last_error(void);
  *                               writes up to max_names distinct kernel names
  *                               (static strings) in first-launch order and
  *                               returns how many there are.
- * Kernel names: route_topk, route_xconv, permute_small, permute_hist,
+ * Kernel names: router_logits, route_topk, route_xconv, permute_small, permute_hist,
  * permute_scan, permute_scatter, ffn_prep, gemm_gateup, gemm_down,
  * gemv_gateup, gemv_down, combine, decode_route_gateup, decode_down_combine.
  */

@@ -38,6 +38,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
+    "router_logits",
     "route",
     "histogram",
     "exclusive_scan",
@@ -52,6 +53,20 @@ __all__ = [
     "moe_layer",
     "moe_out_tokens",
 ]
+
+
+def router_logits(x_bf16: np.ndarray, w_router_bf16: np.ndarray) -> np.ndarray:
+    """Router projection: logits[t][e] = sum_h x[t][h] * W_r[e][h], in fp64.
+
+    The router scores every expert for every token before the top-k picks a
+    few (kongchang.com hands-on, section "Strata快在哪：不是魔法，是物流", the
+    MoE note; penglei.dev "Strata local MoE", section "原理一").  Inputs are
+    bf16 bit patterns (x [T][H], W_r [E][H]), widened exactly; the fp64
+    matmul is one step.  Selections made on these logits are compared with
+    the library's on its own fp32 logits (the decision is taken in the
+    kernel's precision), the logits themselves within an error bound.
+    """
+    return bf16_to_f64(x_bf16) @ bf16_to_f64(w_router_bf16).T
 
 
 def route(logits: np.ndarray, k: int) -> tuple[np.ndarray, np.ndarray]:

@@ -30,6 +30,7 @@ __all__ = [
     "layer",
     "LayerRunner",
     "workspace_size",
+    "router",
     "timing_enable",
     "timing_query",
     "timing_kernels",
@@ -124,6 +125,23 @@ def route(logits: torch.Tensor, k: int):
     w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
     check(load().strata_moe_route(_p(logits), T, E, k, _p(ids), _p(w), _stream(logits)))
     return ids, w
+
+
+def router(x: torch.Tensor, w_router: torch.Tensor, k: int):
+    """``strata_moe_router``: router projection then top-k.  x bf16 [T, H],
+    w_router bf16 [E, H]; returns (logits float32 [T, E], topk_ids int32
+    [T, k], topk_w float32 [T, k])."""
+    _need(x, torch.bfloat16, "x")
+    _need(w_router, torch.bfloat16, "w_router")
+    T, H = x.shape
+    E = w_router.shape[0]
+    if w_router.shape[1] != H:
+        raise ValueError(f"w_router has {w_router.shape[1]} columns, x has {H}")
+    logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    ids = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    check(load().strata_moe_router(_p(x), T, H, _p(w_router), E, k, _p(logits), _p(ids), _p(w), _stream(x)))
+    return logits, ids, w
 
 
 def permute(topk_ids: torch.Tensor, E: int, workspace: torch.Tensor | None = None):

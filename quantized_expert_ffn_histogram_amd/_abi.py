@@ -40,6 +40,7 @@ class StrataMoeWeights(ctypes.Structure):
 
 SIGNATURES = {
     "strata_moe_route": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "strata_moe_router": (ctypes.c_int, [_vp, _i32, _i32, _vp, _i32, _i32, _vp, _vp, _vp, _vp]),
     "strata_moe_permute": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "strata_moe_ffn": (
         ctypes.c_int,

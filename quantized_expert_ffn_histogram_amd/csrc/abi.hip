@@ -153,6 +153,26 @@ int strata_moe_route(const float *logits, int32_t T, int32_t E, int32_t k, int32
   return e == hipSuccess ? ok() : hip_fail(fn, e);
 }
 
+int strata_moe_router(const uint16_t *x_bf16, int32_t T, int32_t H, const uint16_t *w_router_bf16, int32_t E,
+                      int32_t k, float *logits, int32_t *topk_ids, float *topk_w, void *stream) {
+  static const char *fn = "strata_moe_router";
+  if (int rc = check_tek(fn, T, E, k)) return rc;
+  if (H < 64 || H > 16384 || H % 64)
+    return fail(STRATA_ERR_UNSUPPORTED, fn, "H=%d must be a multiple of 64 in [64, 16384]", H);
+  if ((long long)T * H * 2 >= (1ll << 31) || (long long)E * H * 2 >= (1ll << 31))
+    return fail(STRATA_ERR_UNSUPPORTED, fn, "T*H and E*H must stay below 2^30 elements (T=%d, E=%d, H=%d)", T, E, H);
+  if (T == 0) return ok();
+  REQUIRE_PTR(fn, x_bf16);
+  REQUIRE_PTR(fn, w_router_bf16);
+  REQUIRE_PTR(fn, logits);
+  REQUIRE_PTR(fn, topk_ids);
+  REQUIRE_PTR(fn, topk_w);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = launch_router_logits(x_bf16, T, H, w_router_bf16, E, logits, s);
+  if (e == hipSuccess) e = launch_route(logits, T, E, k, topk_ids, topk_w, s);
+  return e == hipSuccess ? ok() : hip_fail(fn, e);
+}
+
 int strata_moe_permute(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k, int32_t *counts,
                        int32_t *offsets, int32_t *perm, int32_t *inv_perm, void *workspace,
                        size_t workspace_bytes, void *stream) {

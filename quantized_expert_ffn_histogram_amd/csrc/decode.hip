@@ -55,9 +55,11 @@ template <int EPL, int NCH>
 __global__ __launch_bounds__(256) void decode_route_gateup_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nroute = (a.T + 3) / 4;
+  __shared__ TopkScratch sc[4];
   if ((int)blockIdx.x < nroute) {
     const int t = blockIdx.x * 4 + wave;
-    if (t < a.T) wave_route_token<EPL>(a.logits + (size_t)t * a.E, a.E, a.k, a.ids + t * a.k, a.w + t * a.k);
+    if (t < a.T)
+      wave_route_token<EPL>(a.logits + (size_t)t * a.E, a.E, a.k, a.ids + t * a.k, a.w + t * a.k, sc[wave]);
     return;
   }
   const int colsets = a.I / kDecCols;
@@ -77,7 +79,7 @@ __global__ __launch_bounds__(256) void decode_route_gateup_kernel(DecodeArgs a) 
   if (wave == 0) {
     int my_id;
     float my_val;
-    wave_topk<EPL>(a.logits + (size_t)t * a.E, a.E, j + 1, my_id, my_val);
+    wave_topk<EPL>(a.logits + (size_t)t * a.E, a.E, j + 1, my_id, my_val, sc[0]);
     if (lane == j) e_s = my_id;
   }
   __syncthreads();

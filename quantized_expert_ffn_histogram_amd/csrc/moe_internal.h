@@ -46,6 +46,9 @@ struct FfnWeights {
 // ---------------------------------------------------------------- launchers
 hipError_t launch_route(const float *logits, int T, int E, int k, int *ids, float *w,
                         hipStream_t s);
+// Router projection logits[t][e] = x[t] . w_router[e] (bf16 in, fp32 out).
+hipError_t launch_router_logits(const uint16_t *x, int T, int H, const uint16_t *w_router, int E, float *logits,
+                                hipStream_t s);
 // Routing plus the conversion of x (bf16 [T][H], n8 = T*H/8) to the grouped
 // GEMM's fp16 slot order in xq, in one launch (layer call, GEMM path).
 hipError_t launch_route_convert(const float *logits, int T, int E, int k, int *ids, float *w, const uint16_t *x,

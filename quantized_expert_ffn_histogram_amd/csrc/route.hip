@@ -6,11 +6,12 @@
 //
 // Every lane holds ceil(E/64) logits as order-preserving unsigned keys
 // (-0.0 is canonicalised to +0.0 first, so signed zeros tie as under IEEE
-// equality).  Each of k rounds takes the wavefront maximum key and then the
-// minimum expert index among the lanes holding it (ties go to the lowest
-// index; with a single holder that is the holder's own candidate), and
-// removes the winner.  Lane j then owns winner j, and the softmax
-// over the k selected logits is a wavefront sum in fixed order.
+// equality); the k winners are the first k in the order (key descending,
+// expert index ascending).  A threshold from the lane maxima leaves a few
+// candidates, which are ranked against each other in LDS (route_dev.h; many
+// equal logits fall back to k rounds of wavefront maxima).  Lane j then owns
+// winner j, and the softmax over the k selected logits is a wavefront sum in
+// fixed order.
 #include <algorithm>
 
 #include "route_dev.h"
@@ -23,26 +24,31 @@ template <int EPL>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float *__restrict__ logits, int T,
                                                          int E, int k, int *__restrict__ ids,
                                                          float *__restrict__ w) {
+  __shared__ TopkScratch sc[4];
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  wave_route_token<EPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
+  wave_route_token<EPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k, sc[threadIdx.x >> 6]);
 }
 
-// Routing plus the grouped-GEMM path's conversion of x to fp16: workgroups
-// below nroute route 4 tokens each, the others convert x (the two are
-// independent; sharing one launch saves a kernel boundary in the layer call).
+// Routing plus the grouped-GEMM path's conversion of x to fp16: the first
+// gridDim.x - nroute workgroups convert x, the other nroute route 4 tokens
+// each (the two are independent; sharing one launch saves a kernel boundary
+// in the layer call).  The streaming conversion blocks go first so that they
+// start together and the routing blocks fill in around them.
 template <int EPL>
 __global__ __launch_bounds__(256) void route_convert_kernel(const float *__restrict__ logits, int T, int E, int k,
                                                             int *__restrict__ ids, float *__restrict__ w,
                                                             const uint4 *__restrict__ x, uint4 *__restrict__ xq,
                                                             size_t n8, int nroute) {
-  if ((int)blockIdx.x >= nroute) {
-    convert_x_slots(x, xq, n8, blockIdx.x - nroute, gridDim.x - nroute);
+  const int nconv = gridDim.x - nroute;
+  if ((int)blockIdx.x < nconv) {
+    convert_x_slots(x, xq, n8, blockIdx.x, nconv);
     return;
   }
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ TopkScratch sc[4];
+  const int t = (blockIdx.x - nconv) * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
-  wave_route_token<EPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
+  wave_route_token<EPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k, sc[threadIdx.x >> 6]);
 }
 
 }  // namespace

@@ -8,6 +8,7 @@ from .gen import (  # noqa: F401
     decode_steps,
     make_inputs,
     make_logits,
+    make_router,
     make_x,
     quantize_int4_groups,
     weight_bytes_per_expert,

@@ -148,6 +148,17 @@ def make_x(cfg: MoEConfig, seq: np.random.SeedSequence) -> np.ndarray:
     return bf16_bits_from_f32(rng.standard_normal((cfg.T, cfg.H), dtype=np.float32))
 
 
+def make_router(T: int, H: int, E: int, seed: int) -> tuple[np.ndarray, np.ndarray]:
+    """Inputs of the router projection: x bf16 [T][H] ~ N(0, 1) and router
+    rows W_r bf16 [E][H] ~ N(0, 1/H), so that the logits x . W_r^T are about
+    N(0, 1) like the logits of the layer configurations.  Returns bf16 bit
+    patterns (uint16)."""
+    sx, sw = np.random.SeedSequence(seed).spawn(2)
+    x = np.random.default_rng(sx).standard_normal((T, H), dtype=np.float32)
+    w = np.random.default_rng(sw).standard_normal((E, H), dtype=np.float32) * np.float32(1.0 / np.sqrt(H))
+    return bf16_bits_from_f32(x), bf16_bits_from_f32(w)
+
+
 def _expert_weights(cfg: MoEConfig, seq, e: int, out: dict) -> None:
     rng = np.random.default_rng(seq)
     std = np.float32(WEIGHT_STD)

@@ -89,6 +89,35 @@ def test_route_rejects_null_and_misaligned_pointers():
     assert "not 16-byte aligned" in _err(lib)
 
 
+@pytest.mark.parametrize(
+    "T,H,E,k,code,needle",
+    [
+        (4, 100, 16, 2, 2, "H=100"),
+        (4, 0, 16, 2, 2, "H=0"),
+        (4, 32768, 16, 2, 2, "H=32768"),
+        (4, 256, 16, 17, 1, "k=17 exceeds E=16"),
+        (-1, 256, 16, 2, 1, "T=-1"),
+        (1 << 20, 2048, 16, 2, 2, "2^30"),
+    ],
+)
+def test_router_rejects_bad_sizes(T, H, E, k, code, needle):
+    _, lib = _lib()
+    assert lib.strata_moe_router(None, T, H, None, E, k, None, None, None, None) == code
+    assert needle in _err(lib)
+    assert _err(lib).startswith("strata_moe_router")
+
+
+def test_router_rejects_null_and_misaligned_pointers():
+    _, lib = _lib()
+    assert lib.strata_moe_router(None, 4, 256, None, 16, 2, None, None, None, None) == 1
+    assert "x_bf16 is NULL" in _err(lib)
+    assert lib.strata_moe_router(ctypes.c_void_p(0x1000), 4, 256, ctypes.c_void_p(0x2008), 16, 2,
+                                 ctypes.c_void_p(0x3000), ctypes.c_void_p(0x4000), ctypes.c_void_p(0x5000),
+                                 None) == 1
+    assert "not 16-byte aligned" in _err(lib)
+    assert lib.strata_moe_router(None, 0, 256, None, 16, 2, None, None, None, None) == 0  # T = 0: nothing
+
+
 def test_zero_tokens_is_ok_and_launches_nothing():
     _, lib = _lib()
     assert lib.strata_moe_route(None, 0, 16, 2, None, None, None) == 0

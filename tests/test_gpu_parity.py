@@ -65,6 +65,8 @@ def test_route_bitexact(qe, name):
         (9, 1, 1, "normal"),
         (11, 32, 32, "grid"),
         (3, 64, 1, "huge"),
+        (500, 512, 10, "grid_fine"),
+        (60, 40, 30, "neg_max"),
     ],
 )
 def test_route_ties_and_shapes(qe, T, E, k, kind):
@@ -81,6 +83,10 @@ def test_route_ties_and_shapes(qe, T, E, k, kind):
         logits[:, ::5] = -1.0
     elif kind == "huge":
         logits = z * 1e30
+    elif kind == "grid_fine":  # a few ties among the leading candidates
+        logits = np.round(z * 32) / 32
+    elif kind == "neg_max":  # about half at the most negative float, so some selected ones tie there
+        logits = np.where(rng.random((T, E)) < 0.5, np.finfo(np.float32).min, z)
     else:
         logits = z
     _check_route(qe, logits.astype(np.float32), k)
@@ -382,3 +388,39 @@ def test_layer_call_repeatable_and_zero_tokens(qe):
         assert torch.equal(a[key], b[key]), key
     z = qe.layer(logits[:0], x[:0], ex, cfg.k)
     assert int(z["counts"].abs().sum()) == 0 and int(z["offsets"].abs().sum()) == 0
+
+
+# ----------------------------------------------------------------------------- router projection
+ROUTER_CFGS = [
+    (6144, 2048, 512, 10, 61),  # the prefill chunk's tokens and expert pool
+    (100, 128, 37, 5, 62),      # tokens and experts off the 128 tile, E % 4 != 0
+    (1, 64, 1, 1, 63),          # one token, one expert, one K stage
+    (70, 448, 130, 4, 65),      # seven K stages: one ring turn of four, then three more
+    (257, 320, 1024, 32, 64),   # largest E and k, odd number of K stages
+]
+
+
+@pytest.mark.parametrize("T,H,E,k,seed", ROUTER_CFGS)
+def test_router_projection_then_topk(qe, T, H, E, k, seed):
+    """strata_moe_router: fp32 logits within the error bound of fp32
+    accumulation of H exact bf16 products (|err| <= H * 2^-24 * sum_h
+    |x_h w_h|) of the fp64 projection; the selection bit-exact against the
+    oracle's top-k taken on the kernel's own logits (the decision in the
+    kernel's precision), weights within the routing tolerance."""
+    import torch
+
+    x, w = synth.make_router(T, H, E, seed)
+    xd = torch.from_numpy(x.view(np.int16)).cuda().view(torch.bfloat16)
+    wd = torch.from_numpy(w.view(np.int16)).cuda().view(torch.bfloat16)
+    logits, ids, wts = qe.router(xd, wd, k)
+    got = _np(logits)
+    ref = oracle.router_logits(x, w)
+    mag = np.abs(oracle.bf16_to_f64(x)) @ np.abs(oracle.bf16_to_f64(w)).T
+    bound = H * 2.0 ** -24 * mag + 1e-30
+    assert (np.abs(got.astype(np.float64) - ref) <= bound).all(), float(np.max(np.abs(got - ref) / bound))
+    rid, rw = oracle.route(got, k)
+    assert (_np(ids) == rid).all()
+    assert np.abs(_np(wts).astype(np.float64) - rw).max() <= W_ATOL
+    # The same selection as the routing call on those logits.
+    ids2, w2 = qe.route(logits, k)
+    assert torch.equal(ids, ids2) and torch.equal(wts, w2)

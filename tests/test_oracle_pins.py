@@ -40,6 +40,49 @@ def _bruteforce_softmax(vals):
     return [v / s for v in z]
 
 
+# ----------------------------------------------------------------------------- router projection
+def test_router_logits_match_bruteforce_loops():
+    """x . W_r^T against explicit per-element loops over exactly widened bf16
+    values, summed with math.fsum (exactly rounded)."""
+    x, w = synth.make_router(3, 16, 5, seed=7)
+    got = oracle.router_logits(x, w)
+
+    def widen(b):
+        return float(np.array([int(b) << 16], dtype=np.uint32).view(np.float32)[0])
+
+    for t in range(3):
+        for e in range(5):
+            ref = math.fsum(widen(x[t, h]) * widen(w[e, h]) for h in range(16))
+            assert abs(got[t, e] - ref) <= 1e-12 * max(1.0, abs(ref))
+
+
+def test_router_logits_one_hot_rows_select_x():
+    """A router row with a single 1.0 picks one hidden feature exactly."""
+    x, _ = synth.make_router(4, 32, 1, seed=8)
+    cols = [3, 0, 31, 17, 3]
+    w = np.zeros((len(cols), 32), dtype=np.uint16)
+    for e, c in enumerate(cols):
+        w[e, c] = 0x3F80  # bf16 1.0
+    got = oracle.router_logits(x, w)
+    xf = oracle.bf16_to_f64(x)
+    for e, c in enumerate(cols):
+        assert np.array_equal(got[:, e], xf[:, c])
+
+
+def test_router_logits_scale_exactly_with_router_rows():
+    """Doubling every router weight (bf16 exponent + 1, exact) doubles the
+    logits exactly, and negating a row negates its column."""
+    x, w = synth.make_router(5, 64, 6, seed=9)
+    base = oracle.router_logits(x, w)
+    w2 = w.copy()
+    nz = (w2 & 0x7F80) != 0
+    w2[nz] = w2[nz] + 0x0080  # exponent + 1 on normal values (no overflow at these magnitudes)
+    assert np.array_equal(oracle.router_logits(x, w2), 2 * base)
+    wn = w.copy()
+    wn[2] ^= 0x8000
+    assert np.array_equal(oracle.router_logits(x, wn)[:, 2], -base[:, 2])
+
+
 @pytest.mark.parametrize("grid", [None, 0.25, 1.0])
 @pytest.mark.parametrize("T,E,k", [(7, 16, 2), (5, 33, 10), (3, 8, 8), (4, 64, 1)])
 def test_route_matches_bruteforce(T, E, k, grid):
