@@ -361,14 +361,16 @@ def bench_secondary(qe, args):
     """The other configurations, each timed the same way as the headline one
     (whole layer, inputs resident, HIP events), against the roofline that
     bounds it: HBM for small-batch prefill, the matrix cores for the skewed
-    large-chunk prefill; the tiny case is launch-latency bound."""
+    large-chunk prefill and for the 6144-token chunk with 32- and 128-wide
+    scale groups; the tiny case is launch-latency bound."""
     import torch
 
     import synth
 
     out = {}
     dev = torch.device("cuda:0")
-    for name, bound, steps in (("tiny", None, 200), ("prefill512", "hbm", 50), ("zipf6144", "mfma", 10)):
+    for name, bound, steps in (("tiny", None, 200), ("prefill512", "hbm", 50), ("zipf6144", "mfma", 10),
+                               ("prefill6144_g32", "mfma", 50), ("prefill6144_g128", "mfma", 50)):
         cfg = synth.config(name)
         inp = synth.make_inputs(cfg)
         logits = torch.from_numpy(inp.logits).to(dev)

@@ -77,6 +77,9 @@ CONFIGS: dict[str, MoEConfig] = {
     "prefill6144": MoEConfig("prefill6144", T=6144, H=2048, I=512, E=512, k=10, g=64, seed=3),
     # skewed, larger-shape prefill: Zipf(1.1) expert popularity
     "zipf6144": MoEConfig("zipf6144", T=6144, H=4096, I=1024, E=256, k=8, g=128, seed=4, zipf_s=1.1),
+    # the 6144-token chunk with the other two group sizes the pages name
+    "prefill6144_g32": MoEConfig("prefill6144_g32", T=6144, H=2048, I=512, E=512, k=10, g=32, seed=5),
+    "prefill6144_g128": MoEConfig("prefill6144_g128", T=6144, H=2048, I=512, E=512, k=10, g=128, seed=6),
 }
 
 

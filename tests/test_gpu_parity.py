@@ -225,7 +225,8 @@ def _sample_tokens(T, n, seed):
     return np.array(sorted(pick))
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill512", "prefill6144", "zipf6144"])
+@pytest.mark.parametrize("name", ["decode", "prefill512", "prefill6144", "zipf6144", "prefill6144_g32",
+                                  "prefill6144_g128"])
 def test_ffn_full_size_sampled_tokens(qe, name):
     inp = inputs(name)
     cfg = inp.cfg
@@ -237,7 +238,7 @@ def test_ffn_full_size_sampled_tokens(qe, name):
     check_close(_np(res["out"])[toks], ref, f"{name} out[sampled tokens]")
 
 
-@pytest.mark.parametrize("name", ["prefill6144", "zipf6144"])
+@pytest.mark.parametrize("name", ["prefill6144", "zipf6144", "prefill6144_g32", "prefill6144_g128"])
 def test_ffn_full_size_sampled_grouped_rows(qe, name):
     """Deterministic path: grouped rows y[i] of the busiest expert (many tiles,
     ragged last tile) and of a median expert, against the oracle row by row."""
