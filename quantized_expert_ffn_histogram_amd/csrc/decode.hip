@@ -14,19 +14,23 @@
 //     the others: block (pair p = t*k + j, 16 h columns) re-selects the j-th
 //       expert of token t in one wavefront (same code, so the same expert),
 //       then streams that expert's gate and up rows for its columns and
-//       writes h[p] = silu(gate . x_t) * (up . x_t) in fp16, pair order.
+//       writes h[p] = silu(gate . x_t) * (up . x_t) in fp16, pair order,
+//       each 8 consecutive columns stored as the pairs (c, c+4) that the
+//       dot products consume (h lives only between the two kernels);
 //       The token's activations are loaded before the selection finishes.
 //   decode_down_combine (grid: 1 grouping block + T * H/rows blocks)
 //     grouping block: counts / offsets / perm / inv_perm from topk_ids with
 //       the single-workgroup grouping of the grouping step (same code);
 //     the others: block (token t, rows) stages h of the token's k pairs in
-//       LDS, streams row n of each of its k experts' down weights and writes
+//       LDS with the sum of each 32-value chunk (once per block instead of
+//       once per row), streams row n of each of its k experts' down weights and writes
 //       out[t][n] = sum_j w[t][j] * (W_down[e_j][n] . h[t*k+j]), summed in j
 //       order: deterministic, with no y round trip and no combine kernel.
 //
-// Dot products are those of the GEMV path (ffn_gemv.hip): fp16 pairs
-// (1024 + u) against fp16 activations with v_dot2_f32_f16 and the exact
-// offset correction per lane.
+// Dot products: fp16 pairs (1024 + u) against fp16 activations with
+// v_dot2_f32_f16 and the exact offset correction per lane, as in the GEMV
+// path (ffn_gemv.hip), except that the activations' odd pairs are held
+// divided by 16 so that half of the nibbles need no shift (dot32_split).
 #include "gemv_dev.h"
 #include "permute_dev.h"
 #include "route_dev.h"
@@ -50,6 +54,27 @@ struct DecodeArgs {
   uint16_t *h;     // fp16 [T*k][I], pair order
   float *out;      // fp32 [T][H]
 };
+
+// Sum over each group of W consecutive lanes (W a power of two), in every
+// lane of the group, with DPP moves inside 16-lane rows instead of LDS
+// permutes; the whole wavefront must be active.
+template <int W>
+__device__ __forceinline__ float dpp_group_sum(float v) {
+  if constexpr (W >= 2) v += dpp_f32<0xB1>(v);    // quad_perm [1,0,3,2]
+  if constexpr (W >= 4) v += dpp_f32<0x4E>(v);    // quad_perm [2,3,0,1]
+  if constexpr (W == 8) v += dpp_f32<0x141>(v);   // row_half_mirror: the other quad of the 8
+  if constexpr (W >= 16) {
+    v += dpp_f32<0x124>(v);                       // row_ror 4
+    v += dpp_f32<0x128>(v);                       // row_ror 8
+  }
+  if constexpr (W == 32) v += __shfl_xor(v, 16, kWave);
+  if constexpr (W == 64) {
+    const int b = __float_as_int(v);
+    v = (__int_as_float(__builtin_amdgcn_readlane(b, 0)) + __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+        (__int_as_float(__builtin_amdgcn_readlane(b, 32)) + __int_as_float(__builtin_amdgcn_readlane(b, 48)));
+  }
+  return v;
+}
 
 template <int EPL, int NCH>
 __global__ __launch_bounds__(256) void decode_route_gateup_kernel(DecodeArgs a) {
@@ -109,22 +134,32 @@ __global__ __launch_bounds__(256) void decode_route_gateup_kernel(DecodeArgs a) 
     half2_t xp[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) bf16x8_pairs(xv[c][q], &xp[4 * q]);
-    float xs = 0.0f;
+    // Odd pairs divided by 16 (dot32_split), once for the wavefront's 8 rows.
+    const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+    float se = 0.0f, so = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) xs += pair_sum(xp[i]);
+    for (int q = 0; q < 4; ++q) {
+      xp[4 * q + 1] *= sixteenth;
+      xp[4 * q + 3] *= sixteenth;
+      se += pair_sum(xp[4 * q]) + pair_sum(xp[4 * q + 2]);
+      so += pair_sum(xp[4 * q + 1]) + pair_sum(xp[4 * q + 3]);
+    }
+    const float corr = 1032.0f * se + 1152.0f * so;
 #pragma unroll
     for (int cc = 0; cc < kDecColsPerWave; ++cc) {
-      gs[cc] += dot32(wg[cc][c], xp, xs, on * half_bits_to_float((uint16_t)sgb[cc][c]));
-      us[cc] += dot32(wu[cc][c], xp, xs, on * half_bits_to_float((uint16_t)sub_[cc][c]));
+      gs[cc] += dot32_split<false>(wg[cc][c], xp, corr, on * half_bits_to_float((uint16_t)sgb[cc][c]));
+      us[cc] += dot32_split<false>(wu[cc][c], xp, corr, on * half_bits_to_float((uint16_t)sub_[cc][c]));
     }
   }
 #pragma unroll
   for (int cc = 0; cc < kDecColsPerWave; ++cc) {
-    const float gv = group_sum<kWave>(gs[cc]);
-    const float uv = group_sum<kWave>(us[cc]);
+    const float gv = dpp_group_sum<kWave>(gs[cc]);
+    const float uv = dpp_group_sum<kWave>(us[cc]);
     if (lane == 0) {
       const float hv = gv / (1.0f + __expf(-gv)) * uv;
-      reinterpret_cast<_Float16 *>(a.h)[(size_t)p * a.I + n0 + cc] = (_Float16)hv;
+      // Pair order (c, c+4); the odd pairs (c % 4 = 1, 3) divided by 16 for dot32_split.
+      const int c = n0 + cc, slot = (c & ~7) | (2 * (c & 3) + ((c >> 2) & 1));
+      reinterpret_cast<_Float16 *>(a.h)[(size_t)p * a.I + slot] = (_Float16)((c & 1) ? hv * 0.0625f : hv);
     }
   }
 }
@@ -180,23 +215,43 @@ __global__ __launch_bounds__(256) void decode_down_combine_kernel(DecodeArgs a) 
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wavefront's h loads have landed
   __syncthreads();                                 // ... and everyone's
+  // Sum of each 32-value chunk of h (the offset correction of the dot
+  // products), once per chunk: thread tid sums chunks tid, tid + 256, ...
+  __shared__ float hsums[kDecodeMaxKI / 32];
+  for (int c = tid; c < a.k * a.I / 32; c += 256) {
+    const uint4 *hc = hs + 4 * c;
+    float se = 0.0f, so = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint4 u = hc[q];
+      se += pair_sum(__builtin_bit_cast(half2_t, u.x)) + pair_sum(__builtin_bit_cast(half2_t, u.z));
+      so += pair_sum(__builtin_bit_cast(half2_t, u.y)) + pair_sum(__builtin_bit_cast(half2_t, u.w));
+    }
+    hsums[c] = 1032.0f * se + 1152.0f * so;  // the offset term of dot32_split
+  }
+  __syncthreads();
 
   float acc = 0.0f;
 #pragma unroll
   for (int jj = 0; jj < KMAX; ++jj) {
     if (jj < a.k) {
+      // h is stored in pair order: each 32-bit word is one fp16 pair.
       const uint4 *hrow = hs + (jj * a.I + 32 * sub) / 8;
       half2_t hp[16];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) f16x8_pairs(hrow[q], &hp[4 * q]);
-      float hsum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) hsum += pair_sum(hp[i]);
+      for (int q = 0; q < 4; ++q) {
+        const uint4 u = hrow[q];
+        hp[4 * q] = __builtin_bit_cast(half2_t, u.x);
+        hp[4 * q + 1] = __builtin_bit_cast(half2_t, u.y);
+        hp[4 * q + 2] = __builtin_bit_cast(half2_t, u.z);
+        hp[4 * q + 3] = __builtin_bit_cast(half2_t, u.w);
+      }
+      const float corr = hsums[(jj * a.I) / 32 + sub];
       const float wsel = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), jj));
-      acc += wsel * dot32(wq[jj], hp, hsum, half_bits_to_float((uint16_t)sdb[jj]));
+      acc += wsel * dot32_split<true>(wq[jj], hp, corr, half_bits_to_float((uint16_t)sdb[jj]));
     }
   }
-  const float y = group_sum<LPR>(acc);
+  const float y = dpp_group_sum<LPR>(acc);
   if (sub == 0 && n < a.H) a.out[(size_t)t * a.H + n] = y;
 }
 

@@ -9,6 +9,17 @@ namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 
+// (a & m) | o as one v_and_or_b32, m in an SGPR and o in a VGPR (one
+// scalar operand per VOP3 here); left to itself the compiler emits a
+// separate and and or with literal operands.  The asm is volatile: as a
+// plain asm the compiler hoists these ahead of their uses and holds the
+// results in registers.
+__device__ __forceinline__ uint32_t and_or_sv(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm volatile("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(o));
+  return r;
+}
+
 __device__ __forceinline__ half2_t magic_pair(uint32_t d, int m) {
   return __builtin_bit_cast(half2_t, ((d >> (4 * m)) & 0x000F000Fu) | 0x64006400u);
 }
@@ -48,6 +59,33 @@ __device__ __forceinline__ float dot32(const uint4 wq, const half2_t *xp, float 
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc = __builtin_amdgcn_fdot2(xp[4 * q + m], magic_pair(d[q], m), acc, false);
   return s * (acc - 1032.0f * xsum);
+}
+
+// dot32 for activations whose odd pairs (m = 1, 3: slots 4q+1, 4q+3) are
+// held divided by 16.  The nibbles of those pairs are then used in place as
+// 1024 + 16u (one and-or, no shift): (x/16)(1024 + 16u) = 64x + xu, so the
+// offset term is corr = 1032 * (sum of the even-pair x) + 1152 * (sum of the
+// stored odd-pair x/16) and the result is s * (acc - corr).  Exact in the
+// same way as dot32 while x/16 is an fp16 normal.
+// kFused: each nibble pair as one v_and_or_b32 (and_or_sv); otherwise
+// plain and + or, which leaves the compiler more freedom to schedule (the
+// gate/up kernel keeps its register count that way).
+template <bool kFused>
+__device__ __forceinline__ float dot32_split(const uint4 wq, const half2_t *xp, float corr, float s) {
+  auto pair = [](uint32_t d, uint32_t m) {
+    return __builtin_bit_cast(half2_t, kFused ? and_or_sv(d, m, 0x64006400u) : ((d & m) | 0x64006400u));
+  };
+  float acc = 0.0f;
+  const uint32_t d[4] = {wq.x, wq.y, wq.z, wq.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t d8 = d[q] >> 8;
+    acc = __builtin_amdgcn_fdot2(xp[4 * q], pair(d[q], 0x000F000Fu), acc, false);
+    acc = __builtin_amdgcn_fdot2(xp[4 * q + 1], pair(d[q], 0x00F000F0u), acc, false);
+    acc = __builtin_amdgcn_fdot2(xp[4 * q + 2], pair(d8, 0x000F000Fu), acc, false);
+    acc = __builtin_amdgcn_fdot2(xp[4 * q + 3], pair(d8, 0x00F000F0u), acc, false);
+  }
+  return s * (acc - corr);
 }
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
