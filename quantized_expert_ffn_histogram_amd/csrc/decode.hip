@@ -55,27 +55,6 @@ struct DecodeArgs {
   float *out;      // fp32 [T][H]
 };
 
-// Sum over each group of W consecutive lanes (W a power of two), in every
-// lane of the group, with DPP moves inside 16-lane rows instead of LDS
-// permutes; the whole wavefront must be active.
-template <int W>
-__device__ __forceinline__ float dpp_group_sum(float v) {
-  if constexpr (W >= 2) v += dpp_f32<0xB1>(v);    // quad_perm [1,0,3,2]
-  if constexpr (W >= 4) v += dpp_f32<0x4E>(v);    // quad_perm [2,3,0,1]
-  if constexpr (W == 8) v += dpp_f32<0x141>(v);   // row_half_mirror: the other quad of the 8
-  if constexpr (W >= 16) {
-    v += dpp_f32<0x124>(v);                       // row_ror 4
-    v += dpp_f32<0x128>(v);                       // row_ror 8
-  }
-  if constexpr (W == 32) v += __shfl_xor(v, 16, kWave);
-  if constexpr (W == 64) {
-    const int b = __float_as_int(v);
-    v = (__int_as_float(__builtin_amdgcn_readlane(b, 0)) + __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
-        (__int_as_float(__builtin_amdgcn_readlane(b, 32)) + __int_as_float(__builtin_amdgcn_readlane(b, 48)));
-  }
-  return v;
-}
-
 template <int EPL, int NCH>
 __global__ __launch_bounds__(256) void decode_route_gateup_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;

@@ -19,11 +19,13 @@
 // so each lane has 8 (gate/up) or 8 (down) 16-byte loads in flight.
 //
 // Dot products: a dword of 8 nibbles gives four fp16 pairs (1024 + u_m,
-// 1024 + u_{m+4}) with one shift and one and-or; v_dot2_f32_f16 accumulates
-// x * (1024 + u) in fp32, and per lane (32 K values, inside one group since
-// g >= 32) the exact identity  sum x*q*s = s * (sum x*(1024+u) - 1032 * sum x)
-// removes the offset.  Activations are converted to fp16 pairs in the same
-// slot order.
+// 1024 + u_{m+4}) with one and-or each (and one shift per dword: the pairs
+// from bits 4..7 of each byte are used in place as 1024 + 16u against
+// activations divided by 16, dot32_split); v_dot2_f32_f16 accumulates in
+// fp32, and per lane (32 K values, inside one group since g >= 32) the exact
+// identity  sum x*q*s = s * (acc - offset term)  removes the offset.
+// Activations are converted to fp16 pairs in the same slot order; h between
+// the two kernels is stored in that order already.
 //
 //   gemv_gateup: workgroup = (entry, 16 h columns); wavefront = 4 columns,
 //                gate and up rows; lane 0 writes h = silu(g)*u (fp16).
@@ -170,22 +172,33 @@ __global__ __launch_bounds__(256, NCH == 1 ? 4 : 2) void gemv_gateup_kernel(Gemv
       half2_t xp[16];
 #pragma unroll
       for (int q = 0; q < 4; ++q) bf16x8_pairs(xv[c][q], &xp[4 * q]);
-      float xs = 0.0f;
+      // Odd pairs divided by 16 (dot32_split), once for the wavefront's 8 rows.
+      const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+      float se = 0.0f, so = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) xs += pair_sum(xp[i]);
+      for (int q = 0; q < 4; ++q) {
+        xp[4 * q + 1] *= sixteenth;
+        xp[4 * q + 3] *= sixteenth;
+        se += pair_sum(xp[4 * q]) + pair_sum(xp[4 * q + 2]);
+        so += pair_sum(xp[4 * q + 1]) + pair_sum(xp[4 * q + 3]);
+      }
+      const float corr = 1032.0f * se + 1152.0f * so;
 #pragma unroll
       for (int cc = 0; cc < kColsPerWave; ++cc) {
-        gs[cc] += dot32(wg[cc][c], xp, xs, on * half_bits_to_float((uint16_t)sgb[cc][c]));
-        us[cc] += dot32(wu[cc][c], xp, xs, on * half_bits_to_float((uint16_t)sub_[cc][c]));
+        gs[cc] += dot32_split<false>(wg[cc][c], xp, corr, on * half_bits_to_float((uint16_t)sgb[cc][c]));
+        us[cc] += dot32_split<false>(wu[cc][c], xp, corr, on * half_bits_to_float((uint16_t)sub_[cc][c]));
       }
     }
 #pragma unroll
     for (int cc = 0; cc < kColsPerWave; ++cc) {
-      const float gv = group_sum<kWave>(gs[cc]);
-      const float uv = group_sum<kWave>(us[cc]);
+      const float gv = dpp_group_sum<kWave>(gs[cc]);
+      const float uv = dpp_group_sum<kWave>(us[cc]);
       if (lane == 0) {
         const float hv = gv / (1.0f + __expf(-gv)) * uv;
-        reinterpret_cast<_Float16 *>(a.h)[(size_t)(en.row0 + r) * a.I + n0 + cc] = (_Float16)hv;
+        // Pair order (c, c+4) inside each 8 columns, odd pairs divided by 16 (dot32_split).
+        const int col = n0 + cc, slot = (col & ~7) | (2 * (col & 3) + ((col >> 2) & 1));
+        reinterpret_cast<_Float16 *>(a.h)[(size_t)(en.row0 + r) * a.I + slot] =
+            (_Float16)((col & 1) ? hv * 0.0625f : hv);
       }
     }
   };
@@ -240,15 +253,24 @@ __global__ __launch_bounds__(256, 4) void gemv_down_kernel(GemvArgs a) {
       opaque(wq[it]);
       asm volatile("" : "+v"(sdb[it]));
     }
+    // h is stored in pair order with the odd pairs divided by 16: each
+    // 32-bit word is one pair for dot32_split.
     half2_t hp[16];
+    float se = 0.0f, so = 0.0f;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) f16x8_pairs(hv[q], &hp[4 * q]);
-    float hs = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) hs += pair_sum(hp[i]);
+    for (int q = 0; q < 4; ++q) {
+      hp[4 * q] = __builtin_bit_cast(half2_t, hv[q].x);
+      hp[4 * q + 1] = __builtin_bit_cast(half2_t, hv[q].y);
+      hp[4 * q + 2] = __builtin_bit_cast(half2_t, hv[q].z);
+      hp[4 * q + 3] = __builtin_bit_cast(half2_t, hv[q].w);
+      se += pair_sum(hp[4 * q]) + pair_sum(hp[4 * q + 2]);
+      so += pair_sum(hp[4 * q + 1]) + pair_sum(hp[4 * q + 3]);
+    }
+    const float corr = 1032.0f * se + 1152.0f * so;
 #pragma unroll
     for (int it = 0; it < kDownIter; ++it) {
-      const float yv = group_sum<LPR>(dot32(wq[it], hp, hs, half_bits_to_float((uint16_t)sdb[it])));
+      const float yv =
+          dpp_group_sum<LPR>(dot32_split<true>(wq[it], hp, corr, half_bits_to_float((uint16_t)sdb[it])));
       const int n = nbase + it * RPI;
       if (sub == 0 && n < a.H) {
         if (a.fused)

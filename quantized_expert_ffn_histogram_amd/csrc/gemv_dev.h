@@ -20,10 +20,6 @@ __device__ __forceinline__ uint32_t and_or_sv(uint32_t a, uint32_t m, uint32_t o
   return r;
 }
 
-__device__ __forceinline__ half2_t magic_pair(uint32_t d, int m) {
-  return __builtin_bit_cast(half2_t, ((d >> (4 * m)) & 0x000F000Fu) | 0x64006400u);
-}
-
 // 8 consecutive K values as fp16 pairs in slot order (k+m, k+m+4), m = 0..3.
 __device__ __forceinline__ void bf16x8_pairs(uint4 v, half2_t *o) {
   auto lo = [](uint32_t d) { return __uint_as_float(d << 16); };
@@ -34,39 +30,16 @@ __device__ __forceinline__ void bf16x8_pairs(uint4 v, half2_t *o) {
   o[3] = __builtin_bit_cast(half2_t, __builtin_amdgcn_cvt_pkrtz(hi(v.y), hi(v.w)));
 }
 
-__device__ __forceinline__ void f16x8_pairs(uint4 v, half2_t *o) {
-  o[0] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(v.z, v.x, 0x05040100u));
-  o[1] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(v.z, v.x, 0x07060302u));
-  o[2] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(v.w, v.y, 0x05040100u));
-  o[3] = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(v.w, v.y, 0x07060302u));
-}
-
 __device__ __forceinline__ float pair_sum(half2_t p) { return (float)p.x + (float)p.y; }
 
-template <int W>
-__device__ __forceinline__ float group_sum(float v) {
-#pragma unroll
-  for (int off = W / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
-
-// sum over this lane's 32 K values of x * q * s, from 16 bytes of packed row.
-__device__ __forceinline__ float dot32(const uint4 wq, const half2_t *xp, float xsum, float s) {
-  float acc = 0.0f;
-  const uint32_t d[4] = {wq.x, wq.y, wq.z, wq.w};
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int m = 0; m < 4; ++m) acc = __builtin_amdgcn_fdot2(xp[4 * q + m], magic_pair(d[q], m), acc, false);
-  return s * (acc - 1032.0f * xsum);
-}
-
-// dot32 for activations whose odd pairs (m = 1, 3: slots 4q+1, 4q+3) are
+// Sum over this lane's 32 K values of x * q * s, from 16 bytes of packed row
+// (8 nibbles per dword), for activations whose odd pairs (m = 1, 3: slots 4q+1, 4q+3) are
 // held divided by 16.  The nibbles of those pairs are then used in place as
 // 1024 + 16u (one and-or, no shift): (x/16)(1024 + 16u) = 64x + xu, so the
 // offset term is corr = 1032 * (sum of the even-pair x) + 1152 * (sum of the
-// stored odd-pair x/16) and the result is s * (acc - corr).  Exact in the
-// same way as dot32 while x/16 is an fp16 normal.
+// stored odd-pair x/16) and the result is s * (acc - corr).  Per lane (32 K
+// values, inside one scale group) the offset cancels exactly while x/16 is an
+// fp16 normal.
 // kFused: each nibble pair as one v_and_or_b32 (and_or_sv); otherwise
 // plain and + or, which leaves the compiler more freedom to schedule (the
 // gate/up kernel keeps its register count that way).
@@ -86,6 +59,27 @@ __device__ __forceinline__ float dot32_split(const uint4 wq, const half2_t *xp, 
     acc = __builtin_amdgcn_fdot2(xp[4 * q + 3], pair(d8, 0x00F000F0u), acc, false);
   }
   return s * (acc - corr);
+}
+
+// Sum over each group of W consecutive lanes (W a power of two), in every
+// lane of the group, with DPP moves inside 16-lane rows instead of LDS
+// permutes; the whole wavefront must be active.
+template <int W>
+__device__ __forceinline__ float dpp_group_sum(float v) {
+  if constexpr (W >= 2) v += dpp_f32<0xB1>(v);    // quad_perm [1,0,3,2]
+  if constexpr (W >= 4) v += dpp_f32<0x4E>(v);    // quad_perm [2,3,0,1]
+  if constexpr (W == 8) v += dpp_f32<0x141>(v);   // row_half_mirror: the other quad of the 8
+  if constexpr (W >= 16) {
+    v += dpp_f32<0x124>(v);                       // row_ror 4
+    v += dpp_f32<0x128>(v);                       // row_ror 8
+  }
+  if constexpr (W == 32) v += __shfl_xor(v, 16, kWave);
+  if constexpr (W == 64) {
+    const int b = __float_as_int(v);
+    v = (__int_as_float(__builtin_amdgcn_readlane(b, 0)) + __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+        (__int_as_float(__builtin_amdgcn_readlane(b, 32)) + __int_as_float(__builtin_amdgcn_readlane(b, 48)));
+  }
+  return v;
 }
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
