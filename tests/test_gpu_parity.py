@@ -397,6 +397,7 @@ ROUTER_CFGS = [
     (100, 128, 37, 5, 62),      # tokens and experts off the 128 tile, E % 4 != 0
     (1, 64, 1, 1, 63),          # one token, one expert, one K stage
     (70, 448, 130, 4, 65),      # seven K stages: one ring turn of four, then three more
+    (130, 16384, 70, 3, 66),    # the largest H: 256 K stages
     (257, 320, 1024, 32, 64),   # largest E and k, odd number of K stages
 ]
 
