@@ -542,8 +542,12 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
   // g is 32, 64 or 128: group and window indexes are shifts.
   const int lg = 31 - __builtin_clz(a.g);  // log2(g)
   const int lpw = lg - 4;                  // log2(stages per 8-group scale window)
-  const int ngr = a.K >> lg;               // groups per weight row (a multiple of 8)
-  const int nwin = ngr >> 3;               // scale windows per slice
+  const int ngr = a.K >> lg;               // groups per weight row (a multiple of 8, or 1, 2, 4)
+  // Scale windows per slice.  Rows of fewer than 8 groups have one window
+  // per slice whose 16-byte load also covers the next row's first scales
+  // (unused); for the block's last row that part lies past the buffer
+  // resource's range and reads as zero.
+  const int nwin = ngr >= 8 ? ngr >> 3 : 1;
 
   uint32_t aoff[NMB];
 #pragma unroll
@@ -899,11 +903,12 @@ int persistent_grid(long long work_upper, int wg_per_cu) {
 #endif
 
 // The wide pipeline when the scale windows align with the rows (K/g a
-// multiple of 8), the general one otherwise.
+// multiple of 8, or a whole row of fewer than 8 groups in one window), the
+// general one otherwise.
 template <int MODE>
 hipError_t launch_gemm(GemmArgs args, long long tiles_upper, int matrix_rows, hipStream_t s) {
   // The wide pipeline addresses A through a buffer resource: 32-bit offsets.
-  const bool wide = STRATA_GEMM_WIDE && args.K % kKS == 0 && (args.K / args.g) % 8 == 0 &&
+  const bool wide = STRATA_GEMM_WIDE && args.K % kKS == 0 && ((args.K / args.g) % 8 == 0 || args.K / args.g < 8) &&
                     (long long)args.a_rows * args.K * 2 < (1LL << 32);
   if (wide) {
     const int width = MODE == 0 ? Shape<kWideW>::kHCols : Shape<kWideW>::kOutCols;
