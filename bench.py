@@ -163,20 +163,26 @@ def time_region(fn, steps: int):
     return a.elapsed_time(b) / 1e3  # seconds
 
 
-def step_percentiles(fn, steps: int) -> dict:
-    """Per-step device time (HIP events around each step): p10 / p50 / p90 in us."""
+def step_percentiles(fn, steps: int, total: bool = False) -> dict:
+    """Per-step device time (HIP events around each step): p10 / p50 / p90 in
+    us; with total, also the number of steps and the region's wall time."""
     import torch
 
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
     for i, (a, b) in enumerate(ev):
         a.record()
         fn(i)
         b.record()
     torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     t = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
-    return {"p10_us": round(float(np.percentile(t, 10)), 2), "p50_us": round(float(np.percentile(t, 50)), 2),
-            "p90_us": round(float(np.percentile(t, 90)), 2)}
+    out = {"p10_us": round(float(np.percentile(t, 10)), 2), "p50_us": round(float(np.percentile(t, 50)), 2),
+           "p90_us": round(float(np.percentile(t, 90)), 2)}
+    if total:
+        out.update(steps=steps, seconds=round(wall, 3), mean_us=round(float(t.mean()), 2))
+    return out
 
 
 def kernel_table(qe):
@@ -232,15 +238,28 @@ def bench_prefill(qe, args):
     run = qe.LayerRunner(experts, cfg.T, cfg.E, cfg.k, fused=bool(args.fused), device=dev, single_call=True)
     run4 = qe.LayerRunner(experts, cfg.T, cfg.E, cfg.k, fused=bool(args.fused), device=dev)
 
+    # The four separate calls are timed first (context); then W warmup steps
+    # and exactly args.steps layer calls in one region bracketed by
+    # synchronizations: the headline.  After it, a steady-state region of at
+    # least 200 steps and --steady-secs seconds with events around every
+    # step: median and p10/p90 under sustained load, as the clock settles.
+    for _ in range(args.warmup):
+        run4(logits, x)
+    secs4 = time_region(lambda i: run4(logits, x), args.steps)
     for _ in range(args.warmup):
         run(logits, x)
-        run4(logits, x)
-    # The four separate calls are timed first (context), then exactly
-    # args.steps layer calls in one region bracketed by synchronizations.
-    secs4 = time_region(lambda i: run4(logits, x), args.steps)
     secs = time_region(lambda i: run(logits, x), args.steps)
     log(f"[bench] {cfg.name}: {args.steps} steps in {secs * 1e3:.2f} ms "
         f"(four separate calls: {secs4 * 1e3:.2f} ms)")
+    # The output of the timed steps, kept for the parity gate.
+    timed = {k_: getattr(run, k_).detach().cpu().numpy() for k_ in ("ids", "counts", "offsets", "perm", "inv", "out")}
+    timed["w"] = run.w.detach().cpu().numpy()
+    steady = None
+    if args.steady_secs > 0:
+        n_ss = max(200, int(np.ceil(args.steady_secs / (secs / args.steps))))
+        steady = step_percentiles(lambda i: run(logits, x), n_ss, total=True)
+        steady["tokens_per_s_p50"] = round(cfg.T / (steady["p50_us"] * 1e-6), 1)
+        log(f"[bench] {cfg.name}: steady state over {n_ss} steps: {steady}")
 
     qe.timing_enable(True)
     secs_timed = time_region(lambda i: run(logits, x), args.steps)
@@ -253,7 +272,7 @@ def bench_prefill(qe, args):
     dominant = max(table, key=lambda n: table[n]["total_ms"])
     roof = roofline_of(dominant, table[dominant]["avg_us"], cfg, cfg.T * cfg.k, distinct, cfg.name)
     kernels = {n: round(v["avg_us"], 2) for n, v in table.items()}
-    return cfg, inp, secs, secs_timed, roof, kernels, secs4
+    return cfg, inp, secs, secs_timed, roof, kernels, secs4, steady, timed
 
 
 def bench_decode(qe, args):
@@ -446,29 +465,72 @@ def bench_router(qe, args):
                 "hbm_frac": round((T * H * 2 + E * H * 2 + T * E * 4) / (proj_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}}
 
 
-def cpu_baseline(cfg, inp):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, inp, repeats: int = 3):
     """The fp64 oracle on this host over the whole prefill layer (route, grouping,
-    per-expert dequant + SwiGLU, combine), timed once."""
+    per-expert dequant + SwiGLU, combine): median wall time of `repeats` runs.
+    Returns the record and the oracle's output (for the parity gate)."""
     import oracle
 
     try:
         import threadpoolctl
 
-        threads = max(p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()) or 1
+        info = threadpoolctl.threadpool_info()
+        threads = max(p.get("num_threads", 1) for p in info) or 1
+        blas = ", ".join(sorted({f"{p.get('internal_api')} {p.get('num_threads')} threads" for p in info}))
     except Exception:  # pragma: no cover
-        threads = 1
-    t0 = time.perf_counter()
-    oracle.moe_layer(inp.logits, inp.x_bf16, inp.weights, cfg.k, cfg.g)
-    secs = time.perf_counter() - t0
-    return {
+        threads, blas = 1, "unknown"
+    times, ref = [], None
+    for _ in range(repeats):
+        t0 = time.perf_counter()
+        ref = oracle.moe_layer(inp.logits, inp.x_bf16, inp.weights, cfg.k, cfg.g)
+        times.append(time.perf_counter() - t0)
+    secs = float(np.median(times))
+    rec = {
         "value": round(cfg.T / secs, 2),
         "unit": "tokens/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"the whole {cfg.name} layer ({cfg.T} tokens) once, fp64 NumPy with BLAS threads",
+        "sample": f"the whole {cfg.name} layer ({cfg.T} tokens), median of {repeats} runs, fp64 NumPy with "
+                  "BLAS threads",
         "seconds": round(secs, 2),
+        "runs_s": [round(t, 2) for t in times],
         "affinity_cores": len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model(),
+        "blas": blas,
     }
+    return rec, ref
+
+
+def parity_gate(timed: dict, ref: dict) -> dict:
+    """Compare the output of the timed steps with the oracle: routing ids and
+    grouping bit-exact, routing weights within 1e-6, out within max |err| <=
+    2e-2 RMS(out) and sum |err| / sum |ref| <= 5e-3 over every element."""
+    res = {}
+    for key, rkey in (("ids", "ids"), ("counts", "counts"), ("offsets", "offsets"), ("perm", "perm"),
+                      ("inv", "inv_perm")):
+        res[f"{rkey}_bitexact"] = bool(np.array_equal(timed[key].reshape(-1), ref[rkey].reshape(-1)))
+    res["w_max_abs_err"] = float(np.abs(timed["w"].astype(np.float64) - ref["w"]).max())
+    out = timed["out"].astype(np.float64)
+    err = np.abs(out - ref["out"])
+    rms = float(np.sqrt(np.mean(ref["out"] ** 2)))
+    res["max_err_over_rms"] = float(err.max() / rms)
+    res["l1_rel"] = float(err.sum() / np.abs(ref["out"]).sum())
+    res["elements"] = int(out.size)
+    ok = (all(v for k_, v in res.items() if k_.endswith("_bitexact")) and res["w_max_abs_err"] <= 1e-6
+          and res["max_err_over_rms"] <= 2e-2 and res["l1_rel"] <= 5e-3 and bool(np.all(np.isfinite(out))))
+    res["status"] = "ok" if ok else "FAIL"
+    return res
 
 
 def main(argv=None) -> int:
@@ -481,6 +543,10 @@ def main(argv=None) -> int:
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-secondary", action="store_true", help="skip the tiny / prefill512 / zipf6144 lines")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true",
+                    help="with --no-cpu-baseline: skip the oracle comparison of the headline output (profiling)")
+    ap.add_argument("--steady-secs", type=float, default=3.0,
+                    help="length of the steady-state prefill region with per-step percentiles (0: skip)")
     ap.add_argument("--fused", type=int, default=1, help="1: fused weighted scatter-add; 0: y rows + combine")
     ap.add_argument("--router-only", action="store_true",
                     help="time only the router projection + top-k call (router6144) and print its record")
@@ -523,7 +589,8 @@ def main(argv=None) -> int:
         log("[bench] calibration: 3 copies of 1 GiB (read 1 GiB + write 1 GiB each)")
         del src, dst
 
-    cfg, inp, secs, secs_timed, roof, kernels, secs4 = bench_prefill(qe, args)
+    cfg, inp, secs, secs_timed, roof, kernels, secs4, steady, timed = bench_prefill(qe, args)
+    flops, _ = layer_work(cfg, int((timed["counts"] > 0).sum()))
     result = {
         "metric": METRIC,
         "value": round(cfg.T * args.steps / secs, 1),
@@ -545,6 +612,8 @@ def main(argv=None) -> int:
             "parallelism": "single GPU",
         },
         "roofline": roof,
+        "layer_mfma_frac": round(flops / (secs / args.steps) / 1e12 / PEAK_MFMA_TFLOPS, 4),
+        "prefill_steady_state": steady,
         "kernels_us": kernels,
         "ms_per_step_with_kernel_events": round(secs_timed / args.steps * 1e3, 4),
         "ms_per_step_four_calls": round(secs4 / args.steps * 1e3, 4),
@@ -553,8 +622,24 @@ def main(argv=None) -> int:
         result["decode"] = bench_decode(qe, args)
     if not args.no_secondary:
         result["secondary"] = bench_secondary(qe, args)
+    ref = None
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, inp)
+        result["cpu_baseline"], ref = cpu_baseline(cfg, inp)
+    elif not args.no_parity:
+        import oracle
+
+        ref = oracle.moe_layer(inp.logits, inp.x_bf16, inp.weights, cfg.k, cfg.g)
+    # Parity gate: the headline stands only if the output of the timed steps
+    # matches the oracle.
+    if ref is not None:
+        result["parity"] = parity_gate(timed, ref)
+        if result["parity"]["status"] != "ok":
+            result["value"] = None
+            print(json.dumps(result), flush=True)
+            log(f"[bench] PARITY FAILURE: {result['parity']}")
+            return 1
+    else:
+        result["parity"] = {"status": "not checked (--no-cpu-baseline --no-parity)"}
     print(json.dumps(result), flush=True)
     return 0
 

@@ -127,7 +127,8 @@ int strata_moe_router(const uint16_t *x_bf16, int32_t T, int32_t H, const uint16
  *                              routed to expert e.
  *   inv_perm  out int32 [T*k]  inv_perm[perm[i]] = i.
  *   workspace     device scratch of at least
- *                 strata_moe_workspace_size(T, E, k, ...) bytes.
+ *                 strata_moe_permute_workspace_size(T, E, k) bytes (NULL
+ *                 when that is 0).
  * All outputs are bit-exact and deterministic (no dependence on the order of
  * atomic operations).  Expert ids outside [0, E) are a precondition violation.
  */
@@ -143,9 +144,9 @@ int strata_moe_permute(const int32_t *topk_ids, int32_t T, int32_t E, int32_t k,
  * review §1.2; activation fused with the FFN projection: yfxerp.com static
  * review §5.1.)
  *
- *   x_bf16    in  bfloat16 bits [T][H] token activations.  Values must lie in
- *                 the fp16 finite range (|x| <= 65504); the expert matmuls
- *                 run with fp16 operands and fp32 accumulation.
+ *   x_bf16    in  bfloat16 bits [T][H] token activations.  The expert
+ *                 matmuls run with fp16 operands and fp32 accumulation; see
+ *                 "fp16 operand envelope" below.
  *   w         in  host pointer to the weight descriptor (device arrays).
  *   offsets   in  int32 [E+1] and perm int32 [T*k], as from strata_moe_permute.
  *   topk_w    in  float32 [T*k] routing weights, or NULL.
@@ -174,7 +175,35 @@ int strata_moe_ffn(const uint16_t *x_bf16, int32_t T, int32_t k,
                    void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * strata_moe_combine - weighted sum of each token's expert outputs.
+ * fp16 operand envelope (strata_moe_ffn and strata_moe_layer).  The matrix
+ * and dot-product units take fp16 operands (the same matrix-core rate as
+ * bf16, with 3 more mantissa bits); accumulation is fp32.  Three values pass
+ * through fp16:
+ *   x   each bf16 activation is converted with round-toward-zero: exact for
+ *       2^-14 <= |x| <= 65504; |x| < 2^-14 becomes an fp16 subnormal
+ *       (absolute error < 2^-24); |x| > 65504 saturates to +-65504.
+ *   h   silu(gate . x) * (up . x) per pair and intermediate column, rounded
+ *       to nearest fp16: |h| must stay <= 65504 (beyond it h becomes +-inf
+ *       and the output is unspecified); |h| < 2^-14 is kept as a subnormal
+ *       (absolute error <= 2^-25; on the decode paths every other pair of
+ *       columns is held divided by 16, so there the subnormal range starts
+ *       at |h| < 2^-10).
+ *   y   each pair's expert output W_down . h, in fused mode on the grouped-
+ *       GEMM and GEMV paths, rounded to nearest fp16 before the weighted
+ *       sum: |y| must stay <= 65504.  The unfused mode writes y in fp32, and
+ *       the two-kernel decode layer never rounds y.
+ * Inside this envelope the output meets max |err| <= 2e-2 * RMS(out) and
+ * sum |err| / sum |out| <= 5e-3 against an exact evaluation; activations far
+ * below 2^-14 throughout a token lose relative accuracy to the subnormals.
+ */
+
+/*
+ * strata_moe_combine - weighted sum of each token's expert outputs, the last
+ * step of the routed layer: the selected experts' outputs are added up with
+ * the softmax routing weights of strata_moe_route (the layer as the
+ * kongchang.com hands-on describes it, section "Strata快在哪：不是魔法，是
+ * 物流", MoE note: each token's few active experts together form the layer's
+ * output; the weighting is the softmax over the selected logits).
  *
  *   y         in  float32 [T*k][H] grouped-order expert outputs.
  *   inv_perm  in  int32 [T*k]; topk_w in float32 [T*k].
@@ -226,6 +255,13 @@ int strata_moe_layer(const float *logits, const uint16_t *x_bf16, int32_t T, int
  */
 size_t strata_moe_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H,
                                  int32_t I, int32_t g);
+
+/*
+ * Bytes of device workspace that strata_moe_permute alone needs for T tokens,
+ * E experts and top-k (0 when no workspace is needed, e.g. at most 1024
+ * pairs; (size_t)-1 for invalid sizes).  strata_moe_workspace_size covers it.
+ */
+size_t strata_moe_permute_workspace_size(int32_t T, int32_t E, int32_t k);
 
 /* Message describing the last failed call on this thread ("" if none). */
 const char *strata_moe_last_error(void);

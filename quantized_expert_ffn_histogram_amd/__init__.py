@@ -30,6 +30,7 @@ __all__ = [
     "layer",
     "LayerRunner",
     "workspace_size",
+    "permute_workspace_size",
     "router",
     "timing_enable",
     "timing_query",
@@ -111,6 +112,10 @@ def workspace_size(T: int, E: int, k: int, H: int, I: int, g: int) -> int:
     return int(load().strata_moe_workspace_size(T, E, k, H, I, g))
 
 
+def permute_workspace_size(T: int, E: int, k: int) -> int:
+    return int(load().strata_moe_permute_workspace_size(T, E, k))
+
+
 def _workspace(device, nbytes: int, workspace: torch.Tensor | None) -> torch.Tensor:
     if workspace is not None:
         return workspace
@@ -153,7 +158,10 @@ def permute(topk_ids: torch.Tensor, E: int, workspace: torch.Tensor | None = Non
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     perm = torch.empty(T * k, dtype=torch.int32, device=dev)
     inv = torch.empty(T * k, dtype=torch.int32, device=dev)
-    ws = _workspace(dev, load().strata_moe_workspace_size(T, E, k, 256, 128, 32), workspace)
+    need = load().strata_moe_permute_workspace_size(T, E, k)
+    if need == ctypes.c_size_t(-1).value:
+        check(load().strata_moe_permute(None, T, E, k, None, None, None, None, None, 0, None))
+    ws = _workspace(dev, need, workspace)
     check(load().strata_moe_permute(_p(topk_ids), T, E, k, _p(counts), _p(offsets), _p(perm), _p(inv),
                                     _p(ws), ws.numel(), _stream(topk_ids)))
     return counts, offsets, perm, inv
@@ -221,18 +229,22 @@ def layer(logits: torch.Tensor, x: torch.Tensor, experts: QuantizedExperts, k: i
     dev = x.device
     if workspace is None:
         workspace = _workspace(dev, workspace_size(T, E, k, experts.hidden, experts.inter, experts.group), None)
-    res = dict(ids=torch.empty((T, k), dtype=torch.int32, device=dev),
-               w=torch.empty((T, k), dtype=torch.float32, device=dev),
-               counts=torch.empty(E, dtype=torch.int32, device=dev),
-               offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
-               perm=torch.empty(T * k, dtype=torch.int32, device=dev),
-               inv_perm=torch.empty(T * k, dtype=torch.int32, device=dev),
-               out=torch.empty((T, experts.hidden), dtype=torch.float32, device=dev))
+    res = _layer_outputs(T, E, k, experts.hidden, dev)
     desc = experts.descriptor()
     check(load().strata_moe_layer(_p(logits), _p(x), T, k, ctypes.byref(desc), _p(res["ids"]), _p(res["w"]),
                                   _p(res["counts"]), _p(res["offsets"]), _p(res["perm"]), _p(res["inv_perm"]),
                                   _p(res["out"]), _p(workspace), workspace.numel(), _stream(x)))
     return res
+
+
+def _layer_outputs(T: int, E: int, k: int, H: int, dev) -> dict:
+    return dict(ids=torch.empty((T, k), dtype=torch.int32, device=dev),
+                w=torch.empty((T, k), dtype=torch.float32, device=dev),
+                counts=torch.empty(E, dtype=torch.int32, device=dev),
+                offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                perm=torch.empty(T * k, dtype=torch.int32, device=dev),
+                inv_perm=torch.empty(T * k, dtype=torch.int32, device=dev),
+                out=torch.empty((T, H), dtype=torch.float32, device=dev))
 
 
 def timing_enable(on: bool = True) -> None:

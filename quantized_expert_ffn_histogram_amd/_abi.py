@@ -52,6 +52,7 @@ SIGNATURES = {
         [_vp, _vp, _i32, _i32, ctypes.POINTER(StrataMoeWeights), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     ),
     "strata_moe_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "strata_moe_permute_workspace_size": (_sz, [_i32, _i32, _i32]),
     "strata_moe_last_error": (ctypes.c_char_p, []),
     "strata_moe_timing_enable": (ctypes.c_int, [_i32]),
     "strata_moe_timing_query": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(_i32), ctypes.POINTER(ctypes.c_double)]),

@@ -141,6 +141,11 @@ size_t strata_moe_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int
   return layer_workspace_bytes(T, E, k, H, I);
 }
 
+size_t strata_moe_permute_workspace_size(int32_t T, int32_t E, int32_t k) {
+  if (check_tek("strata_moe_permute_workspace_size", T, E, k) != STRATA_OK) return (size_t)-1;
+  return permute_workspace_bytes((long long)T * k, E);
+}
+
 int strata_moe_route(const float *logits, int32_t T, int32_t E, int32_t k, int32_t *topk_ids,
                      float *topk_w, void *stream) {
   static const char *fn = "strata_moe_route";
@@ -250,10 +255,12 @@ int strata_moe_ffn(const uint16_t *x_bf16, int32_t T, int32_t k, const strata_mo
   return e == hipSuccess ? ok() : hip_fail(fn, e);
 }
 
-int strata_moe_layer(const float *logits, const uint16_t *x_bf16, int32_t T, int32_t k, const strata_moe_weights *w,
-                     int32_t *topk_ids, float *topk_w, int32_t *counts, int32_t *offsets, int32_t *perm,
-                     int32_t *inv_perm, float *out, void *workspace, size_t workspace_bytes, void *stream) {
-  static const char *fn = "strata_moe_layer";
+// The layer call on a given workspace; `fn` names the entry point in error
+// messages.
+static int layer_impl(const char *fn, const float *logits, const uint16_t *x_bf16, int32_t T, int32_t k,
+                      const strata_moe_weights *w, int32_t *topk_ids, float *topk_w, int32_t *counts,
+                      int32_t *offsets, int32_t *perm, int32_t *inv_perm, float *out, void *workspace,
+                      size_t workspace_bytes, void *stream) {
   if (w == nullptr) return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "w is NULL");
   const int E = w->num_experts, H = w->hidden, I = w->inter, g = w->group;
   if (int rc = check_tek(fn, T, E, k)) return rc;
@@ -322,6 +329,13 @@ int strata_moe_layer(const float *logits, const uint16_t *x_bf16, int32_t T, int
     }
   }
   return e == hipSuccess ? ok() : hip_fail(fn, e);
+}
+
+int strata_moe_layer(const float *logits, const uint16_t *x_bf16, int32_t T, int32_t k, const strata_moe_weights *w,
+                     int32_t *topk_ids, float *topk_w, int32_t *counts, int32_t *offsets, int32_t *perm,
+                     int32_t *inv_perm, float *out, void *workspace, size_t workspace_bytes, void *stream) {
+  return layer_impl("strata_moe_layer", logits, x_bf16, T, k, w, topk_ids, topk_w, counts, offsets, perm, inv_perm,
+                    out, workspace, workspace_bytes, stream);
 }
 
 int strata_moe_combine(const float *y, const int32_t *inv_perm, const float *topk_w, int32_t T, int32_t k,

@@ -784,12 +784,15 @@ __device__ __forceinline__ void gemm_tile_general(const GemmArgs &a, const GenRi
   const int col = lane & 31, half = lane >> 5;
   const int nchunks = a.K / kKC;
 
-  uint32_t aoff[NMB];
+  // 64-bit row addresses: this pipeline also takes the shapes whose A
+  // operand spans 4 GiB or more (the wide one's buffer offsets are 32-bit).
+  const char *abase = reinterpret_cast<const char *>(a.A);
+  const char *arow[NMB];
 #pragma unroll
   for (int i = 0; i < NMB; ++i) {
     const int p = (kGenW * i + wave) * 64 + lane;
     const int r = p >> 3, c = (p & 7) ^ (r & 7);
-    aoff[i] = ((uint32_t)rt.src[r] * (uint32_t)a.K + 8 * c) * 2;
+    arow[i] = abase + ((size_t)rt.src[r] * (size_t)a.K + 8 * c) * 2;
   }
   const int col2 = lane >> 1, hh = lane & 1;  // weight-row loads: row lane>>1 of a block, half lane&1
   const bool valid = weight_row0<MODE, kGenW>(slice, wave, 0) < a.N;
@@ -799,14 +802,12 @@ __device__ __forceinline__ void gemm_tile_general(const GemmArgs &a, const GenRi
   const uint32_t boff = (uint32_t)col2 * (a.K / 2) + 16 * hh;
   const uint32_t soff = ((uint32_t)col2 * (a.K / a.g)) * 2;
   const int g_shift = 31 - __clz(a.g);  // g is a power of two
-  const char *abase = reinterpret_cast<const char *>(a.A);
 
   auto issue = [&](GenStage &st, int c) {
     const int kc = c * kKC;
-    const char *ab = abase + 2 * kc;
 #pragma unroll
     for (int i = 0; i < NMB; ++i)
-      __builtin_amdgcn_global_load_lds(ab + aoff[i], as_lds(&st.a[(kGenW * i + wave) * 64]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(arow[i] + 2 * kc, as_lds(&st.a[(kGenW * i + wave) * 64]), 16, 0, 0);
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
       const int base = brow_of(wave, nb, 0) * 2;

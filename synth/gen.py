@@ -49,6 +49,8 @@ class MoEConfig:
     int4 group size g along K.  ``zipf_s`` set means router logits get a
     per-expert bias ``-zipf_s * ln(rank_e)`` over a seeded rank permutation,
     so that expert popularity follows a Zipf law of exponent ``zipf_s``.
+    ``weight_std`` is the standard deviation of the expert weights before
+    quantization (0.02 for every workload configuration).
     """
 
     name: str
@@ -60,6 +62,7 @@ class MoEConfig:
     g: int
     seed: int
     zipf_s: float | None = None
+    weight_std: float = WEIGHT_STD
 
     @property
     def pairs(self) -> int:
@@ -164,7 +167,7 @@ def make_router(T: int, H: int, E: int, seed: int) -> tuple[np.ndarray, np.ndarr
 
 def _expert_weights(cfg: MoEConfig, seq, e: int, out: dict) -> None:
     rng = np.random.default_rng(seq)
-    std = np.float32(WEIGHT_STD)
+    std = np.float32(cfg.weight_std)
     for name, (n, kdim) in (("gate", (cfg.I, cfg.H)), ("up", (cfg.I, cfg.H)), ("down", (cfg.H, cfg.I))):
         w = rng.standard_normal((n, kdim), dtype=np.float32) * std
         packed, scales = quantize_int4_groups(w, cfg.g)

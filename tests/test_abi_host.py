@@ -223,3 +223,14 @@ def test_binding_raises_without_library(tmp_path):
 
     with pytest.raises(RuntimeError, match="no CPU or PyTorch fallback"):
         _abi.load(str(tmp_path / "missing.so"))
+
+
+def test_permute_workspace_query():
+    _, lib = _lib()
+    assert lib.strata_moe_permute_workspace_size(4, 512, 10) == 0  # 40 pairs: one workgroup, no workspace
+    n = lib.strata_moe_permute_workspace_size(6144, 512, 10)
+    assert n >= 60 * 512 * 4 and n % 256 == 0  # 60 segments of 1024 pairs, one histogram row each
+    assert n <= lib.strata_moe_workspace_size(6144, 512, 10, 2048, 512, 64)
+    assert lib.strata_moe_permute_workspace_size(4, 16, 17) == ctypes.c_size_t(-1).value
+    assert "k=17 exceeds E=16" in _err(lib)
+
