@@ -248,6 +248,32 @@ int strata_moe_layer(const float *logits, const uint16_t *x_bf16, int32_t T, int
                      float *out, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * strata_moe_layer_noalloc - strata_moe_layer without a workspace argument,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation.  It runs
+ * the same kernels as strata_moe_layer (same results, bit for bit) on a
+ * scratch array that the library holds in static device memory: one copy of
+ * STRATA_MOE_NOALLOC_SCRATCH_BYTES per device the library runs on, kept until
+ * the process ends.  The call allocates nothing; the caller still provides
+ * every input and output array.
+ *
+ *   Arguments as for strata_moe_layer, without workspace / workspace_bytes.
+ *   Shapes whose workspace (strata_moe_workspace_size) exceeds
+ *   STRATA_MOE_NOALLOC_SCRATCH_BYTES return STRATA_ERR_UNSUPPORTED with the
+ *   required and available bytes in the message (e.g. a decode batch or a
+ *   512-token prefill at H = 2048, I = 512, E = 512, k = 10 fit; the
+ *   6144-token chunk does not).
+ *   All calls on one device share that device's scratch array: calls that
+ *   overlap in time on one device (concurrent streams, several host threads)
+ *   race on it and must be serialized by the caller.  The scratch keeps the
+ *   last call's contents; no result depends on them.
+ */
+#define STRATA_MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int strata_moe_layer_noalloc(const float *logits, const uint16_t *x_bf16, int32_t T, int32_t k,
+                             const strata_moe_weights *w, int32_t *topk_ids, float *topk_w, int32_t *counts,
+                             int32_t *offsets, int32_t *perm, int32_t *inv_perm, float *out, void *stream);
+
+/*
  * Bytes of device workspace that strata_moe_permute, strata_moe_ffn and
  * strata_moe_layer need for this shape (the ffn's regions plus the grouping
  * histogram's, which strata_moe_layer keeps apart).  Returns 0 for invalid

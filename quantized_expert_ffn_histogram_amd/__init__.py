@@ -28,6 +28,7 @@ __all__ = [
     "combine",
     "moe_layer",
     "layer",
+    "layer_noalloc",
     "LayerRunner",
     "workspace_size",
     "permute_workspace_size",
@@ -245,6 +246,20 @@ def _layer_outputs(T: int, E: int, k: int, H: int, dev) -> dict:
                 perm=torch.empty(T * k, dtype=torch.int32, device=dev),
                 inv_perm=torch.empty(T * k, dtype=torch.int32, device=dev),
                 out=torch.empty((T, H), dtype=torch.float32, device=dev))
+
+
+def layer_noalloc(logits: torch.Tensor, x: torch.Tensor, experts: QuantizedExperts, k: int,
+                  outputs: dict | None = None) -> dict:
+    """``strata_moe_layer_noalloc``: the layer call on the library's static
+    device scratch (no workspace).  ``outputs`` (the dict this returns) may be
+    passed back in to reuse the output tensors."""
+    T = x.shape[0]
+    res = outputs if outputs is not None else _layer_outputs(T, experts.num_experts, k, experts.hidden, x.device)
+    desc = experts.descriptor()
+    check(load().strata_moe_layer_noalloc(_p(logits), _p(x), T, k, ctypes.byref(desc), _p(res["ids"]),
+                                          _p(res["w"]), _p(res["counts"]), _p(res["offsets"]), _p(res["perm"]),
+                                          _p(res["inv_perm"]), _p(res["out"]), _stream(x)))
+    return res
 
 
 def timing_enable(on: bool = True) -> None:

@@ -51,6 +51,10 @@ SIGNATURES = {
         ctypes.c_int,
         [_vp, _vp, _i32, _i32, ctypes.POINTER(StrataMoeWeights), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     ),
+    "strata_moe_layer_noalloc": (
+        ctypes.c_int,
+        [_vp, _vp, _i32, _i32, ctypes.POINTER(StrataMoeWeights), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    ),
     "strata_moe_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "strata_moe_permute_workspace_size": (_sz, [_i32, _i32, _i32]),
     "strata_moe_last_error": (ctypes.c_char_p, []),

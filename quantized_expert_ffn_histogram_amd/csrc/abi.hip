@@ -7,6 +7,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "strata_moe.h"
@@ -127,6 +128,52 @@ FfnWorkspace carve_ffn_workspace(void *base, long long T, int k, int E, int H, i
 // the ffn's fp16 x before the grouping runs).
 size_t layer_workspace_bytes(long long T, int E, int k, int H, int I) {
   return up256(ffn_workspace_bytes(T, k, E, H, I)) + up256(permute_workspace_bytes(T * k, E));
+}
+
+// ---------------------------------------------------------------- static scratch
+// Scratch memory of strata_moe_layer_noalloc, for callers that cannot
+// allocate device memory.  Each device the library runs on holds its own copy
+// of this array (in the code object's device globals) until the process ends.
+// Host code never uses the name `scratch` as an address: it is a host-side
+// stand-in; the device address of each device's copy comes from
+// hipGetSymbolAddress, looked up once per device with that device current.
+constexpr size_t kNoAllocScratchBytes = STRATA_MOE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+// Device address of the scratch array on the device of `stream` (the current
+// device for the null stream).  The first call on a device looks it up with
+// that device current and restores the caller's current device afterwards.
+hipError_t noalloc_scratch(hipStream_t stream, void **out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  int dev = cur;
+  if (stream != nullptr) {
+    hipDevice_t sd = 0;
+    if ((e = hipStreamGetDevice(stream, &sd)) != hipSuccess) return e;
+    dev = sd;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t r = hipSetDevice(cur);
+      if (e == hipSuccess) e = r;
+    }
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace strata
@@ -255,8 +302,8 @@ int strata_moe_ffn(const uint16_t *x_bf16, int32_t T, int32_t k, const strata_mo
   return e == hipSuccess ? ok() : hip_fail(fn, e);
 }
 
-// The layer call on a given workspace; `fn` names the entry point in error
-// messages.
+// The layer call on a given workspace (strata_moe_layer and
+// strata_moe_layer_noalloc); `fn` names the entry point in error messages.
 static int layer_impl(const char *fn, const float *logits, const uint16_t *x_bf16, int32_t T, int32_t k,
                       const strata_moe_weights *w, int32_t *topk_ids, float *topk_w, int32_t *counts,
                       int32_t *offsets, int32_t *perm, int32_t *inv_perm, float *out, void *workspace,
@@ -336,6 +383,26 @@ int strata_moe_layer(const float *logits, const uint16_t *x_bf16, int32_t T, int
                      int32_t *inv_perm, float *out, void *workspace, size_t workspace_bytes, void *stream) {
   return layer_impl("strata_moe_layer", logits, x_bf16, T, k, w, topk_ids, topk_w, counts, offsets, perm, inv_perm,
                     out, workspace, workspace_bytes, stream);
+}
+
+int strata_moe_layer_noalloc(const float *logits, const uint16_t *x_bf16, int32_t T, int32_t k,
+                             const strata_moe_weights *w, int32_t *topk_ids, float *topk_w, int32_t *counts,
+                             int32_t *offsets, int32_t *perm, int32_t *inv_perm, float *out, void *stream) {
+  static const char *fn = "strata_moe_layer_noalloc";
+  if (w == nullptr) return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "w is NULL");
+  if (int rc = check_tek(fn, T, w->num_experts, k)) return rc;
+  if (int rc = check_shape(fn, w->hidden, w->inter, w->group)) return rc;
+  const size_t need = layer_workspace_bytes(T, w->num_experts, k, w->hidden, w->inter);
+  if (need > kNoAllocScratchBytes)
+    return fail(STRATA_ERR_UNSUPPORTED, fn,
+                "T=%d, E=%d, k=%d, hidden=%d, inter=%d needs %zu bytes of scratch, more than the library's static "
+                "%zu (STRATA_MOE_NOALLOC_SCRATCH_BYTES); call strata_moe_layer with a workspace instead",
+                T, w->num_experts, k, w->hidden, w->inter, need, kNoAllocScratchBytes);
+  void *ws = nullptr;
+  const hipError_t e = noalloc_scratch(static_cast<hipStream_t>(stream), &ws);
+  if (e != hipSuccess) return hip_fail(fn, e);
+  return layer_impl(fn, logits, x_bf16, T, k, w, topk_ids, topk_w, counts, offsets, perm, inv_perm, out, ws,
+                    kNoAllocScratchBytes, stream);
 }
 
 int strata_moe_combine(const float *y, const int32_t *inv_perm, const float *topk_w, int32_t T, int32_t k,

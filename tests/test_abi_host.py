@@ -234,3 +234,21 @@ def test_permute_workspace_query():
     assert lib.strata_moe_permute_workspace_size(4, 16, 17) == ctypes.c_size_t(-1).value
     assert "k=17 exceeds E=16" in _err(lib)
 
+
+def test_noalloc_layer_checks_sizes_before_launch():
+    """strata_moe_layer_noalloc refuses shapes whose workspace exceeds its
+    static scratch, and bad arguments, before touching a device."""
+    abi, lib = _lib()
+    fake = ctypes.c_void_p(0x10000)
+
+    def call(T, wp, k=10):
+        return lib.strata_moe_layer_noalloc(fake, fake, T, k, wp, fake, fake, fake, fake, fake, fake, fake, None)
+
+    big = _weights(abi, E=512, H=2048, I=512, g=64)
+    assert call(6144, ctypes.byref(big)) == 2
+    msg = _err(lib)
+    need = lib.strata_moe_workspace_size(6144, 512, 10, 2048, 512, 64)
+    assert msg.startswith("strata_moe_layer_noalloc") and str(need) in msg and str(64 << 20) in msg
+    assert call(4, None) == 1 and "w is NULL" in _err(lib)
+    assert call(4, ctypes.byref(_weights(abi, g=48)), k=2) == 2 and "group=48" in _err(lib)
+    assert call(4, ctypes.byref(_weights(abi)), k=17) == 1 and "k=17 exceeds E=16" in _err(lib)
