@@ -1,4 +1,5 @@
-"""Seeded synthetic inputs for the routed MoE FFN layer (shared by the oracle and the GPU path)."""
+"""Seeded synthetic inputs for the routed MoE FFN layer and the KV-cache attention (shared by the
+oracle and the GPU path)."""
 from .gen import (  # noqa: F401
     CONFIGS,
     MoEConfig,
@@ -13,3 +14,4 @@ from .gen import (  # noqa: F401
     quantize_int4_groups,
     weight_bytes_per_expert,
 )
+from .kv import ATTN_CONFIGS, AttnConfig, AttnInputs, attn_config, make_attn_inputs  # noqa: F401
