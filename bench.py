@@ -465,6 +465,86 @@ def bench_router(qe, args):
                 "hbm_frac": round((T * H * 2 + E * H * 2 + T * E * 4) / (proj_us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}}
 
 
+def bench_kv(qe, args):
+    """The 4-bit KV cache: encoding a prefill chunk's keys and values
+    (T = 6144 tokens x 8 KV heads x 128, bf16 in, codes + scales out), and
+    sparse attention of one decode step (1 + 3 draft tokens, 32 query heads
+    over 8 KV heads) over 2048 selected positions of a 128k-position cache.
+    Both are HBM-bound: algorithmic bytes are the inputs read once and the
+    outputs written once (for attention: the selected key and value rows,
+    q and out)."""
+    import torch
+
+    import synth
+
+    dev = torch.device("cuda:0")
+    res = {}
+    # Encode: K and V of a 6144-token chunk.
+    T, Hkv, D, L = 6144, 8, 128, 131072
+    g = torch.Generator(device=dev).manual_seed(97)
+    xk = torch.randn((T, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+    xv = torch.randn((T, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+    codes_k = torch.empty((L, Hkv, D // 2), dtype=torch.uint8, device=dev)
+    codes_v = torch.empty_like(codes_k)
+    sc_k = torch.empty((L, Hkv), dtype=torch.float16, device=dev)
+    sc_v = torch.empty_like(sc_k)
+    slots = torch.arange(T, dtype=torch.int32, device=dev) + 1000
+
+    def enc(_i):
+        qe.kv_quantize(xk, slots, codes_k, sc_k)
+        qe.kv_quantize(xv, slots, codes_v, sc_v)
+
+    for i in range(5):
+        enc(i)
+    steps = 200
+    secs = time_region(enc, steps)
+    nbytes = 2 * (T * Hkv * D * 2 + T * Hkv * (D // 2 + 2))
+    us = secs / steps * 1e6
+    res["encode"] = {"workload": f"K and V of T={T} tokens x Hkv={Hkv} x D={D} (bf16) into a 4-bit cache",
+                     "us_per_step": round(us, 2), "alg_bytes": nbytes,
+                     "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+    # Sparse attention of a decode step over the 128k cache.
+    for name in ("attn_decode128k", "attn_chunk16"):
+        inp = synth.make_attn_inputs(name)
+        cfg = inp.cfg
+        kc = torch.empty((cfg.L, cfg.Hkv, cfg.D // 2), dtype=torch.uint8, device=dev)
+        vc = torch.empty_like(kc)
+        ks = torch.empty((cfg.L, cfg.Hkv), dtype=torch.float16, device=dev)
+        vs = torch.empty_like(ks)
+        allpos = torch.arange(cfg.L, dtype=torch.int32, device=dev)
+        qe.kv_quantize(torch.from_numpy(inp.k_bf16.view(np.int16)).to(dev).view(torch.bfloat16), allpos, kc, ks)
+        qe.kv_quantize(torch.from_numpy(inp.v_bf16.view(np.int16)).to(dev).view(torch.bfloat16), allpos, vc, vs)
+        q = torch.from_numpy(inp.q_bf16.view(np.int16)).to(dev).view(torch.bfloat16)
+        sel = torch.from_numpy(inp.sel).to(dev)
+        out = torch.empty((cfg.Tq, cfg.Hq, cfg.D), dtype=torch.float32, device=dev)
+        ws = torch.empty(qe.load().strata_sparse_attention_workspace_size(cfg.Tq, cfg.Hq, cfg.n_sel),
+                         dtype=torch.uint8, device=dev)
+
+        def attn(_i):
+            qe.sparse_attention(q, kc, ks, vc, vs, sel, cfg.sm_scale, out=out, workspace=ws)
+
+        for i in range(10):
+            attn(i)
+        steps = 2000
+        secs = time_region(attn, steps)
+        us = secs / steps * 1e6
+        qe.timing_enable(True)
+        time_region(attn, 200)
+        kern = {n: round(qe.timing_query(n)[1] / max(qe.timing_query(n)[0], 1) * 1e3, 2) for n in qe.timing_kernels()}
+        qe.timing_enable(False)
+        pct = step_percentiles(attn, 500)
+        rows = cfg.Tq * cfg.n_sel * cfg.Hkv * 2 * (cfg.D // 2 + 2)
+        nbytes = rows + cfg.Tq * cfg.n_sel * 4 + cfg.Tq * cfg.Hq * cfg.D * (2 + 4)
+        res[name] = {"workload": f"{name}: Tq={cfg.Tq} Hq={cfg.Hq} Hkv={cfg.Hkv} D={cfg.D} L={cfg.L} "
+                                 f"n_sel={cfg.n_sel} (4-bit cache, selected rows only)",
+                     "us_per_call": round(us, 2), "step_percentiles": pct, "kernels_us": kern,
+                     "alg_bytes": int(nbytes), "hbm_frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
+        log(f"[bench] {name}: {us:.2f} us/call {kern}")
+        del kc, vc, ks, vs, q, sel, out, ws, inp
+        torch.cuda.empty_cache()
+    return res
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -550,6 +630,8 @@ def main(argv=None) -> int:
     ap.add_argument("--fused", type=int, default=1, help="1: fused weighted scatter-add; 0: y rows + combine")
     ap.add_argument("--router-only", action="store_true",
                     help="time only the router projection + top-k call (router6144) and print its record")
+    ap.add_argument("--kv-only", action="store_true",
+                    help="time only the 4-bit KV cache encode and sparse attention and print their record")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain 1 GiB device copy (reference for HBM byte counters)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -579,6 +661,9 @@ def main(argv=None) -> int:
     qe.load()
     if args.router_only:
         print(json.dumps(bench_router(qe, args)), flush=True)
+        return 0
+    if args.kv_only:
+        print(json.dumps(bench_kv(qe, args)), flush=True)
         return 0
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
@@ -622,6 +707,7 @@ def main(argv=None) -> int:
         result["decode"] = bench_decode(qe, args)
     if not args.no_secondary:
         result["secondary"] = bench_secondary(qe, args)
+        result["kv_cache"] = bench_kv(qe, args)
     ref = None
     if not args.no_cpu_baseline:
         result["cpu_baseline"], ref = cpu_baseline(cfg, inp)

@@ -289,6 +289,67 @@ size_t strata_moe_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H,
  */
 size_t strata_moe_permute_workspace_size(int32_t T, int32_t E, int32_t k);
 
+/*
+ * 4-bit KV cache and sparse attention over it.
+ *
+ * The key/value cache can be stored in 4 bits per element (the optional
+ * 4-bit KV cache of "40天64个版本：Strata如何用发版密度定义AI本地推理路线图",
+ * release 0.1.8), quantized per head and symmetrically (lqnn.cn static
+ * review, §3.1), with the dequantization fused into the operator that reads
+ * the cache (yfxerp.com static review, §4.2).  The attention reads only the
+ * ~2000 cache rows that an indexer selected for each query
+ * ("两天移植，预填充提速8倍：Strata引擎实测" (kongchang.com), section
+ * "Strata快在哪：不是魔法，是物流", attention paragraph).
+ *
+ * Cache format (one array for keys, one for values): codes uint8 [L][Hkv][D/2]
+ * holding offset-binary nibbles u = q + 8 (even element in the low nibble)
+ * and scales fp16 [L][Hkv], one per (position, head) vector:
+ * x[l][h][d] = (u - 8) * scale[l][h].  Supported: D = 128, Hkv in {1, 2, 4, 8}
+ * (outside: STRATA_ERR_UNSUPPORTED).
+ */
+
+/*
+ * strata_kv_quantize - write T new (token, head) vectors into the cache.
+ *
+ *   x_bf16   in  bf16 bits [T][Hkv][D].
+ *   slots    in  int32 [T]: cache position of token t; rows whose slot lies
+ *                outside [0, L) are skipped.
+ *   codes    out uint8 [L][Hkv][D/2], rows slots[t] written.
+ *   scales   out fp16 bits [L][Hkv], rows slots[t] written.
+ * Per vector: s = fp16(max|x| / 7) and q = clamp(rint(x / s), -8, 7), the
+ * division and rounding in IEEE fp32 (nearest-even); an all-zero vector gets
+ * s = 0 and codes 8.  Bit-exact and deterministic.  Inputs must satisfy
+ * max|x| <= 7 * 65504 (beyond it the fp16 scale overflows to inf).  Two
+ * tokens with the same slot race (the last write is unspecified).
+ */
+int strata_kv_quantize(const uint16_t *x_bf16, int32_t T, int32_t Hkv, int32_t D, const int32_t *slots,
+                       uint8_t *codes, uint16_t *scales, int32_t L, void *stream);
+
+/*
+ * strata_sparse_attention - attention of Tq queries over selected positions
+ * of a 4-bit cache, dequantizing the selected rows as they are read.
+ *
+ *   q_bf16   in  bf16 bits [Tq][Hq][D]; query head h reads KV head
+ *                h / (Hq / Hkv) (Hq / Hkv in {1, 2, 4}).
+ *   k_codes, k_scales, v_codes, v_scales  in  the cache, as above, L positions.
+ *   sel      in  int32 [Tq][n_sel] cache positions per query (each in
+ *                [0, L): a precondition), or NULL for positions 0 .. n_sel-1;
+ *                1 <= n_sel <= 32768.
+ *   sm_scale in  score scale (usually 1/sqrt(D)).
+ *   out      out float32 [Tq][Hq][D]:
+ *                out[t][h] = sum_i p_i v[sel[t][i]][h / (Hq/Hkv)],
+ *                p = softmax_i(sm_scale * q[t][h] . k[sel[t][i]][...]),
+ *                in fp32; chunks of 16 positions are combined in a fixed
+ *                order, so the result is deterministic.
+ *   workspace  device scratch of strata_sparse_attention_workspace_size(Tq,
+ *              Hq, n_sel) bytes, 256-byte aligned.
+ */
+size_t strata_sparse_attention_workspace_size(int32_t Tq, int32_t Hq, int32_t n_sel);
+int strata_sparse_attention(const uint16_t *q_bf16, int32_t Tq, int32_t Hq, const uint8_t *k_codes,
+                            const uint16_t *k_scales, const uint8_t *v_codes, const uint16_t *v_scales, int32_t L,
+                            int32_t Hkv, int32_t D, const int32_t *sel, int32_t n_sel, float sm_scale, float *out,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
 /* Message describing the last failed call on this thread ("" if none). */
 const char *strata_moe_last_error(void);
 
@@ -311,7 +372,8 @@ const char *strata_moe_last_error(void);
  *                               returns how many there are.
  * Kernel names: router_logits, route_topk, route_xconv, permute_small, permute_hist,
  * permute_scan, permute_scatter, ffn_prep, gemm_gateup, gemm_down,
- * gemv_gateup, gemv_down, combine, decode_route_gateup, decode_down_combine.
+ * gemv_gateup, gemv_down, combine, decode_route_gateup, decode_down_combine,
+ * kv_quantize, attn_partial, attn_merge.
  */
 int strata_moe_timing_enable(int32_t on);
 int strata_moe_timing_query(const char *kernel, int32_t *launches, double *total_ms);

@@ -33,6 +33,8 @@ __all__ = [
     "workspace_size",
     "permute_workspace_size",
     "router",
+    "kv_quantize",
+    "sparse_attention",
     "timing_enable",
     "timing_query",
     "timing_kernels",
@@ -260,6 +262,43 @@ def layer_noalloc(logits: torch.Tensor, x: torch.Tensor, experts: QuantizedExper
                                           _p(res["w"]), _p(res["counts"]), _p(res["offsets"]), _p(res["perm"]),
                                           _p(res["inv_perm"]), _p(res["out"]), _stream(x)))
     return res
+
+
+def kv_quantize(x: torch.Tensor, slots: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor) -> None:
+    """``strata_kv_quantize``: quantize x (bf16 [T, Hkv, D]) into cache rows
+    ``slots`` (int32 [T]) of ``codes`` (uint8 [L, Hkv, D/2]) and ``scales``
+    (float16 [L, Hkv])."""
+    _need(x, torch.bfloat16, "x")
+    _need(slots, torch.int32, "slots")
+    _need(codes, torch.uint8, "codes")
+    _need(scales, torch.float16, "scales")
+    T, Hkv, D = x.shape
+    L = codes.shape[0]
+    check(load().strata_kv_quantize(_p(x), T, Hkv, D, _p(slots), _p(codes), _p(scales), L, _stream(x)))
+
+
+def sparse_attention(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, v_codes: torch.Tensor,
+                     v_scales: torch.Tensor, sel: torch.Tensor | None, sm_scale: float, n_sel: int | None = None,
+                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """``strata_sparse_attention``: q bf16 [Tq, Hq, D] over the selected rows
+    (``sel`` int32 [Tq, n_sel], or None with ``n_sel``: the first n_sel
+    positions) of a 4-bit cache; returns float32 [Tq, Hq, D]."""
+    _need(q, torch.bfloat16, "q")
+    for name, t, dt in (("k_codes", k_codes, torch.uint8), ("v_codes", v_codes, torch.uint8),
+                        ("k_scales", k_scales, torch.float16), ("v_scales", v_scales, torch.float16)):
+        _need(t, dt, name)
+    Tq, Hq, D = q.shape
+    L, Hkv = k_codes.shape[0], k_codes.shape[1]
+    if sel is not None:
+        _need(sel, torch.int32, "sel")
+        n_sel = sel.shape[1]
+    if out is None:
+        out = torch.empty((Tq, Hq, D), dtype=torch.float32, device=q.device)
+    lib = load()
+    ws = _workspace(q.device, lib.strata_sparse_attention_workspace_size(Tq, Hq, n_sel), workspace)
+    check(lib.strata_sparse_attention(_p(q), Tq, Hq, _p(k_codes), _p(k_scales), _p(v_codes), _p(v_scales), L, Hkv,
+                                      D, _p(sel), n_sel, float(sm_scale), _p(out), _p(ws), ws.numel(), _stream(q)))
+    return out
 
 
 def timing_enable(on: bool = True) -> None:

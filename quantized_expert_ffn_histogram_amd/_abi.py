@@ -55,6 +55,12 @@ SIGNATURES = {
         ctypes.c_int,
         [_vp, _vp, _i32, _i32, ctypes.POINTER(StrataMoeWeights), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     ),
+    "strata_kv_quantize": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp]),
+    "strata_sparse_attention_workspace_size": (_sz, [_i32, _i32, _i32]),
+    "strata_sparse_attention": (
+        ctypes.c_int,
+        [_vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, ctypes.c_float, _vp, _vp, _sz, _vp],
+    ),
     "strata_moe_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "strata_moe_permute_workspace_size": (_sz, [_i32, _i32, _i32]),
     "strata_moe_last_error": (ctypes.c_char_p, []),

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <cmath>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -419,6 +420,69 @@ int strata_moe_combine(const float *y, const int32_t *inv_perm, const float *top
   REQUIRE_PTR(fn, topk_w);
   REQUIRE_PTR(fn, out);
   const hipError_t e = launch_combine(y, inv_perm, topk_w, T, k, H, out, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(fn, e);
+}
+
+int strata_kv_quantize(const uint16_t *x_bf16, int32_t T, int32_t Hkv, int32_t D, const int32_t *slots,
+                       uint8_t *codes, uint16_t *scales, int32_t L, void *stream) {
+  static const char *fn = "strata_kv_quantize";
+  if (T < 0) return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "T=%d is negative", T);
+  if (L < 1) return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "L=%d must be >= 1", L);
+  if (!kv_shape_supported(Hkv, D))
+    return fail(STRATA_ERR_UNSUPPORTED, fn, "Hkv=%d, D=%d: supported are D = 128 and Hkv in {1, 2, 4, 8}", Hkv, D);
+  if ((long long)T * Hkv >= (1ll << 31) || (long long)L * Hkv * D >= (1ll << 40))
+    return fail(STRATA_ERR_UNSUPPORTED, fn, "T=%d or L=%d too large", T, L);
+  if (T == 0) return ok();
+  REQUIRE_PTR(fn, x_bf16);
+  REQUIRE_PTR(fn, slots);
+  REQUIRE_PTR(fn, codes);
+  REQUIRE_PTR(fn, scales);
+  const hipError_t e = launch_kv_quantize(x_bf16, T, Hkv, slots, L, codes, scales, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? ok() : hip_fail(fn, e);
+}
+
+size_t strata_sparse_attention_workspace_size(int32_t Tq, int32_t Hq, int32_t n_sel) {
+  if (Tq < 0 || Hq < 1 || n_sel < 1) return 0;
+  return attn_workspace_bytes(Tq, Hq, n_sel);
+}
+
+int strata_sparse_attention(const uint16_t *q_bf16, int32_t Tq, int32_t Hq, const uint8_t *k_codes,
+                            const uint16_t *k_scales, const uint8_t *v_codes, const uint16_t *v_scales, int32_t L,
+                            int32_t Hkv, int32_t D, const int32_t *sel, int32_t n_sel, float sm_scale, float *out,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+  static const char *fn = "strata_sparse_attention";
+  if (Tq < 0) return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "Tq=%d is negative", Tq);
+  if (L < 1) return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "L=%d must be >= 1", L);
+  if (n_sel < 1) return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "n_sel=%d must be >= 1", n_sel);
+  if (n_sel > 32768) return fail(STRATA_ERR_UNSUPPORTED, fn, "n_sel=%d exceeds the supported maximum 32768", n_sel);
+  if (sel == nullptr && n_sel > L)
+    return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "sel is NULL and n_sel=%d exceeds L=%d", n_sel, L);
+  if (!kv_shape_supported(Hkv, D))
+    return fail(STRATA_ERR_UNSUPPORTED, fn, "Hkv=%d, D=%d: supported are D = 128 and Hkv in {1, 2, 4, 8}", Hkv, D);
+  if (Hq < Hkv || Hq % Hkv || Hq / Hkv > 4)
+    return fail(STRATA_ERR_UNSUPPORTED, fn, "Hq=%d must be Hkv=%d times 1, 2 or 4", Hq, Hkv);
+  if (!(sm_scale == sm_scale) || sm_scale == INFINITY || sm_scale == -INFINITY)
+    return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "sm_scale is not finite");
+  if ((long long)Tq * ((n_sel + 31) / 32) >= (1ll << 31) || (long long)L * Hkv * D >= (1ll << 40))
+    return fail(STRATA_ERR_UNSUPPORTED, fn, "Tq=%d, n_sel=%d or L=%d too large", Tq, n_sel, L);
+  if (Tq == 0) return ok();
+  REQUIRE_PTR(fn, q_bf16);
+  REQUIRE_PTR(fn, k_codes);
+  REQUIRE_PTR(fn, k_scales);
+  REQUIRE_PTR(fn, v_codes);
+  REQUIRE_PTR(fn, v_scales);
+  REQUIRE_PTR(fn, out);
+  if (sel != nullptr && !aligned16(sel))
+    return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "sel=%p is not 16-byte aligned", (const void *)sel);
+  const size_t need = attn_workspace_bytes(Tq, Hq, n_sel);
+  if (workspace == nullptr)
+    return fail(STRATA_ERR_WORKSPACE, fn, "workspace is NULL but %zu bytes are required", need);
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "workspace=%p is not 256-byte aligned", workspace);
+  if (workspace_bytes < need)
+    return fail(STRATA_ERR_WORKSPACE, fn, "workspace_bytes=%zu is smaller than the required %zu", workspace_bytes, need);
+  const hipError_t e = launch_sparse_attention(q_bf16, Tq, Hq, k_codes, k_scales, v_codes, v_scales, L, Hkv, sel,
+                                               n_sel, sm_scale, out, workspace, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ok() : hip_fail(fn, e);
 }
 

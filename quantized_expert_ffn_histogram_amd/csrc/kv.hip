@@ -1,0 +1,367 @@
+// 4-bit KV cache: per-head symmetric quantization of key / value vectors,
+// and attention of decode queries over the cache rows an indexer selected,
+// with the dequantization fused into the attention's reads.
+//
+// The cache of keys and values can be kept in 4 bits per element (the
+// optional 4-bit KV cache of the release notes, "40天64个版本：Strata如何用发
+// 版密度定义AI本地推理路线图", release 0.1.8), quantized per head and
+// symmetrically (lqnn.cn static review, §3.1, the KV-cache branch), with the
+// dequantization moved into the operator that reads the cache instead of a
+// separate pass (yfxerp.com static review, §4.2).  The attention reads only
+// the ~2000 cache rows the indexer picked for each query
+// ("两天移植，预填充提速8倍：Strata引擎实测" (kongchang.com), section
+// "Strata快在哪：不是魔法，是物流", attention paragraph).
+//
+// Cache layout: codes [L][Hkv][D/2] (offset-binary nibbles u = q + 8, even
+// element in the low nibble) and one fp16 scale per (position, head)
+// [L][Hkv]; a position's Hkv head vectors are contiguous, so a selected
+// position is one contiguous Hkv * 64-byte read.
+//
+// kv_quantize: one wavefront per (token, head) vector: max |x| by a
+//   wavefront reduction, s = fp16(max / 7), q = clamp(rint(x / s), -8, 7);
+//   the code decision is taken in fp32 with IEEE division.
+// sparse attention, two kernels:
+//   partial (grid: query token x chunk of 16 selected positions, 256
+//     threads): scores of all query heads against the chunk's keys (each
+//     thread a quarter of a head vector, quad reduction), the chunk's
+//     softmax numerators, and the weighted sum of its values, which were
+//     staged in LDS while the scores were computed; writes (max, sum,
+//     unnormalized output) per head and chunk;
+//   merge (grid: query token x head, one thread per element): combines the
+//     chunks in order with the usual rescaling by exp(m_c - M) - so the
+//     result does not depend on scheduling.
+#include "moe_internal.h"
+
+namespace strata {
+namespace {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kKvD = 128;        // head_dim
+constexpr int kAttnChunk = 16;   // selected positions per workgroup
+constexpr int kPartStride = kKvD + 4;  // floats per (token, head, chunk) partial: output, max, sum, pad
+
+__device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
+
+// Each wavefront quantizes kRowsPerWave vectors of D = 128 bf16 values (rows
+// t*Hkv + h): lane l holds elements 2l and 2l+1 of each and writes code byte
+// l.  All of a wavefront's loads are issued before the first reduction.
+// Rows whose slot lies outside [0, L) are skipped.
+constexpr int kRowsPerWave = 4;
+
+__global__ __launch_bounds__(256) void kv_quantize_kernel(const uint32_t *__restrict__ x, int rows, int Hkv,
+                                                          const int *__restrict__ slots, int L,
+                                                          uint8_t *__restrict__ codes, uint16_t *__restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kRowsPerWave;
+  uint32_t d[kRowsPerWave];
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; ++r) d[r] = row0 + r < rows ? x[(size_t)(row0 + r) * (kKvD / 2) + lane] : 0u;
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; ++r) {
+    const int row = row0 + r;
+    if (row >= rows) break;
+    const int t = row / Hkv, h = row - t * Hkv;
+    const int slot = slots[t];
+    const float a = bf16_lo(d[r]), b = bf16_hi(d[r]);
+    const float amax = __uint_as_float(wave_max_u32(__float_as_uint(fmaxf(fabsf(a), fabsf(b)))));
+    if (slot < 0 || slot >= L) continue;
+    const _Float16 s16 = (_Float16)(amax / 7.0f);
+    const float sc = (float)s16;
+    int qa = 0, qb = 0;
+    if (sc > 0.0f) {
+      qa = (int)fminf(fmaxf(__builtin_rintf(a / sc), -8.0f), 7.0f);
+      qb = (int)fminf(fmaxf(__builtin_rintf(b / sc), -8.0f), 7.0f);
+    }
+    const size_t dst = (size_t)slot * Hkv + h;
+    codes[dst * (kKvD / 2) + lane] = (uint8_t)((qa + 8) | ((qb + 8) << 4));
+    if (lane == 0) scale[dst] = __builtin_bit_cast(uint16_t, s16);
+  }
+}
+
+struct AttnArgs {
+  const uint16_t *q;        // bf16 [Tq][Hq][D]
+  const uint8_t *kc, *vc;   // codes [L][Hkv][D/2]
+  const uint16_t *ks, *vs;  // fp16 scales [L][Hkv]
+  const int *sel;           // [Tq][n_sel] or null (positions 0 .. n_sel-1)
+  int Tq, Hq, Hkv, L, n_sel, nchunks;
+  float sm_scale;
+  float *part;              // [Tq][Hq][nchunks][kPartStride]: output, max, sum
+  float *out;               // fp32 [Tq][Hq][D]
+};
+
+// The 8 nibbles of one dword (elements 8j .. 8j+7 in order) as floats u in
+// [0, 15]: two masks and one byte conversion per element.
+__device__ __forceinline__ void nib8(uint32_t w, float *o) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+  // (float)((v >> 8k) & 0xFF) is one v_cvt_f32_ubyte<k>.
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    o[2 * k] = (float)((lo >> (8 * k)) & 0xFFu);
+    o[2 * k + 1] = (float)((hi >> (8 * k)) & 0xFFu);
+  }
+}
+
+template <int G>  // query heads per KV head
+__global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
+  constexpr int D = kKvD, C = kAttnChunk;
+  constexpr int kMaxRounds = (C + 7) / 8;  // score rounds at Hkv = 8 (8 positions per round)
+  const int tid = threadIdx.x;
+  const int t = blockIdx.x / a.nchunks, chunk = blockIdx.x - t * a.nchunks;
+  const int i0 = chunk * C, cnt = min(C, a.n_sel - i0);
+  const int Hkv = a.Hkv, Hq = a.Hq;
+
+  __shared__ int pos_s[C];
+  __shared__ float score[32][C];            // [query head][position]
+  __shared__ u32x4_t vrow[C * 8 * (D / 32)];  // [position][Hkv][D/2 bytes], up to Hkv = 8
+  __shared__ float vscale[C][8];
+  __shared__ float mh[32], lh[32];
+
+  if (tid < C) {
+    const int i = i0 + min(tid, cnt - 1);  // past the end: repeat the last position (weight 0)
+    pos_s[tid] = a.sel ? a.sel[(size_t)t * a.n_sel + i] : i;
+  }
+  __syncthreads();
+
+  // Every load of the workgroup goes out first: the chunk's value rows and
+  // scales (staged to LDS below) and this thread's key words of all rounds.
+  const int units = C * Hkv * 4;  // 16-byte units of value rows
+  u32x4_t vreg[4] = {};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int u = tid + 256 * r;
+    if (u < units) {
+      const int pl = u / (Hkv * 4), w = u - pl * (Hkv * 4);
+      vreg[r] = reinterpret_cast<const u32x4_t *>(a.vc + (size_t)pos_s[pl] * Hkv * (D / 2))[w];
+    }
+  }
+  float vsc = 0.0f;
+  if (tid < C * Hkv) {
+    const int pl = tid / Hkv, g = tid - pl * Hkv;
+    vsc = (float)__builtin_bit_cast(_Float16, a.vs[(size_t)pos_s[pl] * Hkv + g]);
+  }
+  // Scores: thread (position pl, head g, quarter qd) of a round, 4 * Hkv
+  // threads per position.
+  const int tpp = 4 * Hkv, ppr = 256 / tpp;  // threads per position, positions per round
+  const int rounds = (C + ppr - 1) / ppr;    // <= kMaxRounds
+  const int pr = tid / tpp, rem = tid - pr * tpp, g = rem >> 2, qd = rem & 3;
+  u32x4_t kw[kMaxRounds];
+  float ksc[kMaxRounds];
+#pragma unroll
+  for (int r = 0; r < kMaxRounds; ++r) {
+    const int pl = min(r * ppr + pr, C - 1);
+    const size_t row = (size_t)pos_s[pl] * Hkv + g;
+    kw[r] = r < rounds ? reinterpret_cast<const u32x4_t *>(a.kc + row * (D / 2))[qd] : u32x4_t{};
+    ksc[r] = r < rounds ? (float)__builtin_bit_cast(_Float16, a.ks[row]) : 0.0f;
+  }
+  // This thread's query slices (G heads x 32 values) and their sums (the
+  // offset term: q . (u - 8) = q . u - 8 sum(q)).
+  float qv[G][32], qsum[G];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const u32x4_t *qp = reinterpret_cast<const u32x4_t *>(a.q + ((size_t)t * Hq + g * G + hh) * D + 32 * qd);
+    qsum[hh] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const u32x4_t v = qp[c];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        qv[hh][8 * c + 2 * i] = bf16_lo(v[i]);
+        qv[hh][8 * c + 2 * i + 1] = bf16_hi(v[i]);
+        qsum[hh] += qv[hh][8 * c + 2 * i] + qv[hh][8 * c + 2 * i + 1];
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < kMaxRounds; ++r) {
+    if (r >= rounds) break;
+    const int pl = r * ppr + pr;
+    float uf[32];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) nib8(kw[r][c], uf + 8 * c);
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      float acc = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) acc = fmaf(qv[hh][i], uf[i], acc);
+      acc = fmaf(-8.0f, qsum[hh], acc) * ksc[r];
+      acc += dpp_f32<0xB1>(acc);  // quad reduction over the four quarters
+      acc += dpp_f32<0x4E>(acc);
+      if (qd == 0 && pl < C) score[g * G + hh][pl] = pl < cnt ? acc * a.sm_scale : -INFINITY;
+    }
+  }
+  // The staged values go to LDS.
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    if (tid + 256 * r < units) vrow[tid + 256 * r] = vreg[r];
+  if (tid < C * Hkv) vscale[tid / Hkv][tid % Hkv] = vsc;
+  __syncthreads();
+
+  // Chunk softmax numerators: head h = tid / 8, 8 threads x 4 positions.
+  if (tid < Hq * 8) {
+    const int h = tid >> 3, j = tid & 7;
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < C / 8; ++i) m = fmaxf(m, score[h][j * (C / 8) + i]);
+    m = fmaxf(m, dpp_f32<0xB1>(m));
+    m = fmaxf(m, dpp_f32<0x4E>(m));
+    m = fmaxf(m, dpp_f32<0x141>(m));  // the other quad of the 8 lanes
+    float l = 0.0f;
+#pragma unroll
+    for (int i = 0; i < C / 8; ++i) {
+      const float e = __expf(score[h][j * (C / 8) + i] - m);
+      score[h][j * (C / 8) + i] = e;
+      l += e;
+    }
+    l += dpp_f32<0xB1>(l);
+    l += dpp_f32<0x4E>(l);
+    l += dpp_f32<0x141>(l);
+    if (j == 0) {
+      mh[h] = m;
+      lh[h] = l;
+    }
+  }
+  __syncthreads();
+
+  // Weighted sum of the values: thread (query head h, 16 elements dc);
+  // o = sum_p e_p s_p (u_p - 8) = sum_p w_p u_p - 8 sum_p w_p, w_p = e_p s_p.
+  if (tid < Hq * 8) {
+    const int h = tid >> 3, dc = tid & 7, gk = h / G;
+    float o[16], wsum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[i] = 0.0f;
+    const uint8_t *vb = reinterpret_cast<const uint8_t *>(vrow);
+#pragma unroll 4
+    for (int pl = 0; pl < C; ++pl) {
+      const float w = score[h][pl] * vscale[pl][gk];
+      const uint2 wd = *reinterpret_cast<const uint2 *>(vb + ((size_t)pl * Hkv + gk) * (D / 2) + 8 * dc);
+      float uf[16];
+      nib8(wd.x, uf);
+      nib8(wd.y, uf + 8);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[i] = fmaf(w, uf[i], o[i]);
+      wsum += w;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o[i] = fmaf(-8.0f, wsum, o[i]);
+    float *dst = a.part + (((size_t)t * Hq + h) * a.nchunks + chunk) * kPartStride;
+#pragma unroll
+    for (int i = 0; i < 16; i += 4) *reinterpret_cast<float4 *>(dst + 16 * dc + i) = float4{o[i], o[i + 1], o[i + 2], o[i + 3]};
+    if (dc == 0) {
+      dst[D] = mh[h];
+      dst[D + 1] = lh[h];
+    }
+  }
+}
+
+// out[t][h][d] = sum_c exp(m_c - M) o_c[d] / sum_c exp(m_c - M) l_c, chunks
+// in order.  256 threads: element d = tid % 128 of the chunks of parity
+// tid / 128, sixteen loads in flight at a time; the two halves are added in
+// a fixed order.  The chunk weights go through LDS.
+constexpr int kMergeMaxChunks = 2048;
+
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  constexpr int D = kKvD;
+  __shared__ float wc[kMergeMaxChunks];
+  __shared__ float red[256];
+  __shared__ float half_num[D], half_den[D];
+  const int th = blockIdx.x, tid = threadIdx.x;  // th = t * Hq + h
+  const int nc = a.nchunks;
+  const float *p = a.part + (size_t)th * nc * kPartStride;
+  float M = -INFINITY;
+  for (int c = tid; c < nc; c += 256) M = fmaxf(M, p[(size_t)c * kPartStride + D]);
+  red[tid] = M;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  M = red[0];
+  for (int c = tid; c < nc; c += 256) wc[c] = __expf(p[(size_t)c * kPartStride + D] - M);
+  __syncthreads();
+  const int d = tid & (D - 1), par = tid >> 7;
+  float num = 0.0f, den = 0.0f;
+  int c = par;
+  for (; c + 2 * 15 < nc; c += 2 * 16) {
+    float v[16], l[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      v[i] = p[(size_t)(c + 2 * i) * kPartStride + d];
+      l[i] = p[(size_t)(c + 2 * i) * kPartStride + D + 1];
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      num = fmaf(wc[c + 2 * i], v[i], num);
+      den = fmaf(wc[c + 2 * i], l[i], den);
+    }
+  }
+  for (; c < nc; c += 2) {
+    num = fmaf(wc[c], p[(size_t)c * kPartStride + d], num);
+    den = fmaf(wc[c], p[(size_t)c * kPartStride + D + 1], den);
+  }
+  if (par == 1) {
+    half_num[d] = num;
+    half_den[d] = den;
+  }
+  __syncthreads();
+  if (par == 0) a.out[(size_t)th * D + d] = (num + half_num[d]) / (den + half_den[d]);
+}
+
+}  // namespace
+
+bool kv_shape_supported(int Hkv, int D) { return D == kKvD && (Hkv == 1 || Hkv == 2 || Hkv == 4 || Hkv == 8); }
+
+hipError_t launch_kv_quantize(const uint16_t *x, int T, int Hkv, const int *slots, int L, uint8_t *codes,
+                              uint16_t *scale, hipStream_t s) {
+  const int rows = T * Hkv;
+  KernelTimer timer("kv_quantize", s);
+  kv_quantize_kernel<<<ceil_div(rows, 4 * kRowsPerWave), 256, 0, s>>>(reinterpret_cast<const uint32_t *>(x), rows, Hkv, slots, L,
+                                                       codes, scale);
+  return hipGetLastError();
+}
+
+size_t attn_workspace_bytes(int Tq, int Hq, int n_sel) {
+  const long long nchunks = (n_sel + kAttnChunk - 1) / kAttnChunk;
+  return (size_t)Tq * Hq * nchunks * kPartStride * sizeof(float);
+}
+
+hipError_t launch_sparse_attention(const uint16_t *q, int Tq, int Hq, const uint8_t *kc, const uint16_t *ks,
+                                   const uint8_t *vc, const uint16_t *vs, int L, int Hkv, const int *sel,
+                                   int n_sel, float sm_scale, float *out, void *ws, hipStream_t s) {
+  AttnArgs a{};
+  a.q = q;
+  a.kc = kc;
+  a.vc = vc;
+  a.ks = ks;
+  a.vs = vs;
+  a.sel = sel;
+  a.Tq = Tq;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.L = L;
+  a.n_sel = n_sel;
+  a.nchunks = ceil_div(n_sel, kAttnChunk);
+  a.sm_scale = sm_scale;
+  a.part = static_cast<float *>(ws);
+  a.out = out;
+  const int G = Hq / Hkv;
+  {
+    KernelTimer timer("attn_partial", s);
+    const dim3 grid((unsigned)(Tq * a.nchunks));
+    switch (G) {
+      case 1: attn_partial_kernel<1><<<grid, 256, 0, s>>>(a); break;
+      case 2: attn_partial_kernel<2><<<grid, 256, 0, s>>>(a); break;
+      default: attn_partial_kernel<4><<<grid, 256, 0, s>>>(a); break;
+    }
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  {
+    KernelTimer timer("attn_merge", s);
+    attn_merge_kernel<<<dim3((unsigned)(Tq * Hq)), 256, 0, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace strata

@@ -100,6 +100,16 @@ hipError_t launch_combine(const float *y, const int *inv_perm, const float *topk
 hipError_t launch_combine_pairs(const uint16_t *y16, const float *topk_w, int T, int k, int H, float *out,
                                 hipStream_t s);
 
+// 4-bit KV cache (kv.hip): per-head symmetric codes of key/value vectors and
+// attention of queries over selected cache rows.
+bool kv_shape_supported(int Hkv, int D);
+hipError_t launch_kv_quantize(const uint16_t *x, int T, int Hkv, const int *slots, int L, uint8_t *codes,
+                              uint16_t *scale, hipStream_t s);
+size_t attn_workspace_bytes(int Tq, int Hq, int n_sel);
+hipError_t launch_sparse_attention(const uint16_t *q, int Tq, int Hq, const uint8_t *kc, const uint16_t *ks,
+                                   const uint8_t *vc, const uint16_t *vs, int L, int Hkv, const int *sel,
+                                   int n_sel, float sm_scale, float *out, void *ws, hipStream_t s);
+
 inline int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 // ---------------------------------------------------------------- wavefront reductions

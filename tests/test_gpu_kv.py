@@ -1,0 +1,194 @@
+"""GPU parity of the 4-bit KV-cache codec and of sparse attention over it,
+through the C ABI, against the CPU oracle (oracle/kv.py).
+
+* strata_kv_quantize: codes and scales bit-exact (the code decision is taken
+  in fp32 on both sides), including zero vectors, round-half-even ties, huge
+  and tiny magnitudes, and out-of-range slots (skipped).
+* strata_sparse_attention: every output element against the fp64 oracle on
+  the oracle's own cache.  Tolerance: the kernel accumulates in fp32 (dot
+  products of 128 terms, softmax sums and weighted sums of up to a few
+  thousand terms, exp via the hardware exponential), so its error is a few
+  fp32 ulps of the largest partial sums; the bound used, max |err| <= 1e-4
+  RMS(out) and sum |err| / sum |out| <= 1e-5, is well above that and far
+  below any indexing or weighting mistake.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+ATOL_RMS = 1e-4
+L1_REL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def qe(gpu_available):
+    import quantized_expert_ffn_histogram_amd as qe
+
+    qe.load()
+    return qe
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _dev_bf16(bits):
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+def _gpu_cache(qe, x_bf16, fill=0x5A):
+    """Quantize [L, Hkv, D] into a fresh cache (slots 0..L-1) on the GPU."""
+    import torch
+
+    L, Hkv, D = x_bf16.shape
+    codes = torch.full((L, Hkv, D // 2), fill, dtype=torch.uint8, device="cuda")
+    scales = torch.zeros((L, Hkv), dtype=torch.float16, device="cuda")
+    slots = torch.arange(L, dtype=torch.int32, device="cuda")
+    qe.kv_quantize(_dev_bf16(x_bf16), slots, codes, scales)
+    return codes, scales
+
+
+def _check_codes(codes, scales, x_bf16, what):
+    rp, rs = oracle.kv_quantize(x_bf16)
+    got_p, got_s = _np(codes), _np(scales)
+    assert (got_p == rp).all(), f"{what}: codes differ in {(got_p != rp).sum()} bytes"
+    assert (got_s.view(np.uint16) == rs.view(np.uint16)).all(), f"{what}: scales differ"
+
+
+def _edge_vectors(D=128):
+    f = np.zeros((10, D), np.float32)
+    f[1] = 3.5  # ties: every value lands on x / s = 7 after s = 0.5 ... and
+    f[1, ::2] = 0.25  # 0.25 / 0.5 = 0.5 rounds half to even -> 0
+    f[2] = np.linspace(-7, 7, D)
+    f[3] = 4e5 * np.sign(np.linspace(-1, 1, D) + 1e-3)  # near the largest finite scale (7 * 65504)
+    f[4] = np.linspace(-1, 1, D) * 1e-36
+    f[5] = -2.0
+    f[5, 7] = -14.0  # negative maximum
+    f[6, 3] = 5.0  # one non-zero element
+    f[7] = np.tile([2.5, -2.5, 1.5, -1.5], D // 4) / 7 * 2.5  # halfway codes
+    f[8] = np.random.default_rng(3).standard_normal(D) * 100
+    f[9] = 65504.0
+    return synth.bf16_bits_from_f32(f)
+
+
+def test_kv_quantize_bitexact(qe):
+    inp = synth.make_attn_inputs("attn_small")
+    codes, scales = _gpu_cache(qe, inp.k_bf16)
+    _check_codes(codes, scales, inp.k_bf16, "attn_small keys")
+    edge = _edge_vectors().reshape(5, 2, 128)  # 5 tokens x 2 heads
+    codes, scales = _gpu_cache(qe, edge)
+    _check_codes(codes, scales, edge, "edge vectors")
+
+
+def test_kv_quantize_slots_and_skips(qe):
+    """Tokens land on their slots; slots outside [0, L) are skipped and leave
+    the cache untouched."""
+    import torch
+
+    rng = np.random.default_rng(11)
+    L, Hkv, D, T = 50, 4, 128, 12
+    x = synth.bf16_bits_from_f32(rng.standard_normal((T, Hkv, D)).astype(np.float32))
+    slots = np.array([7, 3, 49, 0, -1, 50, 12, 31, 8, 1000, 22, 44], np.int32)
+    codes = torch.full((L, Hkv, D // 2), 0x5A, dtype=torch.uint8, device="cuda")
+    scales = torch.full((L, Hkv), 1.5, dtype=torch.float16, device="cuda")
+    qe.kv_quantize(_dev_bf16(x), torch.from_numpy(slots).cuda(), codes, scales)
+    rp, rs = oracle.kv_quantize(x)
+    got_p, got_s = _np(codes), _np(scales)
+    written = set()
+    for t, s in enumerate(slots):
+        if 0 <= s < L:
+            assert (got_p[s] == rp[t]).all() and (got_s[s] == rs[t]).all(), t
+            written.add(int(s))
+    for s in set(range(L)) - written:
+        assert (got_p[s] == 0x5A).all() and (got_s[s] == np.float16(1.5)).all(), s
+
+
+def _check_attn(got, ref, what):
+    err = np.abs(got.astype(np.float64) - ref)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    stats = dict(max_err_over_rms=float(err.max() / rms), l1=float(err.sum() / np.abs(ref).sum()))
+    assert np.isfinite(got).all(), what
+    assert err.max() <= ATOL_RMS * rms and stats["l1"] <= L1_REL, f"{what}: {stats}"
+    return stats
+
+
+def _attn_case(qe, cfg, use_sel=True):
+    import torch
+
+    inp = synth.make_attn_inputs(cfg)
+    cfg = inp.cfg
+    kc, ks = _gpu_cache(qe, inp.k_bf16)
+    vc, vs = _gpu_cache(qe, inp.v_bf16)
+    kp, kss = oracle.kv_quantize(inp.k_bf16)
+    vp, vss = oracle.kv_quantize(inp.v_bf16)
+    sel = inp.sel if use_sel else np.tile(np.arange(cfg.n_sel, dtype=np.int32), (cfg.Tq, 1))
+    ref = oracle.sparse_attention(inp.q_bf16, kp, kss, vp, vss, sel, cfg.sm_scale)
+    sel_d = torch.from_numpy(np.ascontiguousarray(inp.sel)).cuda() if use_sel else None
+    out = qe.sparse_attention(_dev_bf16(inp.q_bf16), kc, ks, vc, vs, sel_d, cfg.sm_scale, n_sel=cfg.n_sel)
+    torch.cuda.synchronize()
+    return _np(out), ref, (kc, ks, vc, vs, sel_d, inp)
+
+
+@pytest.mark.parametrize(
+    "overrides",
+    [
+        dict(),                                        # Tq 3, 32 heads over 8, 300 selected (10 chunks, ragged)
+        dict(n_sel=1, Tq=2),                           # a single row
+        dict(n_sel=33, Tq=5),                          # two chunks, the last of one position
+        dict(Hkv=4, Hq=16, n_sel=100),                 # GQA 4:1 over 4 KV heads
+        dict(Hkv=2, Hq=4, n_sel=64),                   # 2:1
+        dict(Hkv=1, Hq=1, n_sel=257, L=300),           # one head, 9 chunks
+        dict(Hkv=8, Hq=8, n_sel=77),                   # one query head per KV head
+    ],
+    ids=lambda d: "-".join(f"{k}{v}" for k, v in d.items()) or "default",
+)
+def test_sparse_attention_small(qe, overrides):
+    cfg = synth.attn_config("attn_small", **overrides)
+    got, ref, _ = _attn_case(qe, cfg)
+    _check_attn(got, ref, str(overrides))
+
+
+def test_sparse_attention_dense_prefix_and_repeatable(qe):
+    """sel = NULL reads positions 0 .. n_sel-1; repeated calls are bitwise equal."""
+    import torch
+
+    cfg = synth.attn_config("attn_small", n_sel=100)
+    got, ref, (kc, ks, vc, vs, _, inp) = _attn_case(qe, cfg, use_sel=False)
+    _check_attn(got, ref, "dense prefix")
+    q = _dev_bf16(inp.q_bf16)
+    a = qe.sparse_attention(q, kc, ks, vc, vs, None, cfg.sm_scale, n_sel=cfg.n_sel)
+    b = qe.sparse_attention(q, kc, ks, vc, vs, None, cfg.sm_scale, n_sel=cfg.n_sel)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["attn_decode128k", "attn_chunk16"])
+def test_sparse_attention_full_size(qe, name):
+    """The pages' shape: a 128k-position cache (8 KV heads, head_dim 128),
+    2048 selected positions per query, 32 query heads; the whole cache is
+    quantized on the GPU and compared bit-exactly, then every output element."""
+    import torch
+
+    cfg = synth.attn_config(name)
+    inp = synth.make_attn_inputs(cfg)
+    print(f"[kv] {name}: L={cfg.L} Hkv={cfg.Hkv} Tq={cfg.Tq} n_sel={cfg.n_sel}", flush=True)
+    kc, ks = _gpu_cache(qe, inp.k_bf16)
+    vc, vs = _gpu_cache(qe, inp.v_bf16)
+    _check_codes(kc, ks, inp.k_bf16, "keys")
+    _check_codes(vc, vs, inp.v_bf16, "values")
+    # The oracle works on the selected rows only (quantization is per row).
+    rows = np.unique(inp.sel)
+    remap = np.zeros(cfg.L, np.int64)
+    remap[rows] = np.arange(len(rows))
+    kp, kss = oracle.kv_quantize(inp.k_bf16[rows])
+    vp, vss = oracle.kv_quantize(inp.v_bf16[rows])
+    ref = oracle.sparse_attention(inp.q_bf16, kp, kss, vp, vss, remap[inp.sel], cfg.sm_scale)
+    out = qe.sparse_attention(_dev_bf16(inp.q_bf16), kc, ks, vc, vs, torch.from_numpy(inp.sel).cuda(), cfg.sm_scale)
+    torch.cuda.synchronize()
+    print(f"[kv] {name}: {_check_attn(_np(out), ref, name)}", flush=True)
