@@ -133,14 +133,42 @@ def unpack_int4(packed: np.ndarray) -> np.ndarray:
     return out
 
 
-def dequant(packed: np.ndarray, scales: np.ndarray, g: int) -> np.ndarray:
+def dequant(packed: np.ndarray, scales: np.ndarray, g: int, zeros: np.ndarray | None = None,
+            hi: np.ndarray | None = None) -> np.ndarray:
     """Group dequantization ``W[n, kk] = q[n, kk] * s[n, kk // g]`` in float64 (exact).
 
     Per-group scales: yfxerp.com static review §3.1; lqnn.cn static review §3.1.
+    The code q of element kk comes from its nibble u (``unpack_int4`` gives
+    u - 8) in one of three formats:
+
+    * symmetric 4-bit (default): ``q = u - 8``;
+    * asymmetric 4-bit, one zero point per group (each group stores a scale and
+      a zero point: lqnn.cn static review, §3.1): ``q = u - z[n, kk // g]``,
+      zero points packed two per byte (group j in byte j // 2, even j in the
+      low nibble);
+    * symmetric 5-bit blocks (4- and 5-bit block quantization, kongchang.com
+      hands-on, MMQ note): ``q = u + 16 * b - 16`` where the fifth bit b of
+      element kk = 32m + 8c + i is bit 4i + c of the 32-bit word hi[n, m].
     """
-    q = unpack_int4(packed).astype(np.float64)
+    u = unpack_int4(packed).astype(np.int64) + 8
+    if hi is not None:
+        words = np.asarray(hi, dtype=np.uint32).astype(np.int64)
+        K = u.shape[-1]
+        kk = np.arange(K)
+        m, c, i = kk // 32, (kk % 32) // 8, kk % 8
+        bit = (words[..., m] >> (4 * i + c)) & 1
+        q = u + 16 * bit - 16
+    elif zeros is not None:
+        zb = np.asarray(zeros, dtype=np.uint8)
+        z = np.empty(zb.shape[:-1] + (zb.shape[-1] * 2,), dtype=np.int64)
+        z[..., 0::2] = zb & 0x0F
+        z[..., 1::2] = zb >> 4
+        ngr = u.shape[-1] // g
+        q = u - np.repeat(z[..., :ngr], g, axis=-1)
+    else:
+        q = u - 8
     s = np.asarray(scales, dtype=np.float16).astype(np.float64)
-    return q * np.repeat(s, g, axis=-1)
+    return q.astype(np.float64) * np.repeat(s, g, axis=-1)
 
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
@@ -162,11 +190,18 @@ def expert_ffn(X: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray) ->
 
 
 def _expert_mats(weights: dict, e: int, g: int):
-    return (
-        dequant(weights["gate"][e], weights["gate_scale"][e], g),
-        dequant(weights["up"][e], weights["up_scale"][e], g),
-        dequant(weights["down"][e], weights["down_scale"][e], g),
-    )
+    """Expert e's gate, up and down matrices.  The format follows from the
+    arrays present: per-group zero points ("<name>_zero": asymmetric 4-bit),
+    fifth-bit words ("<name>_hi": 5-bit), neither (symmetric 4-bit)."""
+
+    def one(name):
+        zeros = weights.get(name + "_zero")
+        zeros = None if zeros is None else zeros[e]
+        hi = weights.get(name + "_hi")
+        hi = None if hi is None else hi[e]
+        return dequant(weights[name][e], weights[name + "_scale"][e], g, zeros=zeros, hi=hi)
+
+    return one("gate"), one("up"), one("down")
 
 
 def ffn_grouped(x_bf16, weights: dict, offsets, perm, k: int, g: int) -> np.ndarray:

@@ -11,7 +11,10 @@ from .gen import (  # noqa: F401
     make_logits,
     make_router,
     make_x,
+    quantize_groups,
+    quantize_int4_asym_groups,
     quantize_int4_groups,
+    quantize_int5_groups,
     weight_bytes_per_expert,
 )
 from .kv import ATTN_CONFIGS, AttnConfig, AttnInputs, attn_config, make_attn_inputs  # noqa: F401

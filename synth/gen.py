@@ -50,7 +50,8 @@ class MoEConfig:
     per-expert bias ``-zipf_s * ln(rank_e)`` over a seeded rank permutation,
     so that expert popularity follows a Zipf law of exponent ``zipf_s``.
     ``weight_std`` is the standard deviation of the expert weights before
-    quantization (0.02 for every workload configuration).
+    quantization (0.02 for every workload configuration).  ``fmt`` names the
+    weight format (see ``quantize_groups``).
     """
 
     name: str
@@ -63,6 +64,7 @@ class MoEConfig:
     seed: int
     zipf_s: float | None = None
     weight_std: float = WEIGHT_STD
+    fmt: str = "int4"  # "int4" (symmetric), "int4_asym" (scale + zero point), "int5" (symmetric 5-bit)
 
     @property
     def pairs(self) -> int:
@@ -83,6 +85,13 @@ CONFIGS: dict[str, MoEConfig] = {
     # the 6144-token chunk with the other two group sizes the pages name
     "prefill6144_g32": MoEConfig("prefill6144_g32", T=6144, H=2048, I=512, E=512, k=10, g=32, seed=5),
     "prefill6144_g128": MoEConfig("prefill6144_g128", T=6144, H=2048, I=512, E=512, k=10, g=128, seed=6),
+    # the 6144-token chunk in the two other weight formats the pages name
+    "prefill6144_asym": MoEConfig("prefill6144_asym", T=6144, H=2048, I=512, E=512, k=10, g=64, seed=7,
+                                  fmt="int4_asym"),
+    "prefill6144_int5": MoEConfig("prefill6144_int5", T=6144, H=2048, I=512, E=512, k=10, g=64, seed=8, fmt="int5"),
+    # a decode step in those formats
+    "decode_asym": MoEConfig("decode_asym", T=4, H=2048, I=512, E=512, k=10, g=64, seed=9, fmt="int4_asym"),
+    "decode_int5": MoEConfig("decode_int5", T=4, H=2048, I=512, E=512, k=10, g=64, seed=10, fmt="int5"),
 }
 
 
@@ -92,9 +101,12 @@ def config(name_or_cfg, **overrides) -> MoEConfig:
 
 
 def weight_bytes_per_expert(cfg: MoEConfig) -> int:
-    """Packed bytes of one expert's three matrices plus their fp16 scales."""
+    """Packed bytes of one expert's three matrices plus their side data:
+    fp16 scales (all formats), 4-bit zero points (int4_asym), one fifth bit
+    per weight (int5)."""
     n = 3 * cfg.H * cfg.I
-    return n // 2 + 2 * (n // cfg.g)
+    extra = {"int4": 0, "int4_asym": n // cfg.g // 2, "int5": n // 8}[cfg.fmt]
+    return n // 2 + 2 * (n // cfg.g) + extra
 
 
 @dataclass
@@ -134,6 +146,78 @@ def quantize_int4_groups(w: np.ndarray, g: int) -> tuple[np.ndarray, np.ndarray]
     return packed, s16
 
 
+def quantize_int4_asym_groups(w: np.ndarray, g: int) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Asymmetric 4-bit group quantization of ``w[N, K]`` along K (each group
+    stores a scale and a zero point).
+
+    The group's range is widened to contain 0 (lo = min(min w, 0), hi =
+    max(max w, 0)); ``s = fp16(fp32(hi - lo) / 15)``, ``z = clamp(rint(-lo / s),
+    0, 15)``, ``u = clamp(rint(w / s) + z, 0, 15)`` (all 0 where s = 0), so
+    ``w ~ (u - z) * s``.  Returns ``(packed uint8 [N, K/2], scales float16
+    [N, K/g], zeros uint8 [N, K/g/2])`` with u as offset-binary nibbles (even
+    K in the low nibble) and the zero points two per byte (group j in byte
+    j // 2, even j in the low nibble).
+    """
+    n, kdim = w.shape
+    if kdim % g or (kdim // g) % 2:
+        raise ValueError(f"K={kdim} must hold an even number of groups of g={g}")
+    grp = np.asarray(w, dtype=np.float32).reshape(n, kdim // g, g)
+    lo = np.minimum(grp.min(axis=2), np.float32(0))
+    hi = np.maximum(grp.max(axis=2), np.float32(0))
+    s16 = ((hi - lo) / np.float32(15.0)).astype(np.float16)
+    s = s16.astype(np.float64)
+    safe = np.where(s > 0, s, 1.0)
+    z = np.where(s > 0, np.clip(np.rint(-lo.astype(np.float64) / safe), 0, 15), 0).astype(np.int16)
+    r = np.where(s[..., None] > 0, grp.astype(np.float64) / safe[..., None], 0.0)
+    u = np.where(s[..., None] > 0, np.clip(np.rint(r) + z[..., None], 0, 15), 0).astype(np.uint8).reshape(n, kdim)
+    packed = (u[:, 0::2] | (u[:, 1::2] << np.uint8(4))).astype(np.uint8)
+    zb = z.astype(np.uint8)
+    zeros = (zb[:, 0::2] | (zb[:, 1::2] << np.uint8(4))).astype(np.uint8)
+    return packed, s16, zeros
+
+
+def quantize_int5_groups(w: np.ndarray, g: int) -> tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Symmetric 5-bit group quantization of ``w[N, K]`` along K.
+
+    ``s = fp16(fp32(max|w|) / 15)``, ``q = clamp(rint(w / s), -16, 15)`` (0 where
+    s = 0), ``u5 = q + 16``.  Returns ``(packed uint8 [N, K/2], scales float16
+    [N, K/g], hi uint32 [N, K/32])``: the low four bits of u5 as offset-binary
+    nibbles (even K in the low nibble) and the fifth bits in one 32-bit word
+    per 32 K values, the fifth bit of K = 32m + 8c + i at bit 4i + c of word m.
+    """
+    n, kdim = w.shape
+    if kdim % g or kdim % 32:
+        raise ValueError(f"K={kdim} must be a multiple of g={g} and of 32")
+    grp = np.asarray(w, dtype=np.float32).reshape(n, kdim // g, g)
+    amax = np.abs(grp).max(axis=2)
+    s16 = (amax / np.float32(15.0)).astype(np.float16)
+    s = s16.astype(np.float64)[..., None]
+    safe = np.where(s > 0, s, 1.0)
+    q = np.where(s > 0, np.clip(np.rint(grp.astype(np.float64) / safe), -16, 15), 0).astype(np.int16)
+    u5 = (q + 16).reshape(n, kdim)
+    u = (u5 & 15).astype(np.uint8)
+    packed = (u[:, 0::2] | (u[:, 1::2] << np.uint8(4))).astype(np.uint8)
+    b = (u5 >> 4).astype(np.uint32).reshape(n, kdim // 32, 4, 8)  # [n, m, c, i]
+    shifts = (4 * np.arange(8)[None, :] + np.arange(4)[:, None]).astype(np.uint32)  # [c, i] -> 4i + c
+    hi = (b << shifts[None, None]).sum(axis=(2, 3), dtype=np.uint64).astype(np.uint32)
+    return packed, s16, hi
+
+
+def quantize_groups(w: np.ndarray, g: int, fmt: str) -> dict:
+    """Quantize ``w[N, K]`` in format ``fmt``; returns the arrays by suffix:
+    "" (packed nibbles), "_scale", and "_zero" (int4_asym) or "_hi" (int5)."""
+    if fmt == "int4":
+        p, sc = quantize_int4_groups(w, g)
+        return {"": p, "_scale": sc}
+    if fmt == "int4_asym":
+        p, sc, z = quantize_int4_asym_groups(w, g)
+        return {"": p, "_scale": sc, "_zero": z}
+    if fmt == "int5":
+        p, sc, hi = quantize_int5_groups(w, g)
+        return {"": p, "_scale": sc, "_hi": hi}
+    raise ValueError(f"unknown weight format {fmt!r}")
+
+
 def _streams(seed: int):
     root = np.random.SeedSequence(seed)
     return root.spawn(4)  # logits, x, zipf ranks, weights
@@ -170,9 +254,8 @@ def _expert_weights(cfg: MoEConfig, seq, e: int, out: dict) -> None:
     std = np.float32(cfg.weight_std)
     for name, (n, kdim) in (("gate", (cfg.I, cfg.H)), ("up", (cfg.I, cfg.H)), ("down", (cfg.H, cfg.I))):
         w = rng.standard_normal((n, kdim), dtype=np.float32) * std
-        packed, scales = quantize_int4_groups(w, cfg.g)
-        out[name][e] = packed
-        out[name + "_scale"][e] = scales
+        for suffix, arr in quantize_groups(w, cfg.g, cfg.fmt).items():
+            out[name + suffix][e] = arr
 
 
 def make_weights(cfg: MoEConfig, seq: np.random.SeedSequence, threads: int | None = None) -> dict:
@@ -185,6 +268,11 @@ def make_weights(cfg: MoEConfig, seq: np.random.SeedSequence, threads: int | Non
         "down": np.empty((E, H, I // 2), np.uint8),
         "down_scale": np.empty((E, H, I // g), np.float16),
     }
+    for name, (n, kdim) in (("gate", (I, H)), ("up", (I, H)), ("down", (H, I))):
+        if cfg.fmt == "int4_asym":
+            out[name + "_zero"] = np.empty((E, n, kdim // g // 2), np.uint8)
+        elif cfg.fmt == "int5":
+            out[name + "_hi"] = np.empty((E, n, kdim // 32), np.uint32)
     kids = seq.spawn(E)
     threads = threads or min(16, os.cpu_count() or 1)
     if threads <= 1 or E == 1:

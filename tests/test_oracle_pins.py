@@ -394,3 +394,132 @@ def test_grouped_rows_are_per_pair_expert_outputs():
         one = oracle.moe_out_tokens([p // cfg.k], r["ids"][:, :], np.eye(cfg.k)[None].repeat(cfg.T, 0)[:, p % cfg.k],
                                     inp.x_bf16, inp.weights, cfg.g)
         np.testing.assert_allclose(r["y"][lo], one[0], rtol=1e-12, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------- other weight formats
+def test_asym_dequant_hand_decoded():
+    # u = 1, 2 | 0, 15; zero points 3 (group 0), 5 (group 1); scales 0.5, 2.
+    packed = np.array([[0x21, 0xF0]], np.uint8)
+    zeros = np.array([[0x53]], np.uint8)
+    scales = np.array([[0.5, 2.0]], np.float16)
+    W = oracle.dequant(packed, scales, 2, zeros=zeros)
+    assert W.tolist() == [[-1.0, -0.5, -10.0, 20.0]]
+
+
+def test_int5_dequant_hand_decoded():
+    # all nibbles 0; fifth bits set for elements 19 (= 8*2 + 3: bit 4*3 + 2)
+    # and 15 (= 8*1 + 7: bit 4*7 + 1), so q = -16 except q[19] = q[15] = 0.
+    packed = np.zeros((1, 16), np.uint8)
+    hi = np.array([[(1 << 14) | (1 << 29)]], np.uint32)
+    W = oracle.dequant(packed, np.array([[1.0]], np.float16), 32, hi=hi)
+    want = [-16.0] * 32
+    want[19] = want[15] = 0.0
+    assert W.tolist() == [want]
+
+
+def test_other_formats_match_elementwise_definition():
+    rng = np.random.default_rng(14)
+    N, K, g = 3, 64, 16
+    packed = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    scales = rng.uniform(0.001, 0.05, (N, K // g)).astype(np.float16)
+    zeros = rng.integers(0, 256, (N, K // g // 2), dtype=np.uint8)
+    hi = rng.integers(0, 2**32, (N, K // 32), dtype=np.uint64).astype(np.uint32)
+    Wa = oracle.dequant(packed, scales, g, zeros=zeros)
+    W5 = oracle.dequant(packed, scales, g, hi=hi)
+    for n in range(N):
+        for kk in range(K):
+            byte = int(packed[n, kk >> 1])
+            u = (byte >> 4) if kk & 1 else (byte & 15)
+            grp = kk // g
+            zbyte = int(zeros[n, grp >> 1])
+            z = (zbyte >> 4) if grp & 1 else (zbyte & 15)
+            s = float(scales[n, grp])
+            assert Wa[n, kk] == (u - z) * s
+            word = int(hi[n, kk // 32])
+            c, i = (kk % 32) // 8, kk % 8
+            b = (word >> (4 * i + c)) & 1
+            assert W5[n, kk] == (u + 16 * b - 16) * s
+
+
+def test_asym_quantizer_bounds():
+    rng = np.random.default_rng(15)
+    w = (rng.standard_normal((6, 128)) * 0.02).astype(np.float32)
+    w[1, :32] = np.abs(w[1, :32]) + 0.01   # an all-positive group
+    w[2, 64:96] = 0.0                      # an all-zero group
+    w[3, 32:64] = -0.03                    # a constant negative group
+    packed, s, zeros = synth.quantize_int4_asym_groups(w, 32)
+    W = oracle.dequant(packed, s, 32, zeros=zeros).reshape(6, 4, 32)
+    sf = s.astype(np.float64)[..., None]
+    err = np.abs(w.astype(np.float64).reshape(6, 4, 32) - W)
+    assert (err <= sf * (1 + 2.0**-9) + 1e-30).all()
+    assert s[2, 2] == 0 and (W[2, 2] == 0).all()
+    assert np.abs(W[3, 1] + 0.03).max() <= float(s[3, 1]) / 2 + 1e-9
+
+
+def test_int5_quantizer_bounds():
+    rng = np.random.default_rng(16)
+    w = (rng.standard_normal((6, 128)) * 0.02).astype(np.float32)
+    w[4, :64] = 0.0
+    packed, s, hi = synth.quantize_int5_groups(w, 64)
+    W = oracle.dequant(packed, s, 64, hi=hi).reshape(6, 2, 64)
+    sf = s.astype(np.float64)[..., None]
+    err = np.abs(w.astype(np.float64).reshape(6, 2, 64) - W)
+    assert (err <= sf / 2 * (1 + 2.0**-10) + 1e-30).all()
+    q = np.rint(np.where(sf > 0, W / np.where(sf > 0, sf, 1), 0))
+    nz = sf[..., 0] > 0
+    assert (np.abs(q).max(axis=2)[nz] >= 15).all()
+    assert s[4, 0] == 0 and (W[4, 0] == 0).all()
+
+
+def test_asym_model_bytes_match_page_figure():
+    """The lqnn.cn review §3.1: 4-bit weights with a scale and a zero point per
+    group come to 2.2-2.4 GB for 4B parameters (10-20 % over 0.5 byte per
+    parameter): fp16 scale + 4-bit zero point per 32 weights."""
+    fx = json.load(open(os.path.join(GOLDEN, "int4_model_bytes.json")))
+    n = fx["params"]
+    total = n // 2 + n // 32 * 2 + n // 32 // 2
+    assert fx["low_bytes"] <= total <= fx["high_bytes"]
+    assert 0.10 <= (total - n / 2) / (n / 2) <= 0.20
+
+
+@pytest.mark.parametrize("fmt", ["int4_asym", "int5"])
+def test_layer_matches_bruteforce_dense_other_formats(fmt):
+    inp = synth.make_inputs(_tiny_cfg(H=64, I=32, g=16, fmt=fmt, seed=25))
+    cfg = inp.cfg
+    Wt = inp.weights
+
+    def deq(name, e):
+        packed, sc = Wt[name][e], Wt[name + "_scale"][e]
+        n, half = packed.shape
+        out = [[0.0] * (2 * half) for _ in range(n)]
+        for r in range(n):
+            for kk in range(2 * half):
+                b = int(packed[r, kk // 2])
+                u = (b >> 4) if kk % 2 else (b & 15)
+                grp = kk // cfg.g
+                if fmt == "int4_asym":
+                    zb = int(Wt[name + "_zero"][e][r, grp // 2])
+                    q = u - ((zb >> 4) if grp % 2 else (zb & 15))
+                else:
+                    word = int(Wt[name + "_hi"][e][r, kk // 32])
+                    q = u + 16 * ((word >> (4 * (kk % 8) + (kk % 32) // 8)) & 1) - 16
+                out[r][kk] = q * float(sc[r, grp])
+        return out
+
+    mats = [(deq("gate", e), deq("up", e), deq("down", e)) for e in range(cfg.E)]
+    xs = [[float(np.uint32(int(b) << 16).view(np.float32)) for b in row] for row in inp.x_bf16]
+    ref = np.zeros((cfg.T, cfg.H))
+    for t in range(cfg.T):
+        chosen = _bruteforce_topk(inp.logits[t], cfg.k)
+        wts = _bruteforce_softmax([float(inp.logits[t, e]) for e in chosen])
+        for e, wv in zip(chosen, wts):
+            Wg, Wu, Wd = mats[e]
+            h = []
+            for i in range(cfg.I):
+                gs = sum(Wg[i][c] * xs[t][c] for c in range(cfg.H))
+                us = sum(Wu[i][c] * xs[t][c] for c in range(cfg.H))
+                h.append(gs / (1.0 + math.exp(-gs)) * us)
+            for n_ in range(cfg.H):
+                ref[t, n_] += wv * sum(Wd[n_][i] * h[i] for i in range(cfg.I))
+    got = oracle.moe_layer(inp.logits, inp.x_bf16, Wt, cfg.k, cfg.g)["out"]
+    assert np.abs(got - ref).max() <= 1e-12 * np.abs(ref).max()
