@@ -57,13 +57,39 @@ typedef enum {
 } strata_status;
 
 /*
- * Group-quantized int4 expert weights (all device pointers, caller-owned).
+ * Weight formats of strata_moe_weights.format.
+ *   STRATA_W_INT4       symmetric 4-bit codes, q = u - 8.
+ *   STRATA_W_INT4_ASYM  asymmetric 4-bit: each group stores a scale and a zero
+ *                       point z in [0, 15], q = u - z (lqnn.cn static review,
+ *                       §3.1: per-group scale and zero point).
+ *   STRATA_W_INT5       symmetric 5-bit blocks, q = u + 16 b - 16 in [-16, 15]
+ *                       with a fifth bit b per element (4- and 5-bit block
+ *                       quantization: kongchang.com hands-on, section
+ *                       "Strata快在哪：不是魔法，是物流", MMQ note).
+ */
+typedef enum {
+  STRATA_W_INT4 = 0,
+  STRATA_W_INT4_ASYM = 1,
+  STRATA_W_INT5 = 2
+} strata_weight_format;
+
+/*
+ * Group-quantized expert weights (all device pointers, caller-owned).
  *
  * Each matrix W[N][K] (gate, up: N = I, K = H; down: N = H, K = I) holds
- * symmetric 4-bit codes q in [-8, 7], K-contiguous rows, two codes per byte:
- * byte j of a row = u(2j) | u(2j+1) << 4 with offset-binary nibble u = q + 8
+ * codes q, K-contiguous rows, one nibble u (the code's low 4 bits, offset
+ * binary) per element and two per byte: byte j of a row = u(2j) | u(2j+1) << 4
  * (even K index in the low nibble).  One IEEE fp16 scale per g consecutive K
- * elements: W[n][kk] = q[n][kk] * scale[n][kk / g].
+ * elements: W[n][kk] = q[n][kk] * scale[n][kk / g], where q follows `format`:
+ *   STRATA_W_INT4       q = u - 8.  gate_zero .. down_hi must be NULL.
+ *   STRATA_W_INT4_ASYM  q = u - z[n][kk / g]; the zero points of a row are
+ *                       packed two per byte (group j in byte j / 2, even j in
+ *                       the low nibble): gate_zero, up_zero [E][I][H/g/2],
+ *                       down_zero [E][H][I/g/2].  H/g and I/g must be even.
+ *   STRATA_W_INT5       q = u + 16 b - 16; the fifth bit b of element
+ *                       kk = 32m + 8c + i (c in 0..3, i in 0..7) is bit
+ *                       4i + c of the 32-bit word hi[n][m]: gate_hi, up_hi
+ *                       [E][I][H/32], down_hi [E][H][I/32] (4-byte aligned).
  * (Grouped 4-bit weights with per-group scales: lqnn.cn static review §3.1,
  * group sizes 32/64/128; yfxerp.com static review §3.1.)
  */
@@ -78,6 +104,13 @@ typedef struct {
   int32_t hidden;             /* H */
   int32_t inter;              /* I */
   int32_t group;              /* g */
+  int32_t format;             /* strata_weight_format; 0 (zero-initialised) = STRATA_W_INT4 */
+  const uint8_t *gate_zero;   /* STRATA_W_INT4_ASYM only, else NULL */
+  const uint8_t *up_zero;
+  const uint8_t *down_zero;
+  const uint32_t *gate_hi;    /* STRATA_W_INT5 only, else NULL */
+  const uint32_t *up_hi;
+  const uint32_t *down_hi;
 } strata_moe_weights;
 
 /*

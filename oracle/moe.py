@@ -152,12 +152,12 @@ def dequant(packed: np.ndarray, scales: np.ndarray, g: int, zeros: np.ndarray | 
     """
     u = unpack_int4(packed).astype(np.int64) + 8
     if hi is not None:
-        words = np.asarray(hi, dtype=np.uint32).astype(np.int64)
-        K = u.shape[-1]
-        kk = np.arange(K)
-        m, c, i = kk // 32, (kk % 32) // 8, kk % 8
-        bit = (words[..., m] >> (4 * i + c)) & 1
-        q = u + 16 * bit - 16
+        words = np.asarray(hi, dtype=np.uint32)
+        kk = np.arange(u.shape[-1])
+        c, i = (kk % 32) // 8, kk % 8
+        # word m = kk // 32 of the row, repeated over its 32 elements
+        bit = (np.repeat(words, 32, axis=-1) >> (4 * i + c).astype(np.uint32)) & np.uint32(1)
+        q = u + 16 * bit.astype(np.int64) - 16
     elif zeros is not None:
         zb = np.asarray(zeros, dtype=np.uint8)
         z = np.empty(zb.shape[:-1] + (zb.shape[-1] * 2,), dtype=np.int64)

@@ -15,6 +15,7 @@ from __future__ import annotations
 import ctypes
 from dataclasses import dataclass
 
+import numpy as np
 import torch
 
 from ._abi import LIB_PATH, StrataError, StrataMoeWeights, check, load  # noqa: F401
@@ -62,10 +63,13 @@ def _need(t: torch.Tensor, dtype, name: str) -> None:
 
 @dataclass
 class QuantizedExperts:
-    """Group-quantized int4 expert weights resident on the GPU.
+    """Group-quantized expert weights resident on the GPU.
 
     gate, up: uint8 [E, I, H/2]; down: uint8 [E, H, I/2]; *_scale: float16
-    [E, N, K/g].  Nibble u = q + 8, even K in the low nibble.
+    [E, N, K/g].  Nibble u (the code's low 4 bits), even K in the low nibble.
+    ``fmt`` (``strata_weight_format``): "int4" (q = u - 8), "int4_asym"
+    (q = u - z, zero points ``*_zero`` uint8 [E, N, K/g/2], two per byte) or
+    "int5" (q = u + 16 b - 16, fifth-bit words ``*_hi`` int32 [E, N, K/32]).
     """
 
     gate: torch.Tensor
@@ -75,6 +79,15 @@ class QuantizedExperts:
     down: torch.Tensor
     down_scale: torch.Tensor
     group: int
+    fmt: str = "int4"
+    gate_zero: torch.Tensor | None = None
+    up_zero: torch.Tensor | None = None
+    down_zero: torch.Tensor | None = None
+    gate_hi: torch.Tensor | None = None
+    up_hi: torch.Tensor | None = None
+    down_hi: torch.Tensor | None = None
+
+    FORMATS = {"int4": 0, "int4_asym": 1, "int5": 2}
 
     @property
     def num_experts(self) -> int:
@@ -90,24 +103,41 @@ class QuantizedExperts:
 
     @classmethod
     def from_numpy(cls, w: dict, group: int, device="cuda") -> "QuantizedExperts":
-        def u8(a):
+        """From host arrays by name: gate, gate_scale, ... and, for the other
+        formats, gate_zero, ... (uint8) or gate_hi, ... (uint32 words)."""
+
+        def dev(a):
+            a = np.ascontiguousarray(a)
+            if a.dtype == np.uint32:
+                a = a.view(np.int32)
             return torch.from_numpy(a).to(device)
 
-        def f16(a):
-            return torch.from_numpy(a).to(device)
-
-        return cls(u8(w["gate"]), f16(w["gate_scale"]), u8(w["up"]), f16(w["up_scale"]),
-                   u8(w["down"]), f16(w["down_scale"]), group)
+        fmt = "int4_asym" if "gate_zero" in w else "int5" if "gate_hi" in w else "int4"
+        side = {name + sfx: dev(w[name + sfx]) for name in ("gate", "up", "down")
+                for sfx in ("_zero", "_hi") if name + sfx in w}
+        return cls(dev(w["gate"]), dev(w["gate_scale"]), dev(w["up"]), dev(w["up_scale"]),
+                   dev(w["down"]), dev(w["down_scale"]), group, fmt=fmt, **side)
 
     def descriptor(self) -> StrataMoeWeights:
         for name, dt in (("gate", torch.uint8), ("up", torch.uint8), ("down", torch.uint8),
                          ("gate_scale", torch.float16), ("up_scale", torch.float16),
                          ("down_scale", torch.float16)):
             _need(getattr(self, name), dt, name)
+        if self.fmt not in self.FORMATS:
+            raise ValueError(f"fmt must be one of {sorted(self.FORMATS)}, got {self.fmt!r}")
+        side = {}
+        for name in ("gate", "up", "down"):
+            for sfx, dt in (("_zero", torch.uint8), ("_hi", torch.int32)):
+                t = getattr(self, name + sfx)
+                if t is not None:
+                    _need(t, dt, name + sfx)
+                side[name + sfx] = 0 if t is None else t.data_ptr()
         return StrataMoeWeights(
             self.gate.data_ptr(), self.gate_scale.data_ptr(), self.up.data_ptr(),
             self.up_scale.data_ptr(), self.down.data_ptr(), self.down_scale.data_ptr(),
-            self.num_experts, self.hidden, self.inter, self.group,
+            self.num_experts, self.hidden, self.inter, self.group, self.FORMATS[self.fmt],
+            side["gate_zero"], side["up_zero"], side["down_zero"],
+            side["gate_hi"], side["up_hi"], side["down_hi"],
         )
 
 

@@ -35,6 +35,13 @@ class StrataMoeWeights(ctypes.Structure):
         ("hidden", _i32),
         ("inter", _i32),
         ("group", _i32),
+        ("format", _i32),
+        ("gate_zero", _vp),
+        ("up_zero", _vp),
+        ("down_zero", _vp),
+        ("gate_hi", _vp),
+        ("up_hi", _vp),
+        ("down_hi", _vp),
     ]
 
 

@@ -70,6 +70,61 @@ int check_shape(const char *fn, long long H, long long I, long long g) {
   return STRATA_OK;
 }
 
+// The weight arrays of `w` for its format: the codes and scales always, the
+// zero points (asymmetric 4-bit) or fifth-bit words (5-bit) as the format
+// needs them, NULL side arrays otherwise.
+int check_weights(const char *fn, const strata_moe_weights *w) {
+  REQUIRE_PTR(fn, w->gate);
+  REQUIRE_PTR(fn, w->gate_scale);
+  REQUIRE_PTR(fn, w->up);
+  REQUIRE_PTR(fn, w->up_scale);
+  REQUIRE_PTR(fn, w->down);
+  REQUIRE_PTR(fn, w->down_scale);
+  const bool zeros = w->gate_zero || w->up_zero || w->down_zero;
+  const bool his = w->gate_hi || w->up_hi || w->down_hi;
+  switch (w->format) {
+    case STRATA_W_INT4:
+      if (zeros || his)
+        return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "format=STRATA_W_INT4 takes no zero points or fifth-bit words");
+      return STRATA_OK;
+    case STRATA_W_INT4_ASYM:
+      if (his) return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "format=STRATA_W_INT4_ASYM takes no fifth-bit words");
+      if (!w->gate_zero || !w->up_zero || !w->down_zero)
+        return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "format=STRATA_W_INT4_ASYM needs gate_zero, up_zero and down_zero");
+      if ((w->hidden / w->group) % 2 || (w->inter / w->group) % 2)
+        return fail(STRATA_ERR_UNSUPPORTED, fn,
+                    "format=STRATA_W_INT4_ASYM needs an even number of groups per row (hidden=%d, inter=%d, group=%d)",
+                    w->hidden, w->inter, w->group);
+      return STRATA_OK;
+    case STRATA_W_INT5:
+      if (zeros) return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "format=STRATA_W_INT5 takes no zero points");
+      if (!w->gate_hi || !w->up_hi || !w->down_hi)
+        return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "format=STRATA_W_INT5 needs gate_hi, up_hi and down_hi");
+      for (const void *p : {(const void *)w->gate_hi, (const void *)w->up_hi, (const void *)w->down_hi})
+        if (reinterpret_cast<uintptr_t>(p) & 3u)
+          return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "fifth-bit words at %p are not 4-byte aligned", p);
+      return STRATA_OK;
+    default:
+      return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "format=%d is not a strata_weight_format", (int)w->format);
+  }
+}
+
+strata::FfnWeights ffn_weights(const strata_moe_weights *w) {
+  strata::FfnWeights fw{w->gate,       w->up,         w->down,   w->gate_scale, w->up_scale,
+                        w->down_scale, w->num_experts, w->hidden, w->inter,      w->group};
+  fw.fmt = w->format;
+  if (w->format == STRATA_W_INT4_ASYM) {
+    fw.gate_x = w->gate_zero;
+    fw.up_x = w->up_zero;
+    fw.down_x = w->down_zero;
+  } else if (w->format == STRATA_W_INT5) {
+    fw.gate_x = reinterpret_cast<const uint8_t *>(w->gate_hi);
+    fw.up_x = reinterpret_cast<const uint8_t *>(w->up_hi);
+    fw.down_x = reinterpret_cast<const uint8_t *>(w->down_hi);
+  }
+  return fw;
+}
+
 enum class FfnPath { Auto, Gemm, Gemv };
 
 // Read on every call (a getenv is negligible next to a kernel launch), so a
@@ -269,12 +324,7 @@ int strata_moe_ffn(const uint16_t *x_bf16, int32_t T, int32_t k, const strata_mo
   REQUIRE_PTR(fn, offsets);
   REQUIRE_PTR(fn, perm);
   REQUIRE_PTR(fn, y_or_out);
-  REQUIRE_PTR(fn, w->gate);
-  REQUIRE_PTR(fn, w->gate_scale);
-  REQUIRE_PTR(fn, w->up);
-  REQUIRE_PTR(fn, w->up_scale);
-  REQUIRE_PTR(fn, w->down);
-  REQUIRE_PTR(fn, w->down_scale);
+  if (int rc = check_weights(fn, w)) return rc;
   if (topk_w != nullptr && !aligned16(topk_w))
     return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "topk_w=%p is not 16-byte aligned", (const void *)topk_w);
   const int E = w->num_experts, H = w->hidden, I = w->inter, g = w->group;
@@ -295,7 +345,7 @@ int strata_moe_ffn(const uint16_t *x_bf16, int32_t T, int32_t k, const strata_mo
                 kGemvMaxTokens, T, H, I);
   const bool use_gemv = forced == FfnPath::Gemv || (forced == FfnPath::Auto && gemv_ok);
 
-  FfnWeights fw{w->gate, w->up, w->down, w->gate_scale, w->up_scale, w->down_scale, E, H, I, g};
+  const FfnWeights fw = ffn_weights(w);
   const FfnWorkspace ws = carve_ffn_workspace(workspace, T, k, E, H, I);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = use_gemv ? launch_ffn_gemv(x_bf16, T, k, fw, offsets, perm, topk_w, y_or_out, ws, s)
@@ -330,12 +380,7 @@ static int layer_impl(const char *fn, const float *logits, const uint16_t *x_bf1
   REQUIRE_PTR(fn, perm);
   REQUIRE_PTR(fn, inv_perm);
   REQUIRE_PTR(fn, out);
-  REQUIRE_PTR(fn, w->gate);
-  REQUIRE_PTR(fn, w->gate_scale);
-  REQUIRE_PTR(fn, w->up);
-  REQUIRE_PTR(fn, w->up_scale);
-  REQUIRE_PTR(fn, w->down);
-  REQUIRE_PTR(fn, w->down_scale);
+  if (int rc = check_weights(fn, w)) return rc;
   const long long pairs = (long long)T * k;
   const size_t need = layer_workspace_bytes(T, E, k, H, I);
   if (workspace == nullptr)
@@ -352,10 +397,10 @@ static int layer_impl(const char *fn, const float *logits, const uint16_t *x_bf1
                 "STRATA_MOE_FFN_PATH=gemv needs T <= %d, hidden in {256,512,1024,2048,4096} and inter a power of two "
                 "in [128, 2048] (T=%d, hidden=%d, inter=%d)",
                 kGemvMaxTokens, T, H, I);
-  FfnWeights fw{w->gate, w->up, w->down, w->gate_scale, w->up_scale, w->down_scale, E, H, I, g};
+  const FfnWeights fw = ffn_weights(w);
   const FfnWorkspace ws = carve_ffn_workspace(workspace, T, k, E, H, I);
   hipError_t e;
-  if (forced != FfnPath::Gemm && decode_layer_supported(T, E, k, H, I)) {
+  if (forced != FfnPath::Gemm && fw.fmt == STRATA_W_INT4 && decode_layer_supported(T, E, k, H, I)) {
     e = launch_decode_layer(logits, x_bf16, T, k, fw, topk_ids, topk_w, counts, offsets, perm, inv_perm, out, ws, s);
   } else {
     const bool use_gemv = forced == FfnPath::Gemv || (forced == FfnPath::Auto && gemv_ok);

@@ -88,7 +88,14 @@ struct GemmArgs {
   int nslices;         // weight-row slices per tile
   int spi;             // slices per work item (consecutive slices of one tile)
   int fused;
+  // Weight side data of the other formats (general pipeline): zero points,
+  // two per byte [E][N][K/g/2] (asymmetric 4-bit), or fifth-bit words
+  // [E][N][K/32] (5-bit), for B0 and B1.
+  const uint8_t *X0, *X1;
 };
+
+// Weight formats (values of strata_weight_format).
+constexpr int kFmtInt4 = 0, kFmtInt4Asym = 1, kFmtInt5 = 2;
 
 struct RowTables {
   int src[kGemmRows];  // gate/up: token row of x; down: grouped row of h
@@ -149,6 +156,37 @@ __device__ __forceinline__ half8 dequant8(uint32_t d, half2_t s2, uint32_t mask,
   const half2_t h1 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, r1), sixteenth, off16) * s2;
   const half2_t h2 = (__builtin_bit_cast(half2_t, r2) - off) * s2;
   const half2_t h3 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, r3), sixteenth, off16) * s2;
+  return half8{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
+}
+
+// dequant8 for the three weight formats: the low nibble of each half-word
+// gives 1024 + u, the next nibble 1024 + 16u (as in dequant8); then
+//   asymmetric 4-bit: minus (1024 + z) and (64 + z) for the group's zero
+//     point z (ce, co), both exact in fp16;
+//   5-bit: the fifth bits of the dword's 8 elements come from word hw (bit
+//     4i + b for element i of the 32-element word's dword b) into bit 4 of
+//     the low pairs and bit 8 of the high ones (one and-or each), then
+//     minus 1040 and 80.
+template <int FMT>
+__device__ __forceinline__ half8 dequant8_fmt(uint32_t d, half2_t s2, uint32_t mask, uint32_t magic, half2_t ce,
+                                              half2_t co, uint32_t hw, int b) {
+  const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const uint32_t d8 = d >> 8;
+  uint32_t r0 = and_or(d, mask, magic);
+  uint32_t r1 = and_or(d, mask << 4, magic);
+  uint32_t r2 = and_or(d8, mask, magic);
+  uint32_t r3 = and_or(d8, mask << 4, magic);
+  if constexpr (FMT == kFmtInt5) {
+    const uint32_t t1 = hw << (4 - b), t2 = hw >> (4 + b);
+    r0 |= t1 & 0x00100010u;
+    r1 |= t1 & 0x01000100u;
+    r2 |= t2 & 0x00100010u;
+    r3 |= t2 & 0x01000100u;
+  }
+  const half2_t h0 = (__builtin_bit_cast(half2_t, r0) + ce) * s2;
+  const half2_t h1 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, r1), sixteenth, co) * s2;
+  const half2_t h2 = (__builtin_bit_cast(half2_t, r2) + ce) * s2;
+  const half2_t h3 = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, r3), sixteenth, co) * s2;
   return half8{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
 }
 
@@ -303,9 +341,10 @@ __device__ __forceinline__ void mma_stage_pipelined(floatx16 (&acc)[NMB][kNB], B
 // Four K-steps (64 K) of MFMAs (general pipeline): token fragments from
 // `afrag(j, mb)`, weights from the packed dwords of bw (one per K-step) and
 // the scales s2.
-template <int NMB, typename AFrag>
+template <int NMB, int FMT, typename AFrag>
 __device__ __forceinline__ void mma_k64(floatx16 (&acc)[NMB][kNB], const uint4 (&bw)[kNB],
-                                        const half2_t (&s2)[kNB], AFrag &&afrag) {
+                                        const half2_t (&s2)[kNB], const half2_t (&ce)[kNB], const half2_t (&co)[kNB],
+                                        const uint32_t (&hw)[kNB], AFrag &&afrag) {
   const uint32_t mask = __builtin_amdgcn_readfirstlane(0x000F000Fu);
   const uint32_t magic = __builtin_amdgcn_readfirstlane(0x64006400u);
   // Token fragments are read one K-step ahead of the MFMAs that use them.
@@ -320,7 +359,9 @@ __device__ __forceinline__ void mma_k64(floatx16 (&acc)[NMB][kNB], const uint4 (
     }
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
-      const half8 bf = dequant8(dword_of(bw[nb], j), s2[nb], mask, magic);
+      const half8 bf = FMT == kFmtInt4 ? dequant8(dword_of(bw[nb], j), s2[nb], mask, magic)
+                                       : dequant8_fmt<FMT>(dword_of(bw[nb], j), s2[nb], mask, magic, ce[nb], co[nb],
+                                                           hw[nb], j);
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
         acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf, af[j & 1][mb], acc[mb][nb], 0, 0, 0);
@@ -750,13 +791,18 @@ constexpr int kGenW = 4;
 constexpr int kKC = kGemmKChunk;  // K per pipelined chunk (64)
 constexpr int kGenStages = 3;
 
+template <int FMT>
 struct GenStage {
   uint4 a[kGemmRows * 8];                // token rows [row][segment], XOR-swizzled (ga_slot)
   uint4 b[2 * Shape<kGenW>::kBRows];     // [weight row][lane half]: 16 bytes = 32 K values
   uint32_t s[2 * Shape<kGenW>::kBRows];  // [weight row][lane half]: fp16 group scale in the low half
+  // [weight row][lane half]: the group's zero-point byte (asymmetric) or
+  // the fifth-bit word of the half's 32 K values (5-bit)
+  uint32_t x[FMT == kFmtInt4 ? 1 : 2 * Shape<kGenW>::kBRows];
 };
+template <int FMT>
 struct GenRing {
-  GenStage *st[kGenStages];
+  GenStage<FMT> *st[kGenStages];
 };
 
 // Segment c (0..7) of token row r: the 8 rows read by one 8-lane group of a
@@ -768,17 +814,19 @@ __device__ __forceinline__ int ga_slot(int r, int c) { return r * 8 + (c ^ (r & 
 //     [(4i + wave)*64, +64), i.e. 8 rows x 128 bytes;
 //   * packed weights: 32 rows x 32 bytes per block;
 //   * scales: 32 rows x 2 halves per block (a 2-byte direct-to-LDS load
-//     writes one zero-extended dword per lane).
+//     writes one zero-extended dword per lane);
+//   * other formats: per block one more direct-to-LDS load of the same
+//     shape, the zero-point byte (1 byte) or the fifth-bit word (4 bytes).
 // Step c: wait for this wavefront's loads of chunk c, one barrier (every
 // wavefront's loads landed and the oldest stage is free), issue chunk c+2
 // into it, then dequant + MFMAs.  Past the last chunk the issue repeats the
 // last chunk (loads are never skipped), so every wait counts the same number
 // of operations.
-template <int MODE, int NMB>
-__device__ __forceinline__ void gemm_tile_general(const GemmArgs &a, const GenRing &R, const RowTables &rt, int e,
-                                                  int row0, int nrows, int slice) {
+template <int MODE, int NMB, int FMT>
+__device__ __forceinline__ void gemm_tile_general(const GemmArgs &a, const GenRing<FMT> &R, const RowTables &rt,
+                                                  int e, int row0, int nrows, int slice) {
   constexpr int S_ = kGenStages;
-  constexpr int V = NMB + 2 * kNB;  // direct-to-LDS loads per stage per wavefront
+  constexpr int V = NMB + (FMT == kFmtInt4 ? 2 : 3) * kNB;  // direct-to-LDS loads per stage per wavefront
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
   const int col = lane & 31, half = lane >> 5;
@@ -802,8 +850,21 @@ __device__ __forceinline__ void gemm_tile_general(const GemmArgs &a, const GenRi
   const uint32_t boff = (uint32_t)col2 * (a.K / 2) + 16 * hh;
   const uint32_t soff = ((uint32_t)col2 * (a.K / a.g)) * 2;
   const int g_shift = 31 - __clz(a.g);  // g is a power of two
+  // Side data of the other formats: the row's zero-point bytes or fifth-bit words.
+  const char *xbase[kNB];
+  uint32_t xoff = 0;
+  if constexpr (FMT != kFmtInt4) {
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) {
+      const int n0 = valid ? weight_row0<MODE, kGenW>(slice, wave, nb) : 0;
+      const bool up = MODE == 0 && nb >= kNB / 2;
+      const size_t rowbytes = FMT == kFmtInt4Asym ? (size_t)(a.K / a.g / 2) : (size_t)(a.K / 32) * 4;
+      xbase[nb] = reinterpret_cast<const char *>(up ? a.X1 : a.X0) + ((size_t)e * a.N + n0) * rowbytes;
+    }
+    xoff = FMT == kFmtInt4Asym ? (uint32_t)col2 * (uint32_t)(a.K / a.g / 2) : (uint32_t)col2 * (uint32_t)(a.K / 32) * 4;
+  }
 
-  auto issue = [&](GenStage &st, int c) {
+  auto issue = [&](GenStage<FMT> &st, int c) {
     const int kc = c * kKC;
 #pragma unroll
     for (int i = 0; i < NMB; ++i)
@@ -814,6 +875,11 @@ __device__ __forceinline__ void gemm_tile_general(const GemmArgs &a, const GenRi
       __builtin_amdgcn_global_load_lds(bbase[nb] + kc / 2 + boff, as_lds(&st.b[base]), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(sbase[nb] + 2 * ((kc + 32 * hh) >> g_shift) + soff, as_lds(&st.s[base]), 2,
                                        0, 0);
+      if constexpr (FMT == kFmtInt4Asym)
+        __builtin_amdgcn_global_load_lds(xbase[nb] + (((kc + 32 * hh) >> g_shift) >> 1) + xoff, as_lds(&st.x[base]),
+                                         1, 0, 0);
+      else if constexpr (FMT == kFmtInt5)
+        __builtin_amdgcn_global_load_lds(xbase[nb] + 4 * ((kc >> 5) + hh) + xoff, as_lds(&st.x[base]), 4, 0, 0);
     }
   };
 
@@ -837,17 +903,32 @@ __device__ __forceinline__ void gemm_tile_general(const GemmArgs &a, const GenRi
     issue(*R.st[(S + S_ - 1) % S_], min(c + S_ - 1, last));
     compiler_fence();
     if (c < nchunks) {
-      const GenStage &st = *R.st[S];
+      const GenStage<FMT> &st = *R.st[S];
       uint4 bw[kNB];
-      half2_t s2[kNB];
+      half2_t s2[kNB], ce[kNB], co[kNB];
+      uint32_t hw[kNB];
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
         const int br = brow_of(wave, nb, col);
         bw[nb] = st.b[br * 2 + half];
         const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)st.s[br * 2 + half]);
         s2[nb] = half2_t{sv, sv};
+        ce[nb] = half2_t{(_Float16)-1032.0f, (_Float16)-1032.0f};
+        co[nb] = half2_t{(_Float16)-72.0f, (_Float16)-72.0f};
+        hw[nb] = 0;
+        if constexpr (FMT == kFmtInt4Asym) {
+          // the zero point of this lane's group: nibble (group & 1) of the byte
+          const int grp = (c * kKC + 32 * half) >> g_shift;
+          const int z = (int)((st.x[br * 2 + half] >> (4 * (grp & 1))) & 15u);
+          ce[nb] = half2_t{(_Float16)(-1024 - z), (_Float16)(-1024 - z)};
+          co[nb] = half2_t{(_Float16)(-64 - z), (_Float16)(-64 - z)};
+        } else if constexpr (FMT == kFmtInt5) {
+          hw[nb] = st.x[br * 2 + half];
+          ce[nb] = half2_t{(_Float16)-1040.0f, (_Float16)-1040.0f};
+          co[nb] = half2_t{(_Float16)-80.0f, (_Float16)-80.0f};
+        }
       }
-      mma_k64<NMB>(acc, bw, s2, [&](int j, int mb) {
+      mma_k64<NMB, FMT>(acc, bw, s2, ce, co, hw, [&](int j, int mb) {
         return __builtin_bit_cast(half8, st.a[ga_slot(mb * 32 + col, 4 * half + j)]);
       });
     }
@@ -863,15 +944,17 @@ __device__ __forceinline__ void gemm_tile_general(const GemmArgs &a, const GenRi
   epilogue<MODE, kGenW, NMB>(a, rt, acc, row0, nrows, slice, wave, col, half, valid);
 }
 
-template <int MODE>
-__global__ __launch_bounds__(64 * kGenW, 2) void moe_gemm_general(GemmArgs a) {
-  __shared__ GenStage st0, st1, st2;
+// Two workgroups per CU for the symmetric 4-bit format; one for the others,
+// whose stages carry the side data (more LDS).
+template <int MODE, int FMT>
+__global__ __launch_bounds__(64 * kGenW, FMT == kFmtInt4 ? 2 : 1) void moe_gemm_general(GemmArgs a) {
+  __shared__ GenStage<FMT> st0, st1, st2;
   __shared__ RowTables rt;
-  const GenRing R{{&st0, &st1, &st2}};
+  const GenRing<FMT> R{{&st0, &st1, &st2}};
   gemm_persistent<MODE>(a, rt, [&](int nmb, const Tile &tile, int slice0, int nsl) {
     dispatch_nmb(nmb, [&](auto n) {
       for (int sl = slice0; sl < slice0 + nsl; ++sl)
-        gemm_tile_general<MODE, decltype(n)::value>(a, R, rt, tile.e, tile.row0, tile.rows, sl);
+        gemm_tile_general<MODE, decltype(n)::value, FMT>(a, R, rt, tile.e, tile.row0, tile.rows, sl);
     });
   });
 }
@@ -907,9 +990,11 @@ int persistent_grid(long long work_upper, int wg_per_cu) {
 // multiple of 8, or a whole row of fewer than 8 groups in one window), the
 // general one otherwise.
 template <int MODE>
-hipError_t launch_gemm(GemmArgs args, long long tiles_upper, int matrix_rows, hipStream_t s) {
+hipError_t launch_gemm(GemmArgs args, long long tiles_upper, int matrix_rows, int fmt, hipStream_t s) {
   // The wide pipeline addresses A through a buffer resource: 32-bit offsets.
-  const bool wide = STRATA_GEMM_WIDE && args.K % kKS == 0 && ((args.K / args.g) % 8 == 0 || args.K / args.g < 8) &&
+  // The asymmetric and 5-bit formats run on the general pipeline.
+  const bool wide = STRATA_GEMM_WIDE && fmt == kFmtInt4 && args.K % kKS == 0 &&
+                    ((args.K / args.g) % 8 == 0 || args.K / args.g < 8) &&
                     (long long)args.a_rows * args.K * 2 < (1LL << 32);
   if (wide) {
     const int width = MODE == 0 ? Shape<kWideW>::kHCols : Shape<kWideW>::kOutCols;
@@ -924,7 +1009,13 @@ hipError_t launch_gemm(GemmArgs args, long long tiles_upper, int matrix_rows, hi
     const int width = MODE == 0 ? Shape<kGenW>::kHCols : Shape<kGenW>::kOutCols;
     args.nslices = (matrix_rows + width - 1) / width;
     args.spi = 1;
-    moe_gemm_general<MODE><<<persistent_grid(tiles_upper * args.nslices, 2), 64 * kGenW, 0, s>>>(args);
+    const long long items = tiles_upper * args.nslices;
+    if (fmt == kFmtInt4Asym)
+      moe_gemm_general<MODE, kFmtInt4Asym><<<persistent_grid(items, 1), 64 * kGenW, 0, s>>>(args);
+    else if (fmt == kFmtInt5)
+      moe_gemm_general<MODE, kFmtInt5><<<persistent_grid(items, 1), 64 * kGenW, 0, s>>>(args);
+    else
+      moe_gemm_general<MODE, kFmtInt4><<<persistent_grid(items, 2), 64 * kGenW, 0, s>>>(args);
   }
   return hipGetLastError();
 }
@@ -964,9 +1055,11 @@ hipError_t launch_ffn_gemm(const uint16_t *x, int T, int k, const FfnWeights &w,
   g.meta = ws.meta;
   g.C = ws.h;
   g.fused = 0;
+  g.X0 = w.gate_x;
+  g.X1 = w.up_x;
   {
     KernelTimer timer("gemm_gateup", s);
-    if ((err = launch_gemm<0>(g, tiles_upper, w.I, s)) != hipSuccess) return err;
+    if ((err = launch_gemm<0>(g, tiles_upper, w.I, w.fmt, s)) != hipSuccess) return err;
   }
 
   GemmArgs d = g;
@@ -980,6 +1073,8 @@ hipError_t launch_ffn_gemm(const uint16_t *x, int T, int k, const FfnWeights &w,
   d.K = w.I;
   d.C = fused ? static_cast<void *>(ws.y16) : static_cast<void *>(y_or_out);
   d.fused = fused ? 1 : 0;
+  d.X0 = w.down_x;
+  d.X1 = nullptr;
   // The down GEMM walks the tiles in expert order: its fp16 y rows then
   // reach memory in an order the combine kernel reads measurably faster
   // (50 vs 57 us at T=6144, k=10, H=2048), and the sorted order gains it
@@ -988,7 +1083,7 @@ hipError_t launch_ffn_gemm(const uint16_t *x, int T, int k, const FfnWeights &w,
   d.by_cost = 0;
   {
     KernelTimer timer("gemm_down", s);
-    if ((err = launch_gemm<1>(d, tiles_upper, w.H, s)) != hipSuccess) return err;
+    if ((err = launch_gemm<1>(d, tiles_upper, w.H, w.fmt, s)) != hipSuccess) return err;
   }
   if (fused) return launch_combine_pairs(ws.y16, topk_w, T, k, w.H, y_or_out, s);
   return hipSuccess;

@@ -34,6 +34,8 @@
 //                fp16 rows in pair order and the combine kernel of the
 //                matrix-core path sums each token's k rows in j order
 //                (deterministic, no atomics).
+#include <type_traits>
+
 #include "gemv_dev.h"
 
 namespace strata {
@@ -58,7 +60,24 @@ struct GemvArgs {
   float *out;             // not fused: y [pairs][H] in grouped order
   uint16_t *y16;          // fused: fp16 y [pairs][H] in pair order, summed by the combine kernel
   int fused;
+  // Other weight formats: zero points (two per byte, [E][N][K/g/2]) or
+  // fifth-bit words ([E][N][K/32]) of gate, up and down.
+  const uint8_t *gate_x, *up_x, *down_x;
 };
+
+// The side data of one lane's 32 weights (K from kk) of matrix row `row`
+// (K elements per row, group g): its group's zero point (format 1) or its
+// fifth-bit word (format 2); 0 for format 0.
+template <int FMT>
+__device__ __forceinline__ uint32_t gemv_aux(const uint8_t *x, size_t row, int K, int g, int kk) {
+  if constexpr (FMT == 1) {
+    const int grp = kk / g;
+    return (x[row * (K / g / 2) + (grp >> 1)] >> (4 * (grp & 1))) & 15u;
+  } else if constexpr (FMT == 2) {
+    return reinterpret_cast<const uint32_t *>(x)[row * (K / 32) + kk / 32];
+  }
+  return 0u;
+}
 
 struct Entry {
   int e, row0, rows, nnz;  // e < 0: no such entry
@@ -108,7 +127,7 @@ __device__ Entry find_entry(const int *__restrict__ offsets, int E, int entry) {
 
 // A lane covers K values [32*lane + 2048*c, +32) for c < NCH = ceil(H/2048)
 // (only the first H/32 lanes when H < 2048).
-template <int NCH>
+template <int NCH, int FMT>
 __global__ __launch_bounds__(256, NCH == 1 ? 4 : 2) void gemv_gateup_kernel(GemvArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int colsets = a.I / kGateUpCols;
@@ -129,6 +148,7 @@ __global__ __launch_bounds__(256, NCH == 1 ? 4 : 2) void gemv_gateup_kernel(Gemv
   // This wavefront's gate and up rows (4 columns) and their scales (fp16 bits).
   uint4 wg[kColsPerWave][NCH], wu[kColsPerWave][NCH];
   uint32_t sgb[kColsPerWave][NCH], sub_[kColsPerWave][NCH];
+  uint32_t xg[kColsPerWave][NCH], xu[kColsPerWave][NCH];  // side data of the other formats
 #pragma unroll
   for (int cc = 0; cc < kColsPerWave; ++cc)
 #pragma unroll
@@ -139,6 +159,8 @@ __global__ __launch_bounds__(256, NCH == 1 ? 4 : 2) void gemv_gateup_kernel(Gemv
       wu[cc][c] = *reinterpret_cast<const uint4 *>(a.up + row * kb + kk / 2);
       sgb[cc][c] = a.gate_s[row * ng + kk / a.g];
       sub_[cc][c] = a.up_s[row * ng + kk / a.g];
+      xg[cc][c] = gemv_aux<FMT>(a.gate_x, row, a.H, a.g, kk);
+      xu[cc][c] = gemv_aux<FMT>(a.up_x, row, a.H, a.g, kk);
     }
   asm volatile("" : "+v"(p_first) : : "memory");  // all of the above are issued before p_first is used
   const float on = active ? 1.0f : 0.0f;
@@ -163,6 +185,7 @@ __global__ __launch_bounds__(256, NCH == 1 ? 4 : 2) void gemv_gateup_kernel(Gemv
         opaque(wg[cc][c]);
         opaque(wu[cc][c]);
         asm volatile("" : "+v"(sgb[cc][c]), "+v"(sub_[cc][c]));
+        if constexpr (FMT != 0) asm volatile("" : "+v"(xg[cc][c]), "+v"(xu[cc][c]));
       }
     float gs[kColsPerWave], us[kColsPerWave];
 #pragma unroll
@@ -185,8 +208,15 @@ __global__ __launch_bounds__(256, NCH == 1 ? 4 : 2) void gemv_gateup_kernel(Gemv
       const float corr = 1032.0f * se + 1152.0f * so;
 #pragma unroll
       for (int cc = 0; cc < kColsPerWave; ++cc) {
-        gs[cc] += dot32_split<false>(wg[cc][c], xp, corr, on * half_bits_to_float((uint16_t)sgb[cc][c]));
-        us[cc] += dot32_split<false>(wu[cc][c], xp, corr, on * half_bits_to_float((uint16_t)sub_[cc][c]));
+        const float sg = on * half_bits_to_float((uint16_t)sgb[cc][c]);
+        const float su = on * half_bits_to_float((uint16_t)sub_[cc][c]);
+        if constexpr (FMT == 0) {
+          gs[cc] += dot32_split<false>(wg[cc][c], xp, corr, sg);
+          us[cc] += dot32_split<false>(wu[cc][c], xp, corr, su);
+        } else {
+          gs[cc] += dot32_fmt<false, FMT>(wg[cc][c], xp, se, so, sg, xg[cc][c]);
+          us[cc] += dot32_fmt<false, FMT>(wu[cc][c], xp, se, so, su, xu[cc][c]);
+        }
       }
     }
 #pragma unroll
@@ -206,7 +236,7 @@ __global__ __launch_bounds__(256, NCH == 1 ? 4 : 2) void gemv_gateup_kernel(Gemv
   for (int r = 1; r < en.rows; ++r) one_row(a.perm[en.row0 + r] / a.k, r);
 }
 
-template <int LPR>  // lanes per down row = I / 32
+template <int LPR, int FMT>  // lanes per down row = I / 32
 __global__ __launch_bounds__(256, 4) void gemv_down_kernel(GemvArgs a) {
   constexpr int RPI = kWave / LPR;              // rows per wavefront instruction
   constexpr int kRowsWG = 4 * kDownIter * RPI;  // output rows per workgroup
@@ -235,13 +265,14 @@ __global__ __launch_bounds__(256, 4) void gemv_down_kernel(GemvArgs a) {
 
   // Rows past H (only when H is below the workgroup's row count) load row 0 and are not stored.
   uint4 wq[kDownIter];
-  uint32_t sdb[kDownIter];
+  uint32_t sdb[kDownIter], xd[kDownIter];
 #pragma unroll
   for (int it = 0; it < kDownIter; ++it) {
     const int n = nbase + it * RPI;
     const size_t row = (size_t)en.e * a.H + (n < a.H ? n : 0);
     wq[it] = *reinterpret_cast<const uint4 *>(a.down + row * kb + 16 * sub);
     sdb[it] = a.down_s[row * ng + (32 * sub) / a.g];
+    xd[it] = gemv_aux<FMT>(a.down_x, row, a.I, a.g, 32 * sub);
   }
 
   for (int r = 0; r < en.rows; ++r) {
@@ -269,8 +300,9 @@ __global__ __launch_bounds__(256, 4) void gemv_down_kernel(GemvArgs a) {
     const float corr = 1032.0f * se + 1152.0f * so;
 #pragma unroll
     for (int it = 0; it < kDownIter; ++it) {
-      const float yv =
-          dpp_group_sum<LPR>(dot32_split<true>(wq[it], hp, corr, half_bits_to_float((uint16_t)sdb[it])));
+      const float sd = half_bits_to_float((uint16_t)sdb[it]);
+      const float yv = dpp_group_sum<LPR>(FMT == 0 ? dot32_split<true>(wq[it], hp, corr, sd)
+                                                   : dot32_fmt<true, FMT>(wq[it], hp, se, so, sd, xd[it]));
       const int n = nbase + it * RPI;
       if (sub == 0 && n < a.H) {
         if (a.fused)
@@ -314,13 +346,25 @@ hipError_t launch_ffn_gemv(const uint16_t *x, int T, int k, const FfnWeights &w,
   a.out = y_or_out;
   a.y16 = ws.y16;
   a.fused = topk_w != nullptr;
+  a.gate_x = w.gate_x;
+  a.up_x = w.up_x;
+  a.down_x = w.down_x;
   {
     KernelTimer timer("gemv_gateup", s);
     const int grid = entries * (w.I / kGateUpCols);
-    if (w.H <= 2048)
-      gemv_gateup_kernel<1><<<grid, 256, 0, s>>>(a);
+    auto go = [&](auto fc) {
+      constexpr int F = decltype(fc)::value;
+      if (w.H <= 2048)
+        gemv_gateup_kernel<1, F><<<grid, 256, 0, s>>>(a);
+      else
+        gemv_gateup_kernel<kMaxChunks, F><<<grid, 256, 0, s>>>(a);
+    };
+    if (w.fmt == 1)
+      go(std::integral_constant<int, 1>{});
+    else if (w.fmt == 2)
+      go(std::integral_constant<int, 2>{});
     else
-      gemv_gateup_kernel<kMaxChunks><<<grid, 256, 0, s>>>(a);
+      go(std::integral_constant<int, 0>{});
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -329,13 +373,22 @@ hipError_t launch_ffn_gemv(const uint16_t *x, int T, int k, const FfnWeights &w,
   const int grid = entries * ((w.H + rows_wg - 1) / rows_wg);
   {
     KernelTimer timer("gemv_down", s);
-    switch (lpr) {
-      case 4: gemv_down_kernel<4><<<grid, 256, 0, s>>>(a); break;
-      case 8: gemv_down_kernel<8><<<grid, 256, 0, s>>>(a); break;
-      case 16: gemv_down_kernel<16><<<grid, 256, 0, s>>>(a); break;
-      case 32: gemv_down_kernel<32><<<grid, 256, 0, s>>>(a); break;
-      default: gemv_down_kernel<64><<<grid, 256, 0, s>>>(a); break;
-    }
+    auto go = [&](auto fc) {
+      constexpr int F = decltype(fc)::value;
+      switch (lpr) {
+        case 4: gemv_down_kernel<4, F><<<grid, 256, 0, s>>>(a); break;
+        case 8: gemv_down_kernel<8, F><<<grid, 256, 0, s>>>(a); break;
+        case 16: gemv_down_kernel<16, F><<<grid, 256, 0, s>>>(a); break;
+        case 32: gemv_down_kernel<32, F><<<grid, 256, 0, s>>>(a); break;
+        default: gemv_down_kernel<64, F><<<grid, 256, 0, s>>>(a); break;
+      }
+    };
+    if (w.fmt == 1)
+      go(std::integral_constant<int, 1>{});
+    else if (w.fmt == 2)
+      go(std::integral_constant<int, 2>{});
+    else
+      go(std::integral_constant<int, 0>{});
   }
   if ((err = hipGetLastError()) != hipSuccess) return err;
   if (a.fused) return launch_combine_pairs(ws.y16, topk_w, T, k, w.H, y_or_out, s);

@@ -61,6 +61,49 @@ __device__ __forceinline__ float dot32_split(const uint4 wq, const half2_t *xp, 
   return s * (acc - corr);
 }
 
+// dot32_split for the three weight formats (FMT: 0 symmetric 4-bit, 1
+// asymmetric 4-bit, 2 symmetric 5-bit), from the even- and odd-pair sums se
+// and so of the activations (so over the stored x/16) and the lane's side
+// data `aux`: its group's zero point z (asymmetric) or the fifth-bit word of
+// its 32 weights (5-bit, bit 4i + q for element i of dword q).  The offset
+// term is (1024 + z) se + (1024 + 16 z) so with z = 8 for the symmetric
+// 4-bit format; the 5-bit one puts the fifth bits into bit 4 (low pairs) and
+// bit 8 (high pairs) of each fp16 pair and subtracts 1040 se + 1280 so.
+template <bool kFused, int FMT>
+__device__ __forceinline__ float dot32_fmt(const uint4 wq, const half2_t *xp, float se, float so, float s,
+                                           uint32_t aux) {
+  auto pair = [](uint32_t d, uint32_t m) {
+    return kFused ? and_or_sv(d, m, 0x64006400u) : ((d & m) | 0x64006400u);
+  };
+  float acc = 0.0f;
+  const uint32_t d[4] = {wq.x, wq.y, wq.z, wq.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t d8 = d[q] >> 8;
+    uint32_t p0 = pair(d[q], 0x000F000Fu), p1 = pair(d[q], 0x00F000F0u);
+    uint32_t p2 = pair(d8, 0x000F000Fu), p3 = pair(d8, 0x00F000F0u);
+    if constexpr (FMT == 2) {
+      const uint32_t t1 = aux << (4 - q), t2 = aux >> (4 + q);
+      p0 |= t1 & 0x00100010u;
+      p1 |= t1 & 0x01000100u;
+      p2 |= t2 & 0x00100010u;
+      p3 |= t2 & 0x01000100u;
+    }
+    acc = __builtin_amdgcn_fdot2(xp[4 * q], __builtin_bit_cast(half2_t, p0), acc, false);
+    acc = __builtin_amdgcn_fdot2(xp[4 * q + 1], __builtin_bit_cast(half2_t, p1), acc, false);
+    acc = __builtin_amdgcn_fdot2(xp[4 * q + 2], __builtin_bit_cast(half2_t, p2), acc, false);
+    acc = __builtin_amdgcn_fdot2(xp[4 * q + 3], __builtin_bit_cast(half2_t, p3), acc, false);
+  }
+  float corr;
+  if constexpr (FMT == 2) {
+    corr = 1040.0f * se + 1280.0f * so;
+  } else {
+    const float z = FMT == 1 ? (float)aux : 8.0f;
+    corr = (1024.0f + z) * se + (1024.0f + 16.0f * z) * so;
+  }
+  return s * (acc - corr);
+}
+
 // Sum over each group of W consecutive lanes (W a power of two), in every
 // lane of the group, with DPP moves inside 16-lane rows instead of LDS
 // permutes; the whole wavefront must be active.

@@ -41,6 +41,10 @@ struct FfnWeights {
   const uint8_t *gate, *up, *down;
   const uint16_t *gate_s, *up_s, *down_s;
   int E, H, I, g;
+  int fmt = 0;  // strata_weight_format: 0 symmetric 4-bit, 1 asymmetric 4-bit, 2 symmetric 5-bit
+  // Side data of formats 1 and 2: zero points [E][N][K/g/2] (two per byte)
+  // or fifth-bit words [E][N][K/32] (as bytes).
+  const uint8_t *gate_x = nullptr, *up_x = nullptr, *down_x = nullptr;
 };
 
 // ---------------------------------------------------------------- launchers

@@ -26,7 +26,7 @@ def _lib():
 def declared_symbols():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(strata_moe_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(strata_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_four_calls():
@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported():
     abi, lib = _lib()
     syms = declared_symbols()
     out = subprocess.run(["nm", "-D", "--defined-only", abi.LIB_PATH], capture_output=True, text=True).stdout
-    exported = set(re.findall(r" T (strata_moe_\w+)", out))
+    exported = set(re.findall(r" T (strata_\w+)", out))
     for name in syms:
         assert name in exported, name
         assert hasattr(lib, name)
@@ -172,6 +172,44 @@ def test_ffn_rejects_null_weights_and_small_workspace():
     w = _weights(abi)
     assert lib.strata_moe_ffn(fake, 8, 2, ctypes.byref(w), fake, fake, None, fake, fake, 64, None) == 3
     assert "workspace_bytes=64" in _err(lib)
+
+
+@pytest.mark.parametrize(
+    "fmt,side,kw,code,needle",
+    [
+        (0, ("gate_zero",), {}, 1, "takes no zero points"),
+        (0, ("down_hi",), {}, 1, "takes no zero points or fifth-bit words"),
+        (1, ("gate_zero", "up_zero"), {}, 1, "needs gate_zero, up_zero and down_zero"),
+        (1, ("gate_zero", "up_zero", "down_zero", "up_hi"), {}, 1, "takes no fifth-bit words"),
+        (1, ("gate_zero", "up_zero", "down_zero"), dict(I=384, g=128), 2, "even number of groups"),
+        (2, ("gate_hi", "up_hi"), {}, 1, "needs gate_hi, up_hi and down_hi"),
+        (2, ("gate_hi", "up_hi", "down_hi", "down_zero"), {}, 1, "takes no zero points"),
+        (3, (), {}, 1, "format=3"),
+        (-1, (), {}, 1, "format=-1"),
+    ],
+)
+def test_weight_format_descriptor_is_checked(fmt, side, kw, code, needle):
+    """Each weight format takes exactly its own side arrays; the asymmetric
+    format's two-per-byte zero points need an even number of groups per row."""
+    abi, lib = _lib()
+    w = _weights(abi, **kw)
+    w.format = fmt
+    for name in side:
+        setattr(w, name, 0x20000)
+    fake = ctypes.c_void_p(0x10000)
+    rc = lib.strata_moe_ffn(fake, 8, 2, ctypes.byref(w), fake, fake, None, fake, fake, 1 << 30, None)
+    assert rc == code, _err(lib)
+    assert needle in _err(lib)
+
+
+def test_fifth_bit_words_must_be_word_aligned():
+    abi, lib = _lib()
+    w = _weights(abi)
+    w.format = 2
+    w.gate_hi, w.up_hi, w.down_hi = 0x20000, 0x20002, 0x20000
+    fake = ctypes.c_void_p(0x10000)
+    assert lib.strata_moe_ffn(fake, 8, 2, ctypes.byref(w), fake, fake, None, fake, fake, 1 << 30, None) == 1
+    assert "not 4-byte aligned" in _err(lib)
 
 
 def test_ffn_path_override_is_checked(monkeypatch):
