@@ -396,16 +396,17 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const RowTables &rt,
           hp[i][1] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)hv[2], (_Float16)hv[3]});
         }
         // Half-wave swaps (v_permlane32_swap): for gi = 0, 1 the lanes of
-        // half 0 receive the high four features of group gi from half 1 and
-        // give it the low four of group gi + 2, so afterwards every lane
+        // half 0 receive the high four features of group 2gi from half 1 and
+        // give it the low four of group 2gi + 1, so afterwards every lane
         // holds both halves (lo: from half 0, hi: from half 1) of the group
-        // it stores, 2 * half + gi.
+        // it stores, 2 * gi + half: the two lanes of a row store 32
+        // consecutive bytes with one instruction.
         uint32_t lo[2][2], hi[2][2];
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
           for (int d = 0; d < 2; ++d) {
-            const auto sw = __builtin_amdgcn_permlane32_swap(hp[gi][d], hp[gi + 2][d], false, false);
+            const auto sw = __builtin_amdgcn_permlane32_swap(hp[2 * gi][d], hp[2 * gi + 1][d], false, false);
             lo[gi][d] = sw[0];
             hi[gi][d] = sw[1];
           }
@@ -414,7 +415,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const RowTables &rt,
               static_cast<uint16_t *>(a.C) + (size_t)(row0 + r) * a.N + weight_row0<0, W>(slice, wave, hb);
 #pragma unroll
           for (int gi = 0; gi < 2; ++gi) {
-            const int grp = 2 * half + gi;  // 8-feature group this lane stores
+            const int grp = 2 * gi + half;  // 8-feature group this lane stores
             const uint32_t lo0 = lo[gi][0], lo1 = lo[gi][1], hi0 = hi[gi][0], hi1 = hi[gi][1];
             uint4 o;
             o.x = __builtin_amdgcn_perm(hi0, lo0, 0x05040100u);
@@ -429,7 +430,8 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const RowTables &rt,
       const size_t row = (size_t)rt.dst[r] * a.N;
       if (a.fused) {  // fp16 y rows in pair order, summed by the combine kernel
         // As for h: one exchange with lane l^32 gives each lane two whole
-        // 8-feature groups per block, stored as 16 bytes each.
+        // 8-feature groups per block, stored as 16 bytes each, the two lanes
+        // of a row storing 32 consecutive bytes per instruction.
         uint16_t *yrow = static_cast<uint16_t *>(a.C) + row;
 #pragma unroll
         for (int nb = 0; nb < kNB; ++nb) {
@@ -443,9 +445,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, const RowTables &rt,
           // The same half-wave swaps as for h.
 #pragma unroll
           for (int gi = 0; gi < 2; ++gi) {
-            const int grp = 2 * half + gi;  // 8-feature group this lane stores
-            const auto s0 = __builtin_amdgcn_permlane32_swap(yp[gi][0], yp[gi + 2][0], false, false);
-            const auto s1 = __builtin_amdgcn_permlane32_swap(yp[gi][1], yp[gi + 2][1], false, false);
+            const int grp = 2 * gi + half;  // 8-feature group this lane stores
+            const auto s0 = __builtin_amdgcn_permlane32_swap(yp[2 * gi][0], yp[2 * gi + 1][0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(yp[2 * gi][1], yp[2 * gi + 1][1], false, false);
             uint4 o;
             o.x = s0[0];  // features 0-1 of the group (from the half-0 lane)
             o.y = s1[0];  // 2-3
