@@ -127,8 +127,11 @@ def record_traffic(fetch_csv: str, write_csv: str, prefill_workload: str) -> dic
 
 
 def expert_weight_bytes(cfg, matrices: int = 3) -> int:
+    """Packed codes + fp16 scales (+ zero points or fifth bits) of `matrices`
+    H x I matrices of one expert."""
     n = matrices * cfg.H * cfg.I
-    return n // 2 + 2 * (n // cfg.g)
+    extra = {"int4": 0, "int4_asym": n // cfg.g // 2, "int5": n // 8}[getattr(cfg, "fmt", "int4")]
+    return n // 2 + 2 * (n // cfg.g) + extra
 
 
 def kernel_work(kernel: str, cfg, pairs: int, distinct: int):
@@ -388,14 +391,19 @@ def bench_secondary(qe, args):
 
     out = {}
     dev = torch.device("cuda:0")
-    for name, bound, steps in (("tiny", None, 200), ("prefill512", "hbm", 50), ("zipf6144", "mfma", 10),
-                               ("prefill6144_g32", "mfma", 50), ("prefill6144_g128", "mfma", 50)):
+    # (name, bound, steps, one strata_moe_layer call per step instead of the
+    # separate calls); the last four are the other weight formats.
+    for name, bound, steps, single in (("tiny", None, 200, False), ("prefill512", "hbm", 50, False),
+                                       ("zipf6144", "mfma", 10, False), ("prefill6144_g32", "mfma", 50, False),
+                                       ("prefill6144_g128", "mfma", 50, False),
+                                       ("prefill6144_asym", "mfma", 30, True), ("prefill6144_int5", "mfma", 30, True),
+                                       ("decode_asym", "hbm", 500, True), ("decode_int5", "hbm", 500, True)):
         cfg = synth.config(name)
         inp = synth.make_inputs(cfg)
         logits = torch.from_numpy(inp.logits).to(dev)
         x = torch.from_numpy(inp.x_bf16.view(np.int16)).to(dev).view(torch.bfloat16)
         experts = qe.QuantizedExperts.from_numpy(inp.weights, cfg.g, dev)
-        run = qe.LayerRunner(experts, cfg.T, cfg.E, cfg.k, fused=True, device=dev)
+        run = qe.LayerRunner(experts, cfg.T, cfg.E, cfg.k, fused=True, device=dev, single_call=single)
         for _ in range(max(args.warmup, 3)):
             run(logits, x)
         secs = time_region(lambda i: run(logits, x), steps)
@@ -403,6 +411,7 @@ def bench_secondary(qe, args):
         flops, nbytes = layer_work(cfg, distinct)
         us = secs / steps * 1e6
         rec = {"workload": f"{cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} g={cfg.g}",
+               "weights": cfg.fmt, "call": "strata_moe_layer" if single else "route + permute + ffn",
                "us_per_step": round(us, 2), "tokens_per_s": round(cfg.T / (us * 1e-6), 1), "steps": steps,
                "distinct_experts": distinct, "alg_flops": flops, "alg_bytes": int(nbytes)}
         if bound == "hbm":

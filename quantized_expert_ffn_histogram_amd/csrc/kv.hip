@@ -17,9 +17,10 @@
 // [L][Hkv]; a position's Hkv head vectors are contiguous, so a selected
 // position is one contiguous Hkv * 64-byte read.
 //
-// kv_quantize: one wavefront per (token, head) vector: max |x| by a
-//   wavefront reduction, s = fp16(max / 7), q = clamp(rint(x / s), -8, 7);
-//   the code decision is taken in fp32 with IEEE division.
+// kv_quantize: 16 lanes per (token, head) vector: max |x| by a DPP
+//   reduction, s = fp16(max / 7), q = clamp(rint(x / s), -8, 7); the code
+//   decision is that of the fp32 quotient rounded to nearest (taken from an
+//   exact remainder, see the kernel).
 // sparse attention, two kernels:
 //   partial (grid: query token x chunk of 16 selected positions, 256
 //     threads): scores of all query heads against the chunk's keys (each
@@ -44,39 +45,76 @@ constexpr int kPartStride = kKvD + 4;  // floats per (token, head, chunk) partia
 __device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d & 0xFFFF0000u); }
 
-// Each wavefront quantizes kRowsPerWave vectors of D = 128 bf16 values (rows
-// t*Hkv + h): lane l holds elements 2l and 2l+1 of each and writes code byte
-// l.  All of a wavefront's loads are issued before the first reduction.
-// Rows whose slot lies outside [0, L) are skipped.
-constexpr int kRowsPerWave = 4;
+// Each group of 16 lanes quantizes one vector of D = 128 bf16 values (row
+// t*Hkv + h): lane l of the group holds elements 8l .. 8l+7 (one 16-byte
+// load) and writes their 8 codes as one 32-bit word; max |x| is a DPP
+// reduction inside the 16-lane row.  A wavefront does 4 rows per round and
+// kKvRounds rounds, all loads issued before the first reduction.  Rows whose
+// slot lies outside [0, L) are skipped.
+constexpr int kKvRounds = 4;
+constexpr int kKvRowsPerWave = 4 * kKvRounds;
 
-__global__ __launch_bounds__(256) void kv_quantize_kernel(const uint32_t *__restrict__ x, int rows, int Hkv,
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f32<0x124>(v));  // row_ror 4
+  v = fmaxf(v, dpp_f32<0x128>(v));  // row_ror 8
+  return v;
+}
+
+__global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t *__restrict__ x, int rows, int Hkv,
                                                           const int *__restrict__ slots, int L,
                                                           uint8_t *__restrict__ codes, uint16_t *__restrict__ scale) {
-  const int lane = threadIdx.x & 63;
-  const int row0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kRowsPerWave;
-  uint32_t d[kRowsPerWave];
+  const int lane = threadIdx.x & 63, sub = lane & 15;
+  const int wrow0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kKvRowsPerWave + (lane >> 4);
+  u32x4_t d[kKvRounds];
+  int slot[kKvRounds];
 #pragma unroll
-  for (int r = 0; r < kRowsPerWave; ++r) d[r] = row0 + r < rows ? x[(size_t)(row0 + r) * (kKvD / 2) + lane] : 0u;
+  for (int r = 0; r < kKvRounds; ++r) {
+    const int row = wrow0 + 4 * r;
+    d[r] = row < rows ? *reinterpret_cast<const u32x4_t *>(x + (size_t)row * kKvD + 8 * sub) : u32x4_t{0, 0, 0, 0};
+    slot[r] = row < rows ? slots[row / Hkv] : -1;
+  }
 #pragma unroll
-  for (int r = 0; r < kRowsPerWave; ++r) {
-    const int row = row0 + r;
-    if (row >= rows) break;
-    const int t = row / Hkv, h = row - t * Hkv;
-    const int slot = slots[t];
-    const float a = bf16_lo(d[r]), b = bf16_hi(d[r]);
-    const float amax = __uint_as_float(wave_max_u32(__float_as_uint(fmaxf(fabsf(a), fabsf(b)))));
-    if (slot < 0 || slot >= L) continue;
+  for (int r = 0; r < kKvRounds; ++r) {
+    const int row = wrow0 + 4 * r;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_lo(d[r][i]);
+      v[2 * i + 1] = bf16_hi(d[r][i]);
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    const float amax = row16_max(m);  // every lane of the row group reaches this
+    if (slot[r] < 0 || slot[r] >= L) continue;  // also rows past the end
+    const int h = row % Hkv;
     const _Float16 s16 = (_Float16)(amax / 7.0f);
     const float sc = (float)s16;
-    int qa = 0, qb = 0;
-    if (sc > 0.0f) {
-      qa = (int)fminf(fmaxf(__builtin_rintf(a / sc), -8.0f), 7.0f);
-      qb = (int)fminf(fmaxf(__builtin_rintf(b / sc), -8.0f), 7.0f);
+    // q = rint(x / s) with the fp32 quotient rounded to nearest, without a
+    // division per element: q0 = rint(x * (1/s)) is within one of it, the
+    // remainder x - q0*s is exact (an fma; q0*s and x share a narrow range),
+    // and comparing it with s/2 decides, ties to even.  The fp32 quotient
+    // is a half-integer only when x/s is one exactly (x is bf16 and s fp16,
+    // so any other x/s lies further from k + 1/2 than its rounding error),
+    // so this equals rint of the IEEE quotient.
+    const bool zero = !(sc > 0.0f) || sc == __builtin_huge_valf();  // x / s rounds to 0 (all-zero row, s = inf)
+    const float rs = 1.0f / sc, hs = 0.5f * sc;
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float q0 = __builtin_rintf(v[i] * rs);
+      const float e = __builtin_fmaf(-q0, sc, v[i]);
+      int q = (int)q0;
+      if (e > hs || (e == hs && (q & 1))) ++q;
+      else if (e < -hs || (e == -hs && (q & 1))) --q;
+      q = zero ? 0 : min(max(q, -8), 7);
+      word |= (uint32_t)(q + 8) << (4 * i);
     }
-    const size_t dst = (size_t)slot * Hkv + h;
-    codes[dst * (kKvD / 2) + lane] = (uint8_t)((qa + 8) | ((qb + 8) << 4));
-    if (lane == 0) scale[dst] = __builtin_bit_cast(uint16_t, s16);
+    const size_t dst = (size_t)slot[r] * Hkv + h;
+    reinterpret_cast<uint32_t *>(codes + dst * (kKvD / 2))[sub] = word;
+    if (sub == 0) scale[dst] = __builtin_bit_cast(uint16_t, s16);
   }
 }
 
@@ -316,8 +354,7 @@ hipError_t launch_kv_quantize(const uint16_t *x, int T, int Hkv, const int *slot
                               uint16_t *scale, hipStream_t s) {
   const int rows = T * Hkv;
   KernelTimer timer("kv_quantize", s);
-  kv_quantize_kernel<<<ceil_div(rows, 4 * kRowsPerWave), 256, 0, s>>>(reinterpret_cast<const uint32_t *>(x), rows, Hkv, slots, L,
-                                                       codes, scale);
+  kv_quantize_kernel<<<ceil_div(rows, 4 * kKvRowsPerWave), 256, 0, s>>>(x, rows, Hkv, slots, L, codes, scale);
   return hipGetLastError();
 }
 
