@@ -89,7 +89,7 @@ COUNTED_KERNELS = {
 }
 
 
-def record_traffic(fetch_csv: str, write_csv: str, prefill_workload: str) -> dict:
+def record_traffic(fetch_csv: str, write_csv: str, prefill_workload: str, decode_workload: str = "decode") -> dict:
     """HBM bytes per launch from two rocprofv3 --pmc runs of this script with
     --calibrate-copy (FETCH_SIZE, then WRITE_SIZE; both in KiB per dispatch).
     Each counter is scaled by what it reads for the 1 GiB device copy that
@@ -119,7 +119,7 @@ def record_traffic(fetch_csv: str, write_csv: str, prefill_workload: str) -> dic
             continue
         fb = float(np.mean(fk)) * 1024 * f_scale
         wb = float(np.mean(wk)) * 1024 * w_scale
-        workload = prefill_workload if kind == "prefill" else "decode"
+        workload = prefill_workload if kind == "prefill" else decode_workload
         out[f"{kernel}@{workload}"] = {
             "fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb),
             "dispatches": min(len(fk), len(wk)), "source_sha": source_sha(kernel)}
@@ -278,12 +278,12 @@ def bench_prefill(qe, args):
     return cfg, inp, secs, secs_timed, roof, kernels, secs4, steady, timed
 
 
-def bench_decode(qe, args):
+def bench_decode(qe, args, name: str = "decode"):
     import torch
 
     import synth
 
-    cfg = synth.config("decode")
+    cfg = synth.config(name)
     inp = synth.make_inputs(cfg)
     steps = synth.decode_steps(cfg, 64)
     dev = torch.device("cuda:0")
@@ -356,8 +356,11 @@ def bench_decode(qe, args):
         del graphs
     except Exception as exc:  # reported, not hidden
         graph = {"error": str(exc)}
+    shared = "" if cfg.draft_sigma is None else f", drafts' logits = token 0's + {cfg.draft_sigma} N(0,1)"
     return {
-        "workload": "decode: T=4 (1 token + 3 drafts) H=2048 I=512 E=512 k=10 g=64, 64 rotating steps",
+        "workload": f"{cfg.name}: T={cfg.T} (1 token + {cfg.T - 1} drafts{shared}) H={cfg.H} I={cfg.I} E={cfg.E} "
+                    f"k={cfg.k} g={cfg.g}, 64 rotating steps",
+        "distinct_experts_per_step": round(avg_distinct, 2),
         "us_per_step": round(us, 2),
         "device_us_per_step": round(device_us, 2),
         "step_percentiles": pct,
@@ -639,6 +642,8 @@ def main(argv=None) -> int:
     ap.add_argument("--fused", type=int, default=1, help="1: fused weighted scatter-add; 0: y rows + combine")
     ap.add_argument("--router-only", action="store_true",
                     help="time only the router projection + top-k call (router6144) and print its record")
+    ap.add_argument("--decode-only", metavar="WORKLOAD",
+                    help="time only the decode record of WORKLOAD (decode or decode_shared) and print it")
     ap.add_argument("--kv-only", action="store_true",
                     help="time only the 4-bit KV cache encode and sparse attention and print their record")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -648,9 +653,17 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.record_traffic:
-        rec = record_traffic(*args.record_traffic, prefill_workload=args.workload)
+        # Records of other workloads already in the file are kept.
+        rec = record_traffic(*args.record_traffic, prefill_workload=args.workload,
+                             decode_workload=args.decode_only or "decode")
+        try:
+            with open(TRAFFIC_FILE) as f:
+                merged = json.load(f)
+        except (OSError, ValueError):
+            merged = {}
+        merged.update(rec)
         with open(TRAFFIC_FILE, "w") as f:
-            json.dump(rec, f, indent=1, sort_keys=True)
+            json.dump(merged, f, indent=1, sort_keys=True)
             f.write("\n")
         print(json.dumps(rec, indent=1, sort_keys=True))
         return 0
@@ -682,6 +695,9 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         log("[bench] calibration: 3 copies of 1 GiB (read 1 GiB + write 1 GiB each)")
         del src, dst
+    if args.decode_only:
+        print(json.dumps(bench_decode(qe, args, args.decode_only)), flush=True)
+        return 0
 
     cfg, inp, secs, secs_timed, roof, kernels, secs4, steady, timed = bench_prefill(qe, args)
     flops, _ = layer_work(cfg, int((timed["counts"] > 0).sum()))
@@ -714,6 +730,9 @@ def main(argv=None) -> int:
     }
     if not args.no_decode:
         result["decode"] = bench_decode(qe, args)
+        # Drafts that route mostly to the first token's experts: the pairs of
+        # one expert stream the same weight rows on one XCD at the same time.
+        result["decode_shared"] = bench_decode(qe, args, "decode_shared")
     if not args.no_secondary:
         result["secondary"] = bench_secondary(qe, args)
         result["kv_cache"] = bench_kv(qe, args)

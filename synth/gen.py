@@ -51,7 +51,10 @@ class MoEConfig:
     so that expert popularity follows a Zipf law of exponent ``zipf_s``.
     ``weight_std`` is the standard deviation of the expert weights before
     quantization (0.02 for every workload configuration).  ``fmt`` names the
-    weight format (see ``quantize_groups``).
+    weight format (see ``quantize_groups``).  ``draft_sigma`` set means the
+    tokens after the first are drafts whose router logits stay close to the
+    first token's (its row plus ``draft_sigma`` times an independent N(0, 1)
+    row), so that they select mostly the same experts.
     """
 
     name: str
@@ -65,6 +68,7 @@ class MoEConfig:
     zipf_s: float | None = None
     weight_std: float = WEIGHT_STD
     fmt: str = "int4"  # "int4" (symmetric), "int4_asym" (scale + zero point), "int5" (symmetric 5-bit)
+    draft_sigma: float | None = None  # tokens 1.. = token 0's logits + draft_sigma * N(0, 1)
 
     @property
     def pairs(self) -> int:
@@ -92,6 +96,8 @@ CONFIGS: dict[str, MoEConfig] = {
     # a decode step in those formats
     "decode_asym": MoEConfig("decode_asym", T=4, H=2048, I=512, E=512, k=10, g=64, seed=9, fmt="int4_asym"),
     "decode_int5": MoEConfig("decode_int5", T=4, H=2048, I=512, E=512, k=10, g=64, seed=10, fmt="int5"),
+    # a decode step whose 3 drafts route mostly to the first token's experts
+    "decode_shared": MoEConfig("decode_shared", T=4, H=2048, I=512, E=512, k=10, g=64, seed=11, draft_sigma=0.05),
 }
 
 
@@ -230,6 +236,8 @@ def make_logits(cfg: MoEConfig, seq: np.random.SeedSequence, rank_seq=None) -> n
         ranks = np.random.default_rng(rank_seq).permutation(cfg.E) + 1
         bias = (-cfg.zipf_s * np.log(ranks.astype(np.float64))).astype(np.float32)
         logits = logits + bias[None, :]
+    if cfg.draft_sigma is not None and cfg.T > 1:
+        logits[1:] = logits[0][None, :] + np.float32(cfg.draft_sigma) * logits[1:]
     return np.ascontiguousarray(logits, dtype=np.float32)
 
 

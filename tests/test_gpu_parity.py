@@ -325,7 +325,9 @@ def test_layer_graph_replay(qe, name, single):
 
 
 # ----------------------------------------------------------------------------- whole-layer call
-LAYER_CFGS = [synth.config("decode")] + GEMV_CFGS + [
+LAYER_CFGS = [synth.config("decode"), synth.config("decode_shared")] + GEMV_CFGS + [
+    # drafts that share most of the first token's experts, 16 tokens
+    synth.MoEConfig("layer_shared16", T=16, H=1024, I=256, E=64, k=8, g=64, seed=50, draft_sigma=0.05),
     synth.MoEConfig("layer_e1024", T=3, H=512, I=256, E=1024, k=16, g=64, seed=46),
     # k * inter at the two-kernel path's limit, one down row per wavefront
     synth.MoEConfig("layer_i2048", T=2, H=256, I=2048, E=8, k=8, g=128, seed=47),
