@@ -802,9 +802,18 @@ struct GenStage {
   // the fifth-bit word of the half's 32 K values (5-bit)
   uint32_t x[FMT == kFmtInt4 ? 1 : 2 * Shape<kGenW>::kBRows];
 };
+// Ring depth: 3 stages, except for the down kernel in the other formats
+// (their stages carry the side data): 2 there, so that two workgroups fit a
+// CU's LDS.  The gate/up kernel in those formats (K = H, a long K loop) keeps
+// the deeper ring at one workgroup per CU: measured faster for the 5-bit
+// format (486 vs 711 us at the 6144-token chunk), equal for the asymmetric
+// one; the down kernel gains from the second workgroup (307 -> 237, 286 ->
+// 221 us).
+template <int MODE, int FMT>
+constexpr int gen_stages() { return FMT == kFmtInt4 || MODE == 0 ? kGenStages : 2; }
 template <int FMT>
 struct GenRing {
-  GenStage<FMT> *st[kGenStages];
+  GenStage<FMT> *st[kGenStages];  // the first gen_stages() are used
 };
 
 // Segment c (0..7) of token row r: the 8 rows read by one 8-lane group of a
@@ -827,7 +836,7 @@ __device__ __forceinline__ int ga_slot(int r, int c) { return r * 8 + (c ^ (r & 
 template <int MODE, int NMB, int FMT>
 __device__ __forceinline__ void gemm_tile_general(const GemmArgs &a, const GenRing<FMT> &R, const RowTables &rt,
                                                   int e, int row0, int nrows, int slice) {
-  constexpr int S_ = kGenStages;
+  constexpr int S_ = gen_stages<MODE, FMT>();
   constexpr int V = NMB + (FMT == kFmtInt4 ? 2 : 3) * kNB;  // direct-to-LDS loads per stage per wavefront
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
@@ -938,7 +947,7 @@ __device__ __forceinline__ void gemm_tile_general(const GemmArgs &a, const GenRi
   for (int c0 = 0; c0 < nchunks; c0 += S_) {
     step(std::integral_constant<int, 0>{}, c0);
     step(std::integral_constant<int, 1>{}, c0 + 1);
-    step(std::integral_constant<int, 2>{}, c0 + 2);
+    if constexpr (S_ == 3) step(std::integral_constant<int, 2>{}, c0 + 2);
   }
   compiler_fence();
   wait_vmcnt<0>();  // no load of this tile may land in the next tile's stages
@@ -946,13 +955,15 @@ __device__ __forceinline__ void gemm_tile_general(const GemmArgs &a, const GenRi
   epilogue<MODE, kGenW, NMB>(a, rt, acc, row0, nrows, slice, wave, col, half, valid);
 }
 
-// Two workgroups per CU for the symmetric 4-bit format; one for the others,
-// whose stages carry the side data (more LDS).
+// Two workgroups per CU where the LDS allows it (see gen_stages).
 template <int MODE, int FMT>
-__global__ __launch_bounds__(64 * kGenW, FMT == kFmtInt4 ? 2 : 1) void moe_gemm_general(GemmArgs a) {
-  __shared__ GenStage<FMT> st0, st1, st2;
+__global__ __launch_bounds__(64 * kGenW, 2) void moe_gemm_general(GemmArgs a) {
+  __shared__ GenStage<FMT> st0, st1;
+  __shared__ std::conditional_t<gen_stages<MODE, FMT>() == 3, GenStage<FMT>, char> st2;
   __shared__ RowTables rt;
-  const GenRing<FMT> R{{&st0, &st1, &st2}};
+  GenStage<FMT> *third = &st1;  // unused with a 2-stage ring
+  if constexpr (gen_stages<MODE, FMT>() == 3) third = &st2;
+  const GenRing<FMT> R{{&st0, &st1, third}};
   gemm_persistent<MODE>(a, rt, [&](int nmb, const Tile &tile, int slice0, int nsl) {
     dispatch_nmb(nmb, [&](auto n) {
       for (int sl = slice0; sl < slice0 + nsl; ++sl)
@@ -1013,9 +1024,9 @@ hipError_t launch_gemm(GemmArgs args, long long tiles_upper, int matrix_rows, in
     args.spi = 1;
     const long long items = tiles_upper * args.nslices;
     if (fmt == kFmtInt4Asym)
-      moe_gemm_general<MODE, kFmtInt4Asym><<<persistent_grid(items, 1), 64 * kGenW, 0, s>>>(args);
+      moe_gemm_general<MODE, kFmtInt4Asym><<<persistent_grid(items, MODE == 0 ? 1 : 2), 64 * kGenW, 0, s>>>(args);
     else if (fmt == kFmtInt5)
-      moe_gemm_general<MODE, kFmtInt5><<<persistent_grid(items, 1), 64 * kGenW, 0, s>>>(args);
+      moe_gemm_general<MODE, kFmtInt5><<<persistent_grid(items, MODE == 0 ? 1 : 2), 64 * kGenW, 0, s>>>(args);
     else
       moe_gemm_general<MODE, kFmtInt4><<<persistent_grid(items, 2), 64 * kGenW, 0, s>>>(args);
   }
