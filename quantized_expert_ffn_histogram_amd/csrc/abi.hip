@@ -400,7 +400,7 @@ static int layer_impl(const char *fn, const float *logits, const uint16_t *x_bf1
   const FfnWeights fw = ffn_weights(w);
   const FfnWorkspace ws = carve_ffn_workspace(workspace, T, k, E, H, I);
   hipError_t e;
-  if (forced != FfnPath::Gemm && fw.fmt == STRATA_W_INT4 && decode_layer_supported(T, E, k, H, I)) {
+  if (forced != FfnPath::Gemm && decode_layer_supported(T, E, k, H, I)) {
     e = launch_decode_layer(logits, x_bf16, T, k, fw, topk_ids, topk_w, counts, offsets, perm, inv_perm, out, ws, s);
   } else {
     const bool use_gemv = forced == FfnPath::Gemv || (forced == FfnPath::Auto && gemv_ok);

@@ -31,6 +31,9 @@
 // v_dot2_f32_f16 and the exact offset correction per lane, as in the GEMV
 // path (ffn_gemv.hip), except that the activations' odd pairs are held
 // divided by 16 so that half of the nibbles need no shift (dot32_split).
+// The other weight formats fold their zero points or fifth bits into the
+// same dot products (dot32_fmt), with each lane's side data loaded beside its
+// scale.
 #include "gemv_dev.h"
 #include "permute_dev.h"
 #include "route_dev.h"
@@ -53,9 +56,11 @@ struct DecodeArgs {
   int *counts, *offsets, *perm, *inv_perm;
   uint16_t *h;     // fp16 [T*k][I], pair order
   float *out;      // fp32 [T][H]
+  // Other weight formats: zero points or fifth-bit words of gate, up, down.
+  const uint8_t *gate_x, *up_x, *down_x;
 };
 
-template <int EPL, int NCH>
+template <int EPL, int NCH, int FMT>
 __global__ __launch_bounds__(256) void decode_route_gateup_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nroute = (a.T + 3) / 4;
@@ -93,6 +98,7 @@ __global__ __launch_bounds__(256) void decode_route_gateup_kernel(DecodeArgs a) 
   const int n0 = cs * kDecCols + wave * kDecColsPerWave;
   uint4 wg[kDecColsPerWave][NCH], wu[kDecColsPerWave][NCH];
   uint32_t sgb[kDecColsPerWave][NCH], sub_[kDecColsPerWave][NCH];
+  uint32_t xg[kDecColsPerWave][NCH], xu[kDecColsPerWave][NCH];  // side data of the other formats
 #pragma unroll
   for (int cc = 0; cc < kDecColsPerWave; ++cc)
 #pragma unroll
@@ -103,6 +109,8 @@ __global__ __launch_bounds__(256) void decode_route_gateup_kernel(DecodeArgs a) 
       wu[cc][c] = *reinterpret_cast<const uint4 *>(a.up + row * kb + kk / 2);
       sgb[cc][c] = a.gate_s[row * ng + kk / a.g];
       sub_[cc][c] = a.up_s[row * ng + kk / a.g];
+      xg[cc][c] = gemv_aux<FMT>(a.gate_x, row, a.H, a.g, kk);
+      xu[cc][c] = gemv_aux<FMT>(a.up_x, row, a.H, a.g, kk);
     }
   const float on = active ? 1.0f : 0.0f;
   float gs[kDecColsPerWave], us[kDecColsPerWave];
@@ -126,8 +134,15 @@ __global__ __launch_bounds__(256) void decode_route_gateup_kernel(DecodeArgs a) 
     const float corr = 1032.0f * se + 1152.0f * so;
 #pragma unroll
     for (int cc = 0; cc < kDecColsPerWave; ++cc) {
-      gs[cc] += dot32_split<false>(wg[cc][c], xp, corr, on * half_bits_to_float((uint16_t)sgb[cc][c]));
-      us[cc] += dot32_split<false>(wu[cc][c], xp, corr, on * half_bits_to_float((uint16_t)sub_[cc][c]));
+      const float sg = on * half_bits_to_float((uint16_t)sgb[cc][c]);
+      const float su = on * half_bits_to_float((uint16_t)sub_[cc][c]);
+      if constexpr (FMT == 0) {
+        gs[cc] += dot32_split<false>(wg[cc][c], xp, corr, sg);
+        us[cc] += dot32_split<false>(wu[cc][c], xp, corr, su);
+      } else {
+        gs[cc] += dot32_fmt<false, FMT>(wg[cc][c], xp, se, so, sg, xg[cc][c]);
+        us[cc] += dot32_fmt<false, FMT>(wu[cc][c], xp, se, so, su, xu[cc][c]);
+      }
     }
   }
 #pragma unroll
@@ -143,7 +158,7 @@ __global__ __launch_bounds__(256) void decode_route_gateup_kernel(DecodeArgs a) 
   }
 }
 
-template <int LPR, int KMAX>  // lanes per down row = I / 32; KMAX >= k
+template <int LPR, int KMAX, int FMT>  // lanes per down row = I / 32; KMAX >= k
 __global__ __launch_bounds__(256) void decode_down_combine_kernel(DecodeArgs a) {
   constexpr int RPW = kWave / LPR;  // rows per wavefront
   constexpr int kRowsWG = 4 * RPW;  // output rows per workgroup
@@ -184,19 +199,21 @@ __global__ __launch_bounds__(256) void decode_down_combine_kernel(DecodeArgs a) 
   // Row n of each pair's expert: this lane's 32 K values (16 bytes) and their scale.
   const int kb = a.I / 2, ng = a.I / a.g;
   uint4 wq[KMAX];
-  uint32_t sdb[KMAX];
+  uint32_t sdb[KMAX], xd[KMAX];
 #pragma unroll
   for (int jj = 0; jj < KMAX; ++jj) {
     const int e = __builtin_amdgcn_readlane(eid, jj < a.k ? jj : a.k - 1);  // past k: repeat the last row
     const size_t row = (size_t)e * a.H + nc;
     wq[jj] = *reinterpret_cast<const uint4 *>(a.down + row * kb + 16 * sub);
     sdb[jj] = a.down_s[row * ng + (32 * sub) / a.g];
+    xd[jj] = gemv_aux<FMT>(a.down_x, row, a.I, a.g, 32 * sub);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wavefront's h loads have landed
   __syncthreads();                                 // ... and everyone's
   // Sum of each 32-value chunk of h (the offset correction of the dot
   // products), once per chunk: thread tid sums chunks tid, tid + 256, ...
   __shared__ float hsums[kDecodeMaxKI / 32];
+  __shared__ float hse[FMT == 0 ? 1 : kDecodeMaxKI / 32], hso[FMT == 0 ? 1 : kDecodeMaxKI / 32];
   for (int c = tid; c < a.k * a.I / 32; c += 256) {
     const uint4 *hc = hs + 4 * c;
     float se = 0.0f, so = 0.0f;
@@ -207,6 +224,10 @@ __global__ __launch_bounds__(256) void decode_down_combine_kernel(DecodeArgs a) 
       so += pair_sum(__builtin_bit_cast(half2_t, u.y)) + pair_sum(__builtin_bit_cast(half2_t, u.w));
     }
     hsums[c] = 1032.0f * se + 1152.0f * so;  // the offset term of dot32_split
+    if constexpr (FMT != 0) {  // the other formats' offset terms need both sums
+      hse[c] = se;
+      hso[c] = so;
+    }
   }
   __syncthreads();
 
@@ -225,39 +246,71 @@ __global__ __launch_bounds__(256) void decode_down_combine_kernel(DecodeArgs a) 
         hp[4 * q + 2] = __builtin_bit_cast(half2_t, u.z);
         hp[4 * q + 3] = __builtin_bit_cast(half2_t, u.w);
       }
-      const float corr = hsums[(jj * a.I) / 32 + sub];
+      const int hc = (jj * a.I) / 32 + sub;
       const float wsel = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), jj));
-      acc += wsel * dot32_split<true>(wq[jj], hp, corr, half_bits_to_float((uint16_t)sdb[jj]));
+      const float sd = half_bits_to_float((uint16_t)sdb[jj]);
+      if constexpr (FMT == 0)
+        acc += wsel * dot32_split<true>(wq[jj], hp, hsums[hc], sd);
+      else
+        acc += wsel * dot32_fmt<true, FMT>(wq[jj], hp, hse[hc], hso[hc], sd, xd[jj]);
     }
   }
   const float y = dpp_group_sum<LPR>(acc);
   if (sub == 0 && n < a.H) a.out[(size_t)t * a.H + n] = y;
 }
 
-template <int LPR>
+template <int LPR, int FMT>
 void launch_down_combine(const DecodeArgs &a, int grid, hipStream_t s) {
   if (a.k <= 4)
-    decode_down_combine_kernel<LPR, 4><<<grid, 256, 0, s>>>(a);
+    decode_down_combine_kernel<LPR, 4, FMT><<<grid, 256, 0, s>>>(a);
   else if (a.k <= 8)
-    decode_down_combine_kernel<LPR, 8><<<grid, 256, 0, s>>>(a);
+    decode_down_combine_kernel<LPR, 8, FMT><<<grid, 256, 0, s>>>(a);
   else if (a.k <= 12)  // k = 10: 2 repeated row loads per lane instead of 6
-    decode_down_combine_kernel<LPR, 12><<<grid, 256, 0, s>>>(a);
+    decode_down_combine_kernel<LPR, 12, FMT><<<grid, 256, 0, s>>>(a);
   else
-    decode_down_combine_kernel<LPR, 16><<<grid, 256, 0, s>>>(a);
+    decode_down_combine_kernel<LPR, 16, FMT><<<grid, 256, 0, s>>>(a);
 }
 
-template <int NCH>
+template <int NCH, int FMT>
 void launch_route_gateup(const DecodeArgs &a, int grid, hipStream_t s) {
   if (a.E <= 64)
-    decode_route_gateup_kernel<1, NCH><<<grid, 256, 0, s>>>(a);
+    decode_route_gateup_kernel<1, NCH, FMT><<<grid, 256, 0, s>>>(a);
   else if (a.E <= 128)
-    decode_route_gateup_kernel<2, NCH><<<grid, 256, 0, s>>>(a);
+    decode_route_gateup_kernel<2, NCH, FMT><<<grid, 256, 0, s>>>(a);
   else if (a.E <= 256)
-    decode_route_gateup_kernel<4, NCH><<<grid, 256, 0, s>>>(a);
+    decode_route_gateup_kernel<4, NCH, FMT><<<grid, 256, 0, s>>>(a);
   else if (a.E <= 512)
-    decode_route_gateup_kernel<8, NCH><<<grid, 256, 0, s>>>(a);
+    decode_route_gateup_kernel<8, NCH, FMT><<<grid, 256, 0, s>>>(a);
   else
-    decode_route_gateup_kernel<16, NCH><<<grid, 256, 0, s>>>(a);
+    decode_route_gateup_kernel<16, NCH, FMT><<<grid, 256, 0, s>>>(a);
+}
+
+// The two kernels of one weight format.
+template <int FMT>
+void launch_decode_kernels(const DecodeArgs &a, int T, int k, const FfnWeights &w, hipStream_t s, hipError_t &err) {
+  {
+    KernelTimer timer("decode_route_gateup", s);
+    const int grid = (T + 3) / 4 + T * k * (w.I / kDecCols);
+    if (w.H <= 2048)
+      launch_route_gateup<1, FMT>(a, grid, s);
+    else
+      launch_route_gateup<kDecMaxChunks, FMT>(a, grid, s);
+  }
+  if ((err = hipGetLastError()) != hipSuccess) return;
+  {
+    KernelTimer timer("decode_down_combine", s);
+    const int lpr = w.I / 32;
+    const int rows_wg = 4 * (kWave / lpr);
+    const int grid = 1 + T * ((w.H + rows_wg - 1) / rows_wg);
+    switch (lpr) {
+      case 4: launch_down_combine<4, FMT>(a, grid, s); break;
+      case 8: launch_down_combine<8, FMT>(a, grid, s); break;
+      case 16: launch_down_combine<16, FMT>(a, grid, s); break;
+      case 32: launch_down_combine<32, FMT>(a, grid, s); break;
+      default: launch_down_combine<64, FMT>(a, grid, s); break;
+    }
+  }
+  err = hipGetLastError();
 }
 
 }  // namespace
@@ -293,30 +346,17 @@ hipError_t launch_decode_layer(const float *logits, const uint16_t *x, int T, in
   a.inv_perm = inv_perm;
   a.h = ws.h;
   a.out = out;
-  {
-    KernelTimer timer("decode_route_gateup", s);
-    const int grid = (T + 3) / 4 + T * k * (w.I / kDecCols);
-    if (w.H <= 2048)
-      launch_route_gateup<1>(a, grid, s);
-    else
-      launch_route_gateup<kDecMaxChunks>(a, grid, s);
-  }
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  {
-    KernelTimer timer("decode_down_combine", s);
-    const int lpr = w.I / 32;
-    const int rows_wg = 4 * (kWave / lpr);
-    const int grid = 1 + T * ((w.H + rows_wg - 1) / rows_wg);
-    switch (lpr) {
-      case 4: launch_down_combine<4>(a, grid, s); break;
-      case 8: launch_down_combine<8>(a, grid, s); break;
-      case 16: launch_down_combine<16>(a, grid, s); break;
-      case 32: launch_down_combine<32>(a, grid, s); break;
-      default: launch_down_combine<64>(a, grid, s); break;
-    }
-  }
-  return hipGetLastError();
+  a.gate_x = w.gate_x;
+  a.up_x = w.up_x;
+  a.down_x = w.down_x;
+  hipError_t err = hipSuccess;
+  if (w.fmt == 1)
+    launch_decode_kernels<1>(a, T, k, w, s, err);
+  else if (w.fmt == 2)
+    launch_decode_kernels<2>(a, T, k, w, s, err);
+  else
+    launch_decode_kernels<0>(a, T, k, w, s, err);
+  return err;
 }
 
 }  // namespace strata

@@ -65,19 +65,6 @@ struct GemvArgs {
   const uint8_t *gate_x, *up_x, *down_x;
 };
 
-// The side data of one lane's 32 weights (K from kk) of matrix row `row`
-// (K elements per row, group g): its group's zero point (format 1) or its
-// fifth-bit word (format 2); 0 for format 0.
-template <int FMT>
-__device__ __forceinline__ uint32_t gemv_aux(const uint8_t *x, size_t row, int K, int g, int kk) {
-  if constexpr (FMT == 1) {
-    const int grp = kk / g;
-    return (x[row * (K / g / 2) + (grp >> 1)] >> (4 * (grp & 1))) & 15u;
-  } else if constexpr (FMT == 2) {
-    return reinterpret_cast<const uint32_t *>(x)[row * (K / 32) + kk / 32];
-  }
-  return 0u;
-}
 
 struct Entry {
   int e, row0, rows, nnz;  // e < 0: no such entry

@@ -11,7 +11,8 @@ words).
   code value goes untested.
 * The 6144-token prefill chunk (H 2048, I 512, 512 experts, top-10, g 64) in
   each format through the single layer call the benchmark times, every
-  output element; the 4-token decode step in each format.
+  output element; the 4-token decode step in each format (the two-kernel
+  decode layer), and the GEMV shapes through both combine modes.
 
 Tolerances are those of the symmetric format (the same fp16-operand and
 fp32-accumulation envelope): max |err| <= 2e-2 RMS(out), sum |err| / sum |out|
@@ -125,8 +126,8 @@ def _check_routing(res, ref):
 
 @pytest.mark.parametrize("name", ["decode_asym", "decode_int5"])
 def test_format_decode_layer_call(qe, name):
-    """strata_moe_layer on a decode step: the other formats run the GEMV path
-    (the two-kernel fused decode layer takes symmetric 4-bit weights only)."""
+    """strata_moe_layer on a decode step runs the two-kernel decode layer in
+    the other formats too."""
     inp = inputs(name)
     cfg = inp.cfg
     logits, x, ex = to_device(inp)
@@ -134,7 +135,7 @@ def test_format_decode_layer_call(qe, name):
     res = qe.layer(logits, x, ex, cfg.k)
     names = qe.timing_kernels()
     qe.timing_enable(False)
-    assert "decode_route_gateup" not in names and "gemv_gateup" in names, names
+    assert "decode_route_gateup" in names and "decode_down_combine" in names, names
     ref = oracle.moe_layer(inp.logits, inp.x_bf16, inp.weights, cfg.k, cfg.g)
     _check_routing(res, ref)
     check_close(_np(res["out"]), ref["out"], f"{name} out")
@@ -158,3 +159,19 @@ def test_format_layer_call_full_size(qe, name):
     _check_routing(res, ref)
     stats = check_close(_np(run.out), ref["out"], f"{name} out (all {cfg.T * cfg.H} elements)")
     print(f"[formats] {name}: {stats}", flush=True)
+
+
+@pytest.mark.parametrize("cfg", _gemv_cfgs("int4_asym") + _gemv_cfgs("int5"), ids=lambda c: c.name)
+def test_format_decode_layer_shapes(qe, cfg):
+    """The two-kernel decode layer on the GEMV shapes (T = 16, 1, 8; H up to
+    4096), and on every bit pattern of codes, zero points and fifth bits."""
+    for inp in (inputs(cfg), _all_patterns(inputs(cfg), 73)):
+        logits, x, ex = to_device(inp)
+        qe.timing_enable(True)
+        res = qe.layer(logits, x, ex, cfg.k)
+        names = qe.timing_kernels()
+        qe.timing_enable(False)
+        assert "decode_route_gateup" in names, names
+        ref = oracle.moe_layer(inp.logits, inp.x_bf16, inp.weights, cfg.k, cfg.g)
+        _check_routing(res, ref)
+        check_close(_np(res["out"]), ref["out"], f"{cfg.name} out")
