@@ -22,7 +22,7 @@
 //   decision is that of the fp32 quotient rounded to nearest (taken from an
 //   exact remainder, see the kernel).
 // sparse attention, two kernels:
-//   partial (grid: query token x chunk of 16 selected positions, 256
+//   partial (grid: query token x chunk of 32 selected positions, 256
 //     threads): scores of all query heads against the chunk's keys (each
 //     thread a quarter of a head vector, quad reduction), the chunk's
 //     softmax numerators, and the weighted sum of its values, which were
@@ -39,7 +39,7 @@ namespace {
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kKvD = 128;        // head_dim
-constexpr int kAttnChunk = 16;   // selected positions per workgroup
+constexpr int kAttnChunk = 32;   // selected positions per workgroup
 constexpr int kPartStride = kKvD + 4;  // floats per (token, head, chunk) partial: output, max, sum, pad
 
 __device__ __forceinline__ float bf16_lo(uint32_t d) { return __uint_as_float(d << 16); }
