@@ -372,7 +372,7 @@ int strata_kv_quantize(const uint16_t *x_bf16, int32_t T, int32_t Hkv, int32_t D
  *   out      out float32 [Tq][Hq][D]:
  *                out[t][h] = sum_i p_i v[sel[t][i]][h / (Hq/Hkv)],
  *                p = softmax_i(sm_scale * q[t][h] . k[sel[t][i]][...]),
- *                in fp32; chunks of 32 positions are combined in a fixed
+ *                in fp32; chunks of 32 or 64 positions are combined in a fixed
  *                order, so the result is deterministic.
  *   workspace  device scratch of strata_sparse_attention_workspace_size(Tq,
  *              Hq, n_sel) bytes, 256-byte aligned.

@@ -145,6 +145,8 @@ def _attn_case(qe, cfg, use_sel=True):
         dict(Hkv=2, Hq=4, n_sel=64),                   # 2:1
         dict(Hkv=1, Hq=1, n_sel=257, L=300),           # one head, 9 chunks
         dict(Hkv=8, Hq=8, n_sel=77),                   # one query head per KV head
+        dict(Tq=64, n_sel=300),                        # 64-position chunks (>= 256 workgroups), ragged tail
+        dict(Tq=128, n_sel=130, Hkv=4, Hq=16),         # 64-position chunks, a 2-position last chunk
     ],
     ids=lambda d: "-".join(f"{k}{v}" for k, v in d.items()) or "default",
 )
