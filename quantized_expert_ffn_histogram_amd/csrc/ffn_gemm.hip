@@ -29,9 +29,11 @@
 //     double-buffered window.  This halves the vector-memory instructions and
 //     cache sectors per flop of the general pipeline, which is what bounds
 //     these kernels (the per-CU load path, not HBM bandwidth).  Needs the
-//     groups per row, K/g, to be a multiple of 8.
+//     groups per row, K/g, to be a multiple of 8.  Symmetric 4-bit and, with
+//     a window of zero points beside the scales, asymmetric 4-bit.
 //   * general: 4 wavefronts, two workgroups per CU, K chunks of 64 in a
-//     3-stage ring, one 2-byte scale load per row and chunk.
+//     3-stage ring, one 2-byte scale load per row and chunk; every format
+//     (5-bit only here: its fifth-bit words do not fit the wide LDS budget).
 //
 // Dequant in registers: a dword holds 8 nibbles u_0..u_7 (even K low); the
 // pair (u_m, u_{m+4}) goes into the mantissas of two fp16 values with one
@@ -264,12 +266,18 @@ __device__ __forceinline__ half8 dequant8_c(uint32_t d, half2_t s2, const Dequan
 // Piece q (0..3) of the dequantization of one packed dword for both weight
 // blocks: fp16 pair q of the eight weights (see dequant8_c), for block 0 and
 // block 1 side by side so that no two dependent packed operations are
-// adjacent.
+// adjacent.  Symmetric 4-bit: s2 = (s, s).  Asymmetric 4-bit: s2 = (s, ce)
+// with ce = -(1024 + z) for the group's zero point z, so q = u - z is
+// (1024 + u) + ce for a low nibble and (1024 + 16u)/16 + (ce + 960) for the
+// next one, both exact, then one multiply by s.
+template <int FMT>
 __device__ __forceinline__ void dequant_piece(int q, const uint32_t (&d)[kNB], const half2_t (&s2)[kNB],
                                               const DequantRegs &k, uint32_t (&out)[kNB][4]) {
+  static_assert(FMT == kFmtInt4 || FMT == kFmtInt4Asym, "wide pipeline formats");
   const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
   const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
   const half2_t off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
+  const half2_t c960 = {(_Float16)960.0f, (_Float16)960.0f};
   uint32_t r[kNB];
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
@@ -279,8 +287,15 @@ __device__ __forceinline__ void dequant_piece(int q, const uint32_t (&d)[kNB], c
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
     const half2_t v = __builtin_bit_cast(half2_t, r[nb]);
-    const half2_t qv = (q & 1) ? __builtin_elementwise_fma(v, sixteenth, off16) : v - off;
-    out[nb][q] = __builtin_bit_cast(uint32_t, qv * s2[nb]);
+    if constexpr (FMT == kFmtInt4) {
+      const half2_t qv = (q & 1) ? __builtin_elementwise_fma(v, sixteenth, off16) : v - off;
+      out[nb][q] = __builtin_bit_cast(uint32_t, qv * s2[nb]);
+    } else {
+      const half2_t sb = __builtin_shufflevector(s2[nb], s2[nb], 0, 0);
+      const half2_t cb = __builtin_shufflevector(s2[nb], s2[nb], 1, 1);
+      const half2_t qv = (q & 1) ? __builtin_elementwise_fma(v, sixteenth, cb + c960) : v + cb;
+      out[nb][q] = __builtin_bit_cast(uint32_t, qv * sb);
+    }
   }
 }
 
@@ -292,7 +307,7 @@ __device__ __forceinline__ void dequant_piece(int q, const uint32_t (&d)[kNB], c
 // mb's fragment of K-step j; `pre(j)` runs at the start of K-step j.  Each
 // token block's group (two MFMAs, one fragment read, its dequant pieces) is
 // closed by a scheduling barrier, so the order is the source order.
-template <int NMB, typename BRead, typename AFrag, typename Pre>
+template <int NMB, int FMT, typename BRead, typename AFrag, typename Pre>
 __device__ __forceinline__ void mma_stage_pipelined(floatx16 (&acc)[NMB][kNB], BRead &&bread,
                                                     const half2_t (&s2)[2][kNB], AFrag &&afrag, Pre &&pre) {
   const DequantRegs k = dequant_regs();
@@ -308,7 +323,7 @@ __device__ __forceinline__ void mma_stage_pipelined(floatx16 (&acc)[NMB][kNB], B
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) d[nb] = dword_of(bw[nb], 0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) dequant_piece(q, d, s2[0], k, bf[0]);
+    for (int q = 0; q < 4; ++q) dequant_piece<FMT>(q, d, s2[0], k, bf[0]);
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -327,7 +342,8 @@ __device__ __forceinline__ void mma_stage_pipelined(floatx16 (&acc)[NMB][kNB], B
       if (j < 7) {
         af[mb] = afrag(jn, mb);
 #pragma unroll
-        for (int q = mb * 4 / NMB; q < (mb + 1) * 4 / NMB; ++q) dequant_piece(q, d, s2[jn >> 2], k, bf[cur ^ 1]);
+        for (int q = mb * 4 / NMB; q < (mb + 1) * 4 / NMB; ++q)
+          dequant_piece<FMT>(q, d, s2[jn >> 2], k, bf[cur ^ 1]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -550,6 +566,12 @@ struct WideStage {
 struct ScaleWindow {
   uint4 s[Shape<kWideW>::kBRows];  // weight rows: fp16 scales of 8 consecutive groups
 };
+// Asymmetric 4-bit: the zero points of the same 8 groups (4 bytes per row,
+// group i of the window in bits 4i..4i+3); a placeholder otherwise.
+template <int FMT>
+struct ZeroWindow {
+  uint32_t z[FMT == kFmtInt4Asym ? Shape<kWideW>::kBRows : 1];
+};
 
 // Segment c (0..15) of token row r: 16 consecutive rows read by a ds_read_b128
 // lane group land on 16 different bank quads.
@@ -563,7 +585,8 @@ __device__ __forceinline__ int wb_slot(int br, int q) { return br * 4 + (q ^ ((b
 //   * packed weights: 2 per block, 16 rows x 64 bytes each;
 //   * on the first stage of every 8-group window: one 16-byte scale load per
 //     weight row of the wavefront (64 rows), into the window buffer of the
-//     window's parity.
+//     window's parity (asymmetric 4-bit: and one 4-byte load of the window's
+//     zero points per row, into the zero window of the same parity).
 // Step c: wait for this wavefront's loads, one barrier (every wavefront's
 // loads of stage c landed, and everyone is done with stage c-1, whose buffer
 // is next), read this stage's scales, then dequant + MFMAs, with the loads of
@@ -574,10 +597,11 @@ __device__ __forceinline__ int wb_slot(int br, int q) { return br * 4 + (q ^ ((b
 // tile.  The K stages of consecutive slices form one pipeline: while the last
 // stage of a slice is computed the first stage of the next is already in
 // flight, and the slice's epilogue runs while it lands.
-template <int MODE, int NMB>
+template <int MODE, int NMB, int FMT>
 __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0, WideStage &st1, ScaleWindow &sw0,
-                                               ScaleWindow &sw1, const RowTables &rt, int e, int row0, int nrows,
-                                               int slice0, int nsl) {
+                                               ScaleWindow &sw1, ZeroWindow<FMT> &zw0, ZeroWindow<FMT> &zw1,
+                                               const RowTables &rt, int e, int row0, int nrows, int slice0,
+                                               int nsl) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wavefront-uniform
   const int col = lane & 31, half = lane >> 5;
@@ -611,10 +635,12 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
   // rb / rs are buffer resources over that slice's weight rows and scale rows
   // of this wavefront's two blocks (32 rows each).
   constexpr int kRes = kNB;
+  constexpr bool kAsym = FMT == kFmtInt4Asym;
   int lsl = slice0, lc = 0;
-  __amdgpu_buffer_rsrc_t rb[kRes], rs[kRes];
-  // This lane's scale row in its block.
+  __amdgpu_buffer_rsrc_t rb[kRes], rs[kRes], rz[kAsym ? kRes : 1];
+  // This lane's scale row (and zero-point row) in its block.
   const uint32_t soff = (uint32_t)col * ngr * 2;
+  const uint32_t zoff = (uint32_t)col * (ngr / 2);
   auto bases = [&](int sl) {
     const bool v = weight_row0<MODE, kWideW>(sl, wave, 0) < a.N;
     const char *bb[kNB];
@@ -624,6 +650,11 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
     for (int r = 0; r < kRes; ++r) {
       rb[r] = buffer_rsrc(bb[r], 32u * (uint32_t)a.K / 2);
       rs[r] = buffer_rsrc(sb[r], 32u * (uint32_t)ngr * 2);
+      if constexpr (kAsym) {
+        const int n0 = v ? weight_row0<MODE, kWideW>(sl, wave, r) : 0;
+        const uint8_t *X = MODE == 0 && r >= kNB / 2 ? a.X1 : a.X0;
+        rz[r] = buffer_rsrc(X + ((size_t)e * a.N + n0) * (size_t)(ngr / 2), 32u * (uint32_t)(ngr / 2));
+      }
     }
   };
   bases(lsl);
@@ -652,14 +683,26 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
   };
   // Scale window of the cursor's stage, if it starts one: lanes 0-31 load the
   // rows of block 0, lanes 32-63 those of block 1 (16 bytes = 8 groups each).
+  // Asymmetric 4-bit: the window's zero points likewise, 4 bytes per row
+  // (the wide pipeline takes this format only when K/g is a multiple of 8,
+  // so every row's window is a whole aligned dword).
   auto issue_s = [&]() {
     if ((lc & ((1 << lpw) - 1)) == 0) {
       const int win = lc >> lpw;
-      const lds_ptr_t dst = window_odd(lsl, win) ? lds_at(sw1.s, lds_w1k) : lds_at(sw0.s, lds_w1k);
+      const bool odd = window_odd(lsl, win);
+      const lds_ptr_t dst = odd ? lds_at(sw1.s, lds_w1k) : lds_at(sw0.s, lds_w1k);
       if (half == 0)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[0], dst, 16, soff, 16u * win, 0, 0);
       else
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[1], dst, 16, soff, 16u * win, 0, 0);
+      if constexpr (kAsym) {
+        const uint32_t zw = lds_w1k >> 2;  // 256 bytes per wavefront
+        const lds_ptr_t zdst = odd ? lds_at(zw1.z, zw) : lds_at(zw0.z, zw);
+        if (half == 0)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rz[0], zdst, 4, zoff, 4u * win, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rz[kRes - 1], zdst, 4, zoff, 4u * win, 0, 0);
+      }
     }
   };
   // The loads of the cursor's stage, spread over the 8 K-steps (kk) of the
@@ -709,7 +752,15 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
     refresh_lds_offsets();
     // Scales of this stage's two 64-K halves (group of K offset kc + 32*half).
     const int win = c >> lpw;
-    const ScaleWindow &sw = window_odd(sl, win) ? sw1 : sw0;
+    const bool odd = window_odd(sl, win);
+    const ScaleWindow &sw = odd ? sw1 : sw0;
+    // Asymmetric 4-bit: (s, ce), ce = -(1024 + z) (fp16 bits 0xE400 | z).
+    uint32_t zwin[kNB];
+    if constexpr (kAsym) {
+      const ZeroWindow<FMT> &zw = odd ? zw1 : zw0;
+#pragma unroll
+      for (int nb = 0; nb < kNB; ++nb) zwin[nb] = zw.z[brow_of(wave, nb, col)];
+    }
     half2_t s2[2][kNB];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -717,15 +768,20 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
         const uint16_t bits = reinterpret_cast<const uint16_t *>(&sw.s[brow_of(wave, nb, col)])[grp];
-        const _Float16 sv = __builtin_bit_cast(_Float16, bits);
-        s2[s][nb] = half2_t{sv, sv};
+        if constexpr (kAsym) {
+          const uint32_t ce = 0xE400u | ((zwin[nb] >> (4 * grp)) & 15u);
+          s2[s][nb] = __builtin_bit_cast(half2_t, (uint32_t)bits | (ce << 16));
+        } else {
+          const _Float16 sv = __builtin_bit_cast(_Float16, bits);
+          s2[s][nb] = half2_t{sv, sv};
+        }
       }
     }
     compiler_fence();
     // The scale window of the cursor's stage, if it starts one (the buffer it
     // fills was last read two windows ago).
     if constexpr (MORE) issue_s();
-    mma_stage_pipelined<NMB>(
+    mma_stage_pipelined<NMB, FMT>(
         acc, [&](int h, int nb) { return cur.b[wb_slot(brow_of(wave, nb, col), 2 * h + half)]; }, s2,
         [&](int j, int mb) {
           return __builtin_bit_cast(half8, cur.a[wa_slot(mb * 32 + col, 8 * (j >> 2) + 4 * half + (j & 3))]);
@@ -773,15 +829,16 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
 
 // The ring stages and scale windows are distinct LDS objects so the compiler
 // tracks each one's direct-to-LDS loads separately.
-template <int MODE>  // 0: gate/up + silu*mul -> h;  1: down -> y
+template <int MODE, int FMT>  // MODE 0: gate/up + silu*mul -> h;  1: down -> y
 __global__ __launch_bounds__(64 * kWideW, 1) void moe_gemm_wide(GemmArgs a) {
   __shared__ WideStage st0, st1;
   __shared__ ScaleWindow sw0, sw1;
+  __shared__ ZeroWindow<FMT> zw0, zw1;
   __shared__ RowTables rt;
   gemm_persistent<MODE>(a, rt, [&](int nmb, const Tile &tile, int slice0, int nsl) {
     dispatch_nmb(nmb, [&](auto n) {
-      gemm_tile_wide<MODE, decltype(n)::value>(a, st0, st1, sw0, sw1, rt, tile.e, tile.row0, tile.rows, slice0,
-                                               nsl);
+      gemm_tile_wide<MODE, decltype(n)::value, FMT>(a, st0, st1, sw0, sw1, zw0, zw1, rt, tile.e, tile.row0,
+                                                    tile.rows, slice0, nsl);
     });
   });
 }
@@ -1005,8 +1062,11 @@ int persistent_grid(long long work_upper, int wg_per_cu) {
 template <int MODE>
 hipError_t launch_gemm(GemmArgs args, long long tiles_upper, int matrix_rows, int fmt, hipStream_t s) {
   // The wide pipeline addresses A through a buffer resource: 32-bit offsets.
-  // The asymmetric and 5-bit formats run on the general pipeline.
-  const bool wide = STRATA_GEMM_WIDE && fmt == kFmtInt4 && args.K % kKS == 0 &&
+  // It takes the asymmetric format when K/g is a multiple of 8 (whole zero-
+  // point windows); the 5-bit format's fifth-bit words do not fit its LDS,
+  // so that one runs on the general pipeline.
+  const bool wide_fmt = fmt == kFmtInt4 || (fmt == kFmtInt4Asym && (args.K / args.g) % 8 == 0);
+  const bool wide = STRATA_GEMM_WIDE && wide_fmt && args.K % kKS == 0 &&
                     ((args.K / args.g) % 8 == 0 || args.K / args.g < 8) &&
                     (long long)args.a_rows * args.K * 2 < (1LL << 32);
   if (wide) {
@@ -1017,7 +1077,10 @@ hipError_t launch_gemm(GemmArgs args, long long tiles_upper, int matrix_rows, in
     const int nst = args.K / kKS;
     args.spi = std::max(1, std::min(args.nslices, (STRATA_WIDE_MIN_STAGES + nst - 1) / nst));
     const long long items = tiles_upper * ((args.nslices + args.spi - 1) / args.spi);
-    moe_gemm_wide<MODE><<<persistent_grid(items, 1), 64 * kWideW, 0, s>>>(args);
+    if (fmt == kFmtInt4Asym)
+      moe_gemm_wide<MODE, kFmtInt4Asym><<<persistent_grid(items, 1), 64 * kWideW, 0, s>>>(args);
+    else
+      moe_gemm_wide<MODE, kFmtInt4><<<persistent_grid(items, 1), 64 * kWideW, 0, s>>>(args);
   } else {
     const int width = MODE == 0 ? Shape<kGenW>::kHCols : Shape<kGenW>::kOutCols;
     args.nslices = (matrix_rows + width - 1) / width;

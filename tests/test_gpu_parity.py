@@ -124,6 +124,14 @@ def test_permute_bitexact(qe, name):
         (1025, 300, 1, "random"),   # 1025 pairs: segmented path, ragged last segment
         (3001, 64, 7, "skewed"),
         (2048, 1024, 1, "empty_half"),
+        # segments of 1024 pairs; the scan reads each expert's column in
+        # batches of 32 segments
+        (131072, 512, 1, "random"),  # 128 segments: four whole batches
+        (131073, 512, 1, "random"),  # 129 segments: one pair in the last
+        (65536, 1024, 1, "random"),  # 64 segments at E = 1024
+        (65537, 1024, 1, "random"),  # 65 segments at E = 1024
+        (40000, 16, 4, "one_hot"),   # 157 full segments of one expert
+        (200000, 8, 5, "skewed"),    # 977 segments
     ],
 )
 def test_permute_edge_cases(qe, T, E, k, kind):
