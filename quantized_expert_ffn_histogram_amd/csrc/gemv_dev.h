@@ -40,13 +40,32 @@ __device__ __forceinline__ float pair_sum(half2_t p) { return (float)p.x + (floa
 // stored odd-pair x/16) and the result is s * (acc - corr).  Per lane (32 K
 // values, inside one scale group) the offset cancels exactly while x/16 is an
 // fp16 normal.
-// kFused: each nibble pair as one v_and_or_b32 (and_or_sv); otherwise
-// plain and + or, which leaves the compiler more freedom to schedule (the
-// gate/up kernel keeps its register count that way).
+// Nibble masks in SGPRs and the fp16 exponent pattern in a VGPR, through
+// asm the compiler cannot see into: (d & mask) | magic written as plain C
+// then becomes one v_and_or_b32 (VOP3 takes no literal operands here, so with
+// the constants visible the compiler emits a separate and and or), and the
+// scheduler places it freely.
+struct PairRegs {
+  uint32_t m0, m4, magic;
+};
+__device__ __forceinline__ PairRegs pair_regs() {
+  PairRegs r;
+  asm("s_mov_b32 %0, 0xf000f" : "=s"(r.m0));
+  asm("s_mov_b32 %0, 0xf000f0" : "=s"(r.m4));
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(r.magic));
+  return r;
+}
+
+// kFused: each nibble pair as one v_and_or_b32 (and_or_sv, volatile);
+// otherwise the same instruction from plain C over pair_regs(), which leaves
+// the compiler free to schedule it (the gate/up kernels keep their register
+// counts that way).
 template <bool kFused>
 __device__ __forceinline__ float dot32_split(const uint4 wq, const half2_t *xp, float corr, float s) {
-  auto pair = [](uint32_t d, uint32_t m) {
-    return __builtin_bit_cast(half2_t, kFused ? and_or_sv(d, m, 0x64006400u) : ((d & m) | 0x64006400u));
+  const PairRegs k = pair_regs();
+  auto pair = [&](uint32_t d, uint32_t m) {
+    return __builtin_bit_cast(half2_t, kFused ? and_or_sv(d, m, 0x64006400u)
+                                              : ((d & (m == 0x000F000Fu ? k.m0 : k.m4)) | k.magic));
   };
   float acc = 0.0f;
   const uint32_t d[4] = {wq.x, wq.y, wq.z, wq.w};
@@ -72,8 +91,9 @@ __device__ __forceinline__ float dot32_split(const uint4 wq, const half2_t *xp, 
 template <bool kFused, int FMT>
 __device__ __forceinline__ float dot32_fmt(const uint4 wq, const half2_t *xp, float se, float so, float s,
                                            uint32_t aux) {
-  auto pair = [](uint32_t d, uint32_t m) {
-    return kFused ? and_or_sv(d, m, 0x64006400u) : ((d & m) | 0x64006400u);
+  const PairRegs k = pair_regs();
+  auto pair = [&](uint32_t d, uint32_t m) {
+    return kFused ? and_or_sv(d, m, 0x64006400u) : ((d & (m == 0x000F000Fu ? k.m0 : k.m4)) | k.magic);
   };
   float acc = 0.0f;
   const uint32_t d[4] = {wq.x, wq.y, wq.z, wq.w};
