@@ -313,57 +313,61 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   }
 }
 
-// out[t][h][d] = sum_c exp(m_c - M) o_c[d] / sum_c exp(m_c - M) l_c, chunks
-// in order.  256 threads: element d = tid % 128 of the chunks of parity
-// tid / 128, sixteen loads in flight at a time; the two halves are added in
-// a fixed order.  The chunk weights go through LDS.
-constexpr int kMergeMaxChunks = 2048;
-
+// out[t][h][d] = sum_c exp(m_c - M) o_c[d] / sum_c exp(m_c - M) l_c over the
+// chunks c, M = max_c m_c.  256 threads: thread (d = tid % 128, parity
+// tid / 128) takes the chunks of its parity in index order, keeping a
+// running maximum m and rescaling its two sums by exp(m_old - m_new)
+// whenever a batch raises it (the same quotient; M never has to be known
+// first, so every load of a batch goes out at once: one memory round trip
+// up to 2B chunks), then the two parities are combined in a fixed order.
+// Deterministic: the order of every operation is fixed.
+template <int B>  // chunks per batch per thread
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   constexpr int D = kKvD;
-  __shared__ float wc[kMergeMaxChunks];
-  __shared__ float red[256];
-  __shared__ float half_num[D], half_den[D];
+  __shared__ float om[D], on[D], od[D];
   const int th = blockIdx.x, tid = threadIdx.x;  // th = t * Hq + h
   const int nc = a.nchunks;
   const float *p = a.part + (size_t)th * nc * kPartStride;
-  float M = -INFINITY;
-  for (int c = tid; c < nc; c += 256) M = fmaxf(M, p[(size_t)c * kPartStride + D]);
-  red[tid] = M;
-  __syncthreads();
-  for (int w = 128; w > 0; w >>= 1) {
-    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-    __syncthreads();
-  }
-  M = red[0];
-  for (int c = tid; c < nc; c += 256) wc[c] = __expf(p[(size_t)c * kPartStride + D] - M);
-  __syncthreads();
   const int d = tid & (D - 1), par = tid >> 7;
-  float num = 0.0f, den = 0.0f;
-  int c = par;
-  for (; c + 2 * 15 < nc; c += 2 * 16) {
-    float v[16], l[16];
+  float m = -INFINITY, num = 0.0f, den = 0.0f;
+  for (int c0 = par; c0 < nc; c0 += 2 * B) {
+    float v[B], l[B], mc[B];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      v[i] = p[(size_t)(c + 2 * i) * kPartStride + d];
-      l[i] = p[(size_t)(c + 2 * i) * kPartStride + D + 1];
+    for (int i = 0; i < B; ++i) {
+      const int c = c0 + 2 * i;
+      const float *pc = p + (size_t)min(c, nc - 1) * kPartStride;
+      v[i] = pc[d];
+      l[i] = pc[D + 1];
+      mc[i] = c < nc ? pc[D] : -INFINITY;  // past the end: weight 0
     }
+    float mb = m;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      num = fmaf(wc[c + 2 * i], v[i], num);
-      den = fmaf(wc[c + 2 * i], l[i], den);
+    for (int i = 0; i < B; ++i) mb = fmaxf(mb, mc[i]);
+    // Every chunk holds at least one position with a finite score, so mb is
+    // finite from the first batch on; m is -inf only before it (sums 0).
+    const float sc = m == -INFINITY ? 0.0f : __expf(m - mb);
+    num *= sc;
+    den *= sc;
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      const float w = __expf(mc[i] - mb);
+      num = fmaf(w, v[i], num);
+      den = fmaf(w, l[i], den);
     }
-  }
-  for (; c < nc; c += 2) {
-    num = fmaf(wc[c], p[(size_t)c * kPartStride + d], num);
-    den = fmaf(wc[c], p[(size_t)c * kPartStride + D + 1], den);
+    m = mb;
   }
   if (par == 1) {
-    half_num[d] = num;
-    half_den[d] = den;
+    om[d] = m;
+    on[d] = num;
+    od[d] = den;
   }
   __syncthreads();
-  if (par == 0) a.out[(size_t)th * D + d] = (num + half_num[d]) / (den + half_den[d]);
+  if (par == 0) {
+    // Parity 1 is empty only with a single chunk (its m is then -inf).
+    const float m1 = om[d], M = fmaxf(m, m1);
+    const float f0 = __expf(m - M), f1 = m1 == -INFINITY ? 0.0f : __expf(m1 - M);
+    a.out[(size_t)th * D + d] = (num * f0 + on[d] * f1) / (den * f0 + od[d] * f1);
+  }
 }
 
 }  // namespace
@@ -424,7 +428,10 @@ hipError_t launch_sparse_attention(const uint16_t *q, int Tq, int Hq, const uint
   if (e != hipSuccess) return e;
   {
     KernelTimer timer("attn_merge", s);
-    attn_merge_kernel<<<dim3((unsigned)(Tq * Hq)), 256, 0, s>>>(a);
+    if (a.nchunks <= 32)
+      attn_merge_kernel<16><<<dim3((unsigned)(Tq * Hq)), 256, 0, s>>>(a);
+    else
+      attn_merge_kernel<32><<<dim3((unsigned)(Tq * Hq)), 256, 0, s>>>(a);
   }
   return hipGetLastError();
 }
