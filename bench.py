@@ -78,10 +78,10 @@ def counted_traffic(kernel: str, workload: str):
 
 # rocprofv3 kernel names -> library kernel names (and the workload bench.py runs them on)
 COUNTED_KERNELS = {
-    "moe_gemm_wide<0>": ("gemm_gateup", "prefill"),
-    "moe_gemm_wide<1>": ("gemm_down", "prefill"),
-    "moe_gemm_general<0>": ("gemm_gateup", "prefill"),
-    "moe_gemm_general<1>": ("gemm_down", "prefill"),
+    "moe_gemm_wide<0, ": ("gemm_gateup", "prefill"),
+    "moe_gemm_wide<1, ": ("gemm_down", "prefill"),
+    "moe_gemm_general<0, ": ("gemm_gateup", "prefill"),
+    "moe_gemm_general<1, ": ("gemm_down", "prefill"),
     "gemv_gateup_kernel": ("gemv_gateup", "decode"),
     "gemv_down_kernel": ("gemv_down", "decode"),
     "decode_route_gateup_kernel": ("decode_route_gateup", "decode"),
