@@ -163,7 +163,8 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   __shared__ float score[32][C];            // [query head][position]
   __shared__ u32x4_t vrow[C * 8 * (D / 32)];  // [position][Hkv][D/2 bytes], up to Hkv = 8
   __shared__ float vscale[C][8];
-  __shared__ float mh[32], lh[32];
+  __shared__ float wts[C][32];  // [position][query head]: e_p * s_p (value weights)
+  __shared__ float wsumh[32];   // per query head: sum over the chunk of e_p * s_p
 
   if (tid < C) {
     const int i = i0 + min(tid, cnt - 1);  // past the end: repeat the last position (weight 0)
@@ -256,59 +257,74 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // Chunk softmax numerators: head h = tid / 8, 8 threads x 4 positions.
+  // Chunk softmax numerators: head h = tid / 8, 8 threads x C/8 positions.
+  // Each writes its positions' value weights w_p = e_p * s_p (s_p the value
+  // row's scale) and the head's (max, sum of e) go straight to the partial.
+  float *const part_t = a.part + (size_t)t * Hq * a.nchunks * kPartStride;
   if (tid < Hq * 8) {
-    const int h = tid >> 3, j = tid & 7;
+    const int h = tid >> 3, j = tid & 7, gk = h / G;
     float m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < C / 8; ++i) m = fmaxf(m, score[h][j * (C / 8) + i]);
     m = fmaxf(m, dpp_f32<0xB1>(m));
     m = fmaxf(m, dpp_f32<0x4E>(m));
     m = fmaxf(m, dpp_f32<0x141>(m));  // the other quad of the 8 lanes
-    float l = 0.0f;
+    float l = 0.0f, ws = 0.0f;
 #pragma unroll
     for (int i = 0; i < C / 8; ++i) {
-      const float e = __expf(score[h][j * (C / 8) + i] - m);
-      score[h][j * (C / 8) + i] = e;
+      const int pl = j * (C / 8) + i;
+      const float e = __expf(score[h][pl] - m);
+      const float w = e * vscale[pl][gk];
+      wts[pl][h] = w;
       l += e;
+      ws += w;
     }
     l += dpp_f32<0xB1>(l);
     l += dpp_f32<0x4E>(l);
     l += dpp_f32<0x141>(l);
+    ws += dpp_f32<0xB1>(ws);
+    ws += dpp_f32<0x4E>(ws);
+    ws += dpp_f32<0x141>(ws);
     if (j == 0) {
-      mh[h] = m;
-      lh[h] = l;
+      float *dst = part_t + ((size_t)h * a.nchunks + chunk) * kPartStride;
+      dst[D] = m;
+      dst[D + 1] = l;
+      wsumh[h] = ws;
     }
   }
   __syncthreads();
 
-  // Weighted sum of the values: thread (query head h, 16 elements dc);
-  // o = sum_p e_p s_p (u_p - 8) = sum_p w_p u_p - 8 sum_p w_p, w_p = e_p s_p.
-  if (tid < Hq * 8) {
-    const int h = tid >> 3, dc = tid & 7, gk = h / G;
-    float o[16], wsum = 0.0f;
+  // Weighted sum of the values: thread (KV head gk, dims 4 dq .. 4 dq + 3)
+  // for all G query heads of gk, so each value code is unpacked once:
+  // o = sum_p w_p (u_p - 8) = sum_p w_p u_p - 8 sum_p w_p.
+  if (tid < Hkv * 32) {
+    const int gk = tid >> 5, dq = tid & 31;
+    float o[G][4];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o[i] = 0.0f;
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[hh][i] = 0.0f;
     const uint8_t *vb = reinterpret_cast<const uint8_t *>(vrow);
 #pragma unroll 4
     for (int pl = 0; pl < C; ++pl) {
-      const float w = score[h][pl] * vscale[pl][gk];
-      const uint2 wd = *reinterpret_cast<const uint2 *>(vb + ((size_t)pl * Hkv + gk) * (D / 2) + 8 * dc);
-      float uf[16];
-      nib8(wd.x, uf);
-      nib8(wd.y, uf + 8);
+      // Two code bytes: dims 4dq, 4dq+1 (low, high nibble of the first), 4dq+2, 4dq+3.
+      const uint32_t c2 = *reinterpret_cast<const uint16_t *>(vb + ((size_t)pl * Hkv + gk) * (D / 2) + 2 * dq);
+      const uint32_t lo = c2 & 0x0F0Fu, hi = (c2 >> 4) & 0x0F0Fu;
+      const float u[4] = {(float)(lo & 0xFFu), (float)(hi & 0xFFu), (float)(lo >> 8), (float)(hi >> 8)};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[i] = fmaf(w, uf[i], o[i]);
-      wsum += w;
+      for (int hh = 0; hh < G; ++hh) {
+        const float w = wts[pl][gk * G + hh];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[hh][i] = fmaf(w, u[i], o[hh][i]);
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) o[i] = fmaf(-8.0f, wsum, o[i]);
-    float *dst = a.part + (((size_t)t * Hq + h) * a.nchunks + chunk) * kPartStride;
-#pragma unroll
-    for (int i = 0; i < 16; i += 4) *reinterpret_cast<float4 *>(dst + 16 * dc + i) = float4{o[i], o[i + 1], o[i + 2], o[i + 3]};
-    if (dc == 0) {
-      dst[D] = mh[h];
-      dst[D + 1] = lh[h];
+    for (int hh = 0; hh < G; ++hh) {
+      const int h = gk * G + hh;
+      const float ws8 = -8.0f * wsumh[h];
+      float *dst = part_t + ((size_t)h * a.nchunks + chunk) * kPartStride;
+      *reinterpret_cast<float4 *>(dst + 4 * dq) =
+          float4{o[hh][0] + ws8, o[hh][1] + ws8, o[hh][2] + ws8, o[hh][3] + ws8};
     }
   }
 }
