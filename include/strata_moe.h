@@ -359,6 +359,23 @@ int strata_kv_quantize(const uint16_t *x_bf16, int32_t T, int32_t Hkv, int32_t D
                        uint8_t *codes, uint16_t *scales, int32_t L, void *stream);
 
 /*
+ * strata_kv_quantize_pair - strata_kv_quantize of the keys and the values of
+ * the same T tokens in one launch (each token's K and V vectors are cached
+ * together; one launch instead of two halves the fixed launch and memory-
+ * latency cost, which dominates at decode sizes).
+ *
+ *   k_bf16, v_bf16   in  bf16 bits [T][Hkv][D] each.
+ *   slots            in  int32 [T], shared by both (as in strata_kv_quantize).
+ *   k_codes, k_scales, v_codes, v_scales  out  the key and the value cache
+ *                    arrays ([L][Hkv][D/2] uint8, [L][Hkv] fp16 bits).
+ * Every written byte equals what two strata_kv_quantize calls write (same
+ * arithmetic, bit-exact); errors as there, T * Hkv * 2 < 2^31.
+ */
+int strata_kv_quantize_pair(const uint16_t *k_bf16, const uint16_t *v_bf16, int32_t T, int32_t Hkv, int32_t D,
+                            const int32_t *slots, uint8_t *k_codes, uint16_t *k_scales, uint8_t *v_codes,
+                            uint16_t *v_scales, int32_t L, void *stream);
+
+/*
  * strata_sparse_attention - attention of Tq queries over selected positions
  * of a 4-bit cache, dequantizing the selected rows as they are read.
  *

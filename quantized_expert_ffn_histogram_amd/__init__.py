@@ -35,6 +35,7 @@ __all__ = [
     "permute_workspace_size",
     "router",
     "kv_quantize",
+    "kv_quantize_pair",
     "sparse_attention",
     "timing_enable",
     "timing_query",
@@ -305,6 +306,25 @@ def kv_quantize(x: torch.Tensor, slots: torch.Tensor, codes: torch.Tensor, scale
     T, Hkv, D = x.shape
     L = codes.shape[0]
     check(load().strata_kv_quantize(_p(x), T, Hkv, D, _p(slots), _p(codes), _p(scales), L, _stream(x)))
+
+
+def kv_quantize_pair(k: torch.Tensor, v: torch.Tensor, slots: torch.Tensor, k_codes: torch.Tensor,
+                     k_scales: torch.Tensor, v_codes: torch.Tensor, v_scales: torch.Tensor) -> None:
+    """``strata_kv_quantize_pair``: the keys k and values v (bf16 [T, Hkv, D]
+    each) of the same tokens into cache rows ``slots`` of the key and value
+    caches, in one launch."""
+    _need(k, torch.bfloat16, "k")
+    _need(v, torch.bfloat16, "v")
+    _need(slots, torch.int32, "slots")
+    for name, t, dt in (("k_codes", k_codes, torch.uint8), ("v_codes", v_codes, torch.uint8),
+                        ("k_scales", k_scales, torch.float16), ("v_scales", v_scales, torch.float16)):
+        _need(t, dt, name)
+    if k.shape != v.shape:
+        raise ValueError(f"k {tuple(k.shape)} and v {tuple(v.shape)} differ in shape")
+    T, Hkv, D = k.shape
+    L = k_codes.shape[0]
+    check(load().strata_kv_quantize_pair(_p(k), _p(v), T, Hkv, D, _p(slots), _p(k_codes), _p(k_scales),
+                                         _p(v_codes), _p(v_scales), L, _stream(k)))
 
 
 def sparse_attention(q: torch.Tensor, k_codes: torch.Tensor, k_scales: torch.Tensor, v_codes: torch.Tensor,

@@ -63,6 +63,7 @@ SIGNATURES = {
         [_vp, _vp, _i32, _i32, ctypes.POINTER(StrataMoeWeights), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     ),
     "strata_kv_quantize": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp]),
+    "strata_kv_quantize_pair": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp]),
     "strata_sparse_attention_workspace_size": (_sz, [_i32, _i32, _i32]),
     "strata_sparse_attention": (
         ctypes.c_int,

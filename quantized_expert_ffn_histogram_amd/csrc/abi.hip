@@ -486,6 +486,29 @@ int strata_kv_quantize(const uint16_t *x_bf16, int32_t T, int32_t Hkv, int32_t D
   return e == hipSuccess ? ok() : hip_fail(fn, e);
 }
 
+int strata_kv_quantize_pair(const uint16_t *k_bf16, const uint16_t *v_bf16, int32_t T, int32_t Hkv, int32_t D,
+                            const int32_t *slots, uint8_t *k_codes, uint16_t *k_scales, uint8_t *v_codes,
+                            uint16_t *v_scales, int32_t L, void *stream) {
+  static const char *fn = "strata_kv_quantize_pair";
+  if (T < 0) return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "T=%d is negative", T);
+  if (L < 1) return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "L=%d must be >= 1", L);
+  if (!kv_shape_supported(Hkv, D))
+    return fail(STRATA_ERR_UNSUPPORTED, fn, "Hkv=%d, D=%d: supported are D = 128 and Hkv in {1, 2, 4, 8}", Hkv, D);
+  if ((long long)T * Hkv * 2 >= (1ll << 31) || (long long)L * Hkv * D >= (1ll << 40))
+    return fail(STRATA_ERR_UNSUPPORTED, fn, "T=%d or L=%d too large", T, L);
+  if (T == 0) return ok();
+  REQUIRE_PTR(fn, k_bf16);
+  REQUIRE_PTR(fn, v_bf16);
+  REQUIRE_PTR(fn, slots);
+  REQUIRE_PTR(fn, k_codes);
+  REQUIRE_PTR(fn, k_scales);
+  REQUIRE_PTR(fn, v_codes);
+  REQUIRE_PTR(fn, v_scales);
+  const hipError_t e = launch_kv_quantize(k_bf16, T, Hkv, slots, L, k_codes, k_scales,
+                                          static_cast<hipStream_t>(stream), v_bf16, v_codes, v_scales);
+  return e == hipSuccess ? ok() : hip_fail(fn, e);
+}
+
 size_t strata_sparse_attention_workspace_size(int32_t Tq, int32_t Hq, int32_t n_sel) {
   if (Tq < 0 || Hq < 1 || n_sel < 1) return 0;
   return attn_workspace_bytes(Tq, Hq, n_sel);

@@ -59,9 +59,20 @@ __device__ __forceinline__ float bf16_hi(uint32_t d) { return __uint_as_float(d 
 // load) and writes their 8 codes as one 32-bit word; max |x| is a DPP
 // reduction inside the 16-lane row.  A wavefront does 4 rows per round and
 // kKvRounds rounds, all loads issued before the first reduction.  Rows whose
-// slot lies outside [0, L) are skipped.
+// slot lies outside [0, L) are skipped.  One launch can encode two tensors
+// of the same tokens (keys and values): rows [0, rows1) come from the first,
+// rows [rows1, rows) from the second.
 constexpr int kKvRounds = 4;
 constexpr int kKvRowsPerWave = 4 * kKvRounds;
+
+struct KvQuantArgs {
+  const uint16_t *x[2];  // bf16 [T][Hkv][D] each
+  uint8_t *codes[2];     // [L][Hkv][D/2]
+  uint16_t *scale[2];    // fp16 [L][Hkv]
+  int rows1, rows;       // rows of the first tensor, rows of both
+  int Hkv, L;
+  const int *slots;      // [T], shared by both tensors
+};
 
 __device__ __forceinline__ float row16_max(float v) {
   v = fmaxf(v, dpp_f32<0xB1>(v));   // quad_perm [1,0,3,2]
@@ -71,18 +82,19 @@ __device__ __forceinline__ float row16_max(float v) {
   return v;
 }
 
-__global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t *__restrict__ x, int rows, int Hkv,
-                                                          const int *__restrict__ slots, int L,
-                                                          uint8_t *__restrict__ codes, uint16_t *__restrict__ scale) {
+__global__ __launch_bounds__(256) void kv_quantize_kernel(KvQuantArgs a) {
   const int lane = threadIdx.x & 63, sub = lane & 15;
   const int wrow0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kKvRowsPerWave + (lane >> 4);
+  const int Hkv = a.Hkv;
   u32x4_t d[kKvRounds];
   int slot[kKvRounds];
 #pragma unroll
   for (int r = 0; r < kKvRounds; ++r) {
     const int row = wrow0 + 4 * r;
-    d[r] = row < rows ? *reinterpret_cast<const u32x4_t *>(x + (size_t)row * kKvD + 8 * sub) : u32x4_t{0, 0, 0, 0};
-    slot[r] = row < rows ? slots[row / Hkv] : -1;
+    const int second = row >= a.rows1, rr = row - (second ? a.rows1 : 0);
+    const uint16_t *x = second ? a.x[1] : a.x[0];
+    d[r] = row < a.rows ? *reinterpret_cast<const u32x4_t *>(x + (size_t)rr * kKvD + 8 * sub) : u32x4_t{0, 0, 0, 0};
+    slot[r] = row < a.rows ? a.slots[rr / Hkv] : -1;
   }
 #pragma unroll
   for (int r = 0; r < kKvRounds; ++r) {
@@ -97,8 +109,9 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t *__rest
 #pragma unroll
     for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
     const float amax = row16_max(m);  // every lane of the row group reaches this
-    if (slot[r] < 0 || slot[r] >= L) continue;  // also rows past the end
-    const int h = row % Hkv;
+    if (slot[r] < 0 || slot[r] >= a.L) continue;  // also rows past the end
+    const int second = row >= a.rows1, rr = row - (second ? a.rows1 : 0);
+    const int h = rr % Hkv;
     const _Float16 s16 = (_Float16)(amax / 7.0f);
     const float sc = (float)s16;
     // q = rint(x / s) with the fp32 quotient rounded to nearest, without a
@@ -122,8 +135,8 @@ __global__ __launch_bounds__(256) void kv_quantize_kernel(const uint16_t *__rest
       word |= (uint32_t)(q + 8) << (4 * i);
     }
     const size_t dst = (size_t)slot[r] * Hkv + h;
-    reinterpret_cast<uint32_t *>(codes + dst * (kKvD / 2))[sub] = word;
-    if (sub == 0) scale[dst] = __builtin_bit_cast(uint16_t, s16);
+    reinterpret_cast<uint32_t *>((second ? a.codes[1] : a.codes[0]) + dst * (kKvD / 2))[sub] = word;
+    if (sub == 0) (second ? a.scale[1] : a.scale[0])[dst] = __builtin_bit_cast(uint16_t, s16);
   }
 }
 
@@ -391,10 +404,22 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 bool kv_shape_supported(int Hkv, int D) { return D == kKvD && (Hkv == 1 || Hkv == 2 || Hkv == 4 || Hkv == 8); }
 
 hipError_t launch_kv_quantize(const uint16_t *x, int T, int Hkv, const int *slots, int L, uint8_t *codes,
-                              uint16_t *scale, hipStream_t s) {
-  const int rows = T * Hkv;
+                              uint16_t *scale, hipStream_t s, const uint16_t *x2, uint8_t *codes2,
+                              uint16_t *scale2) {
+  KvQuantArgs a{};
+  a.x[0] = x;
+  a.codes[0] = codes;
+  a.scale[0] = scale;
+  a.x[1] = x2 ? x2 : x;
+  a.codes[1] = x2 ? codes2 : codes;
+  a.scale[1] = x2 ? scale2 : scale;
+  a.rows1 = T * Hkv;
+  a.rows = (x2 ? 2 : 1) * T * Hkv;
+  a.Hkv = Hkv;
+  a.L = L;
+  a.slots = slots;
   KernelTimer timer("kv_quantize", s);
-  kv_quantize_kernel<<<ceil_div(rows, 4 * kKvRowsPerWave), 256, 0, s>>>(x, rows, Hkv, slots, L, codes, scale);
+  kv_quantize_kernel<<<ceil_div(a.rows, 4 * kKvRowsPerWave), 256, 0, s>>>(a);
   return hipGetLastError();
 }
 

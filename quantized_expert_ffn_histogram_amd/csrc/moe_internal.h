@@ -107,8 +107,11 @@ hipError_t launch_combine_pairs(const uint16_t *y16, const float *topk_w, int T,
 // 4-bit KV cache (kv.hip): per-head symmetric codes of key/value vectors and
 // attention of queries over selected cache rows.
 bool kv_shape_supported(int Hkv, int D);
+// With x2 non-null a second tensor of the same tokens (values beside keys) is
+// encoded in the same launch into codes2 / scale2.
 hipError_t launch_kv_quantize(const uint16_t *x, int T, int Hkv, const int *slots, int L, uint8_t *codes,
-                              uint16_t *scale, hipStream_t s);
+                              uint16_t *scale, hipStream_t s, const uint16_t *x2 = nullptr,
+                              uint8_t *codes2 = nullptr, uint16_t *scale2 = nullptr);
 size_t attn_workspace_bytes(int Tq, int Hq, int n_sel);
 hipError_t launch_sparse_attention(const uint16_t *q, int Tq, int Hq, const uint8_t *kc, const uint16_t *ks,
                                    const uint8_t *vc, const uint16_t *vs, int L, int Hkv, const int *sel,

@@ -290,3 +290,33 @@ def test_noalloc_layer_checks_sizes_before_launch():
     assert call(4, None) == 1 and "w is NULL" in _err(lib)
     assert call(4, ctypes.byref(_weights(abi, g=48)), k=2) == 2 and "group=48" in _err(lib)
     assert call(4, ctypes.byref(_weights(abi)), k=17) == 1 and "k=17 exceeds E=16" in _err(lib)
+
+
+@pytest.mark.parametrize(
+    "T,Hkv,D,L,code,needle",
+    [
+        (-1, 8, 128, 16, 1, "T=-1"),
+        (4, 8, 128, 0, 1, "L=0"),
+        (4, 3, 128, 16, 2, "Hkv=3"),
+        (4, 8, 64, 16, 2, "D=64"),
+        (1 << 27, 8, 128, 16, 2, "too large"),
+    ],
+)
+def test_kv_quantize_pair_rejects_bad_sizes(T, Hkv, D, L, code, needle):
+    _, lib = _lib()
+    assert lib.strata_kv_quantize_pair(None, None, T, Hkv, D, None, None, None, None, None, L, None) == code
+    assert needle in _err(lib)
+    assert _err(lib).startswith("strata_kv_quantize_pair")
+
+
+def test_kv_quantize_pair_rejects_null_pointers_and_accepts_zero_tokens():
+    _, lib = _lib()
+    p = ctypes.c_void_p(0x10000)
+    assert lib.strata_kv_quantize_pair(None, p, 4, 8, 128, p, p, p, p, p, 16, None) == 1
+    assert "k_bf16 is NULL" in _err(lib)
+    assert lib.strata_kv_quantize_pair(p, None, 4, 8, 128, p, p, p, p, p, 16, None) == 1
+    assert "v_bf16 is NULL" in _err(lib)
+    assert lib.strata_kv_quantize_pair(p, p, 4, 8, 128, p, p, p, None, p, 16, None) == 1
+    assert "v_codes is NULL" in _err(lib)
+    assert lib.strata_kv_quantize_pair(None, None, 0, 8, 128, None, None, None, None, None, 16, None) == 0
+    assert _err(lib) == ""

@@ -109,6 +109,49 @@ def test_kv_quantize_slots_and_skips(qe):
         assert (got_p[s] == 0x5A).all() and (got_s[s] == np.float16(1.5)).all(), s
 
 
+@pytest.mark.parametrize("Hkv", [1, 2, 8])
+def test_kv_quantize_pair_matches_oracle_and_single_calls(qe, Hkv):
+    """strata_kv_quantize_pair: keys and values of the same tokens in one
+    launch.  T * Hkv rows of keys are not a multiple of a wavefront's 16 rows,
+    so one wavefront holds both key and value rows; slots outside [0, L) are
+    skipped for both.  Every byte equals the oracle's and two single calls'."""
+    import torch
+
+    rng = np.random.default_rng(40 + Hkv)
+    L, D, T = 40, 128, 13
+    k = synth.bf16_bits_from_f32(rng.standard_normal((T, Hkv, D)).astype(np.float32) * 3)
+    v = synth.bf16_bits_from_f32(rng.standard_normal((T, Hkv, D)).astype(np.float32) * 0.01)
+    v[0] = _edge_vectors()[:Hkv]  # zero, tie, huge and tiny vectors among the values
+    slots = np.array([5, 39, 0, -3, 17, 40, 2, 31, 8, 1 << 20, 22, 11, 30], np.int32)
+    dslots = torch.from_numpy(slots).cuda()
+
+    def fresh():
+        return (torch.full((L, Hkv, D // 2), 0x5A, dtype=torch.uint8, device="cuda"),
+                torch.full((L, Hkv), 1.5, dtype=torch.float16, device="cuda"))
+
+    kc, ks = fresh()
+    vc, vs = fresh()
+    qe.kv_quantize_pair(_dev_bf16(k), _dev_bf16(v), dslots, kc, ks, vc, vs)
+    kc1, ks1 = fresh()
+    vc1, vs1 = fresh()
+    qe.kv_quantize(_dev_bf16(k), dslots, kc1, ks1)
+    qe.kv_quantize(_dev_bf16(v), dslots, vc1, vs1)
+    for a, b, what in ((kc, kc1, "key codes"), (ks, ks1, "key scales"), (vc, vc1, "value codes"),
+                       (vs, vs1, "value scales")):
+        assert (_np(a).view(np.uint8) == _np(b).view(np.uint8)).all(), what
+    for x, codes, scales, what in ((k, kc, ks, "keys"), (v, vc, vs, "values")):
+        rp, rs = oracle.kv_quantize(x)
+        got_p, got_s = _np(codes), _np(scales)
+        written = set()
+        for t, s in enumerate(slots):
+            if 0 <= s < L:
+                assert (got_p[s] == rp[t]).all() and (got_s[s].view(np.uint16) == rs[t].view(np.uint16)).all(), \
+                    (what, t)
+                written.add(int(s))
+        for s in set(range(L)) - written:
+            assert (got_p[s] == 0x5A).all() and (got_s[s] == np.float16(1.5)).all(), (what, s)
+
+
 def _check_attn(got, ref, what):
     err = np.abs(got.astype(np.float64) - ref)
     rms = float(np.sqrt(np.mean(ref ** 2)))
