@@ -166,6 +166,22 @@ def time_region(fn, steps: int):
     return a.elapsed_time(b) / 1e3  # seconds
 
 
+def warm_up(fn, min_steps: int, min_secs: float = 0.2, max_steps: int = 2000) -> int:
+    """Untimed steps until at least min_steps ran and min_secs of device work
+    passed (the clock ramps up after the idle of a host-to-device upload);
+    returns the number of steps."""
+    import torch
+
+    n = 0
+    t0 = time.perf_counter()
+    while n < min_steps or (time.perf_counter() - t0 < min_secs and n < max_steps):
+        for _ in range(4):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
 def step_percentiles(fn, steps: int, total: bool = False) -> dict:
     """Per-step device time (HIP events around each step): p10 / p50 / p90 in
     us; with total, also the number of steps and the region's wall time."""
@@ -384,7 +400,8 @@ def layer_work(cfg, distinct: int):
 
 def bench_secondary(qe, args):
     """The other configurations, each timed the same way as the headline one
-    (whole layer, inputs resident, HIP events), against the roofline that
+    (whole layer, inputs resident, HIP events, after at least 0.2 s of
+    untimed steps), against the roofline that
     bounds it: HBM for small-batch prefill, the matrix cores for the skewed
     large-chunk prefill and for the 6144-token chunk with 32- and 128-wide
     scale groups; the tiny case is launch-latency bound."""
@@ -407,8 +424,7 @@ def bench_secondary(qe, args):
         x = torch.from_numpy(inp.x_bf16.view(np.int16)).to(dev).view(torch.bfloat16)
         experts = qe.QuantizedExperts.from_numpy(inp.weights, cfg.g, dev)
         run = qe.LayerRunner(experts, cfg.T, cfg.E, cfg.k, fused=True, device=dev, single_call=single)
-        for _ in range(max(args.warmup, 3)):
-            run(logits, x)
+        warm = warm_up(lambda i: run(logits, x), max(args.warmup, 3))
         secs = time_region(lambda i: run(logits, x), steps)
         distinct = int((run.counts > 0).sum().item())
         flops, nbytes = layer_work(cfg, distinct)
@@ -416,6 +432,7 @@ def bench_secondary(qe, args):
         rec = {"workload": f"{cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} g={cfg.g}",
                "weights": cfg.fmt, "call": "strata_moe_layer" if single else "route + permute + ffn",
                "us_per_step": round(us, 2), "tokens_per_s": round(cfg.T / (us * 1e-6), 1), "steps": steps,
+               "warmup_steps": warm,
                "distinct_experts": distinct, "alg_flops": flops, "alg_bytes": int(nbytes)}
         if bound == "hbm":
             rec["roofline"] = {"bound": "hbm", "frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
