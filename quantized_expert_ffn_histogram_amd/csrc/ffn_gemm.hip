@@ -29,11 +29,13 @@
 //     double-buffered window.  This halves the vector-memory instructions and
 //     cache sectors per flop of the general pipeline, which is what bounds
 //     these kernels (the per-CU load path, not HBM bandwidth).  Needs the
-//     groups per row, K/g, to be a multiple of 8.  Symmetric 4-bit and, with
-//     a window of zero points beside the scales, asymmetric 4-bit.
+//     groups per row, K/g, to be a multiple of 8.  Every format: asymmetric
+//     4-bit with a window of zero points beside the scales, 5-bit with its
+//     fifth-bit words in a ring beside the stages (and 4-group scale windows
+//     to make LDS room for them).
 //   * general: 4 wavefronts, two workgroups per CU, K chunks of 64 in a
-//     3-stage ring, one 2-byte scale load per row and chunk; every format
-//     (5-bit only here: its fifth-bit words do not fit the wide LDS budget).
+//     3-stage ring, one 2-byte scale load per row and chunk; every format,
+//     for the shapes the wide pipeline does not take.
 //
 // Dequant in registers: a dword holds 8 nibbles u_0..u_7 (even K low); the
 // pair (u_m, u_{m+4}) goes into the mantissas of two fp16 values with one
@@ -270,10 +272,13 @@ __device__ __forceinline__ half8 dequant8_c(uint32_t d, half2_t s2, const Dequan
 // with ce = -(1024 + z) for the group's zero point z, so q = u - z is
 // (1024 + u) + ce for a low nibble and (1024 + 16u)/16 + (ce + 960) for the
 // next one, both exact, then one multiply by s.
+// 5-bit: the fifth bits of the dword's 8 weights come from the lane's word
+// hw of its 32-K block (bit 4i + b for weight i of dword b), shifted into bit
+// 4 of the low pairs and bit 8 of the high ones, then minus 1040 and 80.
 template <int FMT>
 __device__ __forceinline__ void dequant_piece(int q, const uint32_t (&d)[kNB], const half2_t (&s2)[kNB],
-                                              const DequantRegs &k, uint32_t (&out)[kNB][4]) {
-  static_assert(FMT == kFmtInt4 || FMT == kFmtInt4Asym, "wide pipeline formats");
+                                              const DequantRegs &k, uint32_t (&out)[kNB][4],
+                                              const uint32_t (&hw)[kNB] = {}, int b = 0) {
   const half2_t off = {(_Float16)1032.0f, (_Float16)1032.0f};
   const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
   const half2_t off16 = {(_Float16)-72.0f, (_Float16)-72.0f};
@@ -283,11 +288,21 @@ __device__ __forceinline__ void dequant_piece(int q, const uint32_t (&d)[kNB], c
   for (int nb = 0; nb < kNB; ++nb) {
     const uint32_t src = q < 2 ? d[nb] : d[nb] >> 8;
     r[nb] = (src & ((q & 1) ? k.mask4 : k.mask)) | k.magic;
+    if constexpr (FMT == kFmtInt5) {
+      const uint32_t t = q < 2 ? hw[nb] << (4 - b) : hw[nb] >> (4 + b);
+      r[nb] |= t & ((q & 1) ? 0x01000100u : 0x00100010u);
+    }
   }
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) {
     const half2_t v = __builtin_bit_cast(half2_t, r[nb]);
-    if constexpr (FMT == kFmtInt4) {
+    if constexpr (FMT == kFmtInt5) {
+      const half2_t sixteenth5 = {(_Float16)0.0625f, (_Float16)0.0625f};
+      const half2_t o5 = {(_Float16)-1040.0f, (_Float16)-1040.0f};
+      const half2_t o80 = {(_Float16)-80.0f, (_Float16)-80.0f};
+      const half2_t qv = (q & 1) ? __builtin_elementwise_fma(v, sixteenth5, o80) : v + o5;
+      out[nb][q] = __builtin_bit_cast(uint32_t, qv * s2[nb]);
+    } else if constexpr (FMT == kFmtInt4) {
       const half2_t qv = (q & 1) ? __builtin_elementwise_fma(v, sixteenth, off16) : v - off;
       out[nb][q] = __builtin_bit_cast(uint32_t, qv * s2[nb]);
     } else {
@@ -307,13 +322,21 @@ __device__ __forceinline__ void dequant_piece(int q, const uint32_t (&d)[kNB], c
 // mb's fragment of K-step j; `pre(j)` runs at the start of K-step j.  Each
 // token block's group (two MFMAs, one fragment read, its dequant pieces) is
 // closed by a scheduling barrier, so the order is the source order.
-template <int NMB, int FMT, typename BRead, typename AFrag, typename Pre>
+// `hread(h, nb)` (5-bit only) gives the fifth-bit word of 64-K half h,
+// block nb for this lane's 32 K values.
+template <int NMB, int FMT, typename BRead, typename AFrag, typename Pre, typename HRead>
 __device__ __forceinline__ void mma_stage_pipelined(floatx16 (&acc)[NMB][kNB], BRead &&bread,
-                                                    const half2_t (&s2)[2][kNB], AFrag &&afrag, Pre &&pre) {
+                                                    const half2_t (&s2)[2][kNB], AFrag &&afrag, Pre &&pre,
+                                                    HRead &&hread) {
   const DequantRegs k = dequant_regs();
   uint4 bw[kNB];
+  uint32_t hw[kNB] = {};
 #pragma unroll
   for (int nb = 0; nb < kNB; ++nb) bw[nb] = bread(0, nb);
+  if constexpr (FMT == kFmtInt5) {
+#pragma unroll
+    for (int nb = 0; nb < kNB; ++nb) hw[nb] = hread(0, nb);
+  }
   half8 af[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) af[mb] = afrag(0, mb);
@@ -323,7 +346,7 @@ __device__ __forceinline__ void mma_stage_pipelined(floatx16 (&acc)[NMB][kNB], B
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) d[nb] = dword_of(bw[nb], 0);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) dequant_piece<FMT>(q, d, s2[0], k, bf[0]);
+    for (int q = 0; q < 4; ++q) dequant_piece<FMT>(q, d, s2[0], k, bf[0], hw, 0);
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -343,13 +366,17 @@ __device__ __forceinline__ void mma_stage_pipelined(floatx16 (&acc)[NMB][kNB], B
         af[mb] = afrag(jn, mb);
 #pragma unroll
         for (int q = mb * 4 / NMB; q < (mb + 1) * 4 / NMB; ++q)
-          dequant_piece<FMT>(q, d, s2[jn >> 2], k, bf[cur ^ 1]);
+          dequant_piece<FMT>(q, d, s2[jn >> 2], k, bf[cur ^ 1], hw, jn & 3);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     if (j == 2) {  // half 0's packed weights are dead after K-step 3's dequant
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) bw[nb] = bread(1, nb);
+      if constexpr (FMT == kFmtInt5) {
+#pragma unroll
+        for (int nb = 0; nb < kNB; ++nb) hw[nb] = hread(1, nb);
+      }
     }
   }
 }
@@ -563,8 +590,19 @@ struct WideStage {
   uint4 a[kGemmRows * 16];             // token rows [row][16-byte segment], XOR-swizzled (wa_slot)
   uint4 b[Shape<kWideW>::kBRows * 4];  // weight rows [row][16-byte quarter], XOR-swizzled (wb_slot)
 };
+// Weight rows' fp16 scales of 8 consecutive groups (16 bytes per row); for
+// the 5-bit format 4 groups (8 bytes per row, as two dwords: the first of
+// every row of a wavefront's 64, then the second), which leaves LDS room for
+// the fifth-bit words.
+template <int FMT>
 struct ScaleWindow {
-  uint4 s[Shape<kWideW>::kBRows];  // weight rows: fp16 scales of 8 consecutive groups
+  uint4 s[FMT == kFmtInt5 ? Shape<kWideW>::kBRows / 2 : Shape<kWideW>::kBRows];
+};
+// 5-bit: the fifth-bit words of a stage (4 per row, 16 bytes), one per ring
+// slot; a placeholder otherwise.
+template <int FMT>
+struct HiStage {
+  uint4 h[FMT == kFmtInt5 ? Shape<kWideW>::kBRows : 1];
 };
 // Asymmetric 4-bit: the zero points of the same 8 groups (4 bytes per row,
 // group i of the window in bits 4i..4i+3); a placeholder otherwise.
@@ -598,8 +636,9 @@ __device__ __forceinline__ int wb_slot(int br, int q) { return br * 4 + (q ^ ((b
 // stage of a slice is computed the first stage of the next is already in
 // flight, and the slice's epilogue runs while it lands.
 template <int MODE, int NMB, int FMT>
-__device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0, WideStage &st1, ScaleWindow &sw0,
-                                               ScaleWindow &sw1, ZeroWindow<FMT> &zw0, ZeroWindow<FMT> &zw1,
+__device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0, WideStage &st1,
+                                               ScaleWindow<FMT> &sw0, ScaleWindow<FMT> &sw1, ZeroWindow<FMT> &zw0,
+                                               ZeroWindow<FMT> &zw1, HiStage<FMT> &hs0, HiStage<FMT> &hs1,
                                                const RowTables &rt, int e, int row0, int nrows, int slice0,
                                                int nsl) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -608,13 +647,16 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
   const int nst = a.K / kKS;  // K stages per slice
   // g is 32, 64 or 128: group and window indexes are shifts.
   const int lg = 31 - __builtin_clz(a.g);  // log2(g)
-  const int lpw = lg - 4;                  // log2(stages per 8-group scale window)
+  constexpr bool k5 = FMT == kFmtInt5;
+  constexpr int kWinG = k5 ? 4 : 8;        // groups per scale window
+  const int lpw = lg - (k5 ? 5 : 4);       // log2(stages per scale window)
   const int ngr = a.K >> lg;               // groups per weight row (a multiple of 8, or 1, 2, 4)
   // Scale windows per slice.  Rows of fewer than 8 groups have one window
   // per slice whose 16-byte load also covers the next row's first scales
   // (unused); for the block's last row that part lies past the buffer
-  // resource's range and reads as zero.
-  const int nwin = ngr >= 8 ? ngr >> 3 : 1;
+  // resource's range and reads as zero.  (The 5-bit format takes the wide
+  // pipeline only with K/g a multiple of 8.)
+  const int nwin = ngr >= 8 ? ngr / kWinG : 1;
 
   uint32_t aoff[NMB];
 #pragma unroll
@@ -637,10 +679,11 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
   constexpr int kRes = kNB;
   constexpr bool kAsym = FMT == kFmtInt4Asym;
   int lsl = slice0, lc = 0;
-  __amdgpu_buffer_rsrc_t rb[kRes], rs[kRes], rz[kAsym ? kRes : 1];
-  // This lane's scale row (and zero-point row) in its block.
+  __amdgpu_buffer_rsrc_t rb[kRes], rs[kRes], rz[kAsym ? kRes : 1], rh[k5 ? kRes : 1];
+  // This lane's scale row (and zero-point or fifth-bit row) in its block.
   const uint32_t soff = (uint32_t)col * ngr * 2;
   const uint32_t zoff = (uint32_t)col * (ngr / 2);
+  const uint32_t hoff = (uint32_t)col * (uint32_t)(a.K / 32) * 4u;
   auto bases = [&](int sl) {
     const bool v = weight_row0<MODE, kWideW>(sl, wave, 0) < a.N;
     const char *bb[kNB];
@@ -654,6 +697,12 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
         const int n0 = v ? weight_row0<MODE, kWideW>(sl, wave, r) : 0;
         const uint8_t *X = MODE == 0 && r >= kNB / 2 ? a.X1 : a.X0;
         rz[r] = buffer_rsrc(X + ((size_t)e * a.N + n0) * (size_t)(ngr / 2), 32u * (uint32_t)(ngr / 2));
+      }
+      if constexpr (k5) {
+        const int n0 = v ? weight_row0<MODE, kWideW>(sl, wave, r) : 0;
+        const uint8_t *X = MODE == 0 && r >= kNB / 2 ? a.X1 : a.X0;
+        const size_t rowb = (size_t)(a.K / 32) * 4;
+        rh[r] = buffer_rsrc(X + ((size_t)e * a.N + n0) * rowb, 32u * (uint32_t)rowb);
       }
     }
   };
@@ -690,11 +739,23 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
     if ((lc & ((1 << lpw) - 1)) == 0) {
       const int win = lc >> lpw;
       const bool odd = window_odd(lsl, win);
-      const lds_ptr_t dst = odd ? lds_at(sw1.s, lds_w1k) : lds_at(sw0.s, lds_w1k);
-      if (half == 0)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[0], dst, 16, soff, 16u * win, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[1], dst, 16, soff, 16u * win, 0, 0);
+      if constexpr (k5) {  // 8 bytes per row as two dword loads, 512 bytes per wavefront
+        const lds_ptr_t dst = odd ? lds_at(sw1.s, lds_w1k >> 1) : lds_at(sw0.s, lds_w1k >> 1);
+        const lds_ptr_t dst2 = odd ? lds_at(sw1.s, (lds_w1k >> 1) + 256u) : lds_at(sw0.s, (lds_w1k >> 1) + 256u);
+        if (half == 0) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[0], dst, 4, soff, 8u * win, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[0], dst2, 4, soff, 8u * win + 4u, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[1], dst, 4, soff, 8u * win, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[1], dst2, 4, soff, 8u * win + 4u, 0, 0);
+        }
+      } else {
+        const lds_ptr_t dst = odd ? lds_at(sw1.s, lds_w1k) : lds_at(sw0.s, lds_w1k);
+        if (half == 0)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[0], dst, 16, soff, 16u * win, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[1], dst, 16, soff, 16u * win, 0, 0);
+      }
       if constexpr (kAsym) {
         const uint32_t zw = lds_w1k >> 2;  // 256 bytes per wavefront
         const lds_ptr_t zdst = odd ? lds_at(zw1.z, zw) : lds_at(zw0.z, zw);
@@ -710,10 +771,23 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
   // all at the first K-step, so their latency has the whole stage to land,
   // and the token rows (mostly L2 hits) one per K-step after that.  kk is a
   // compile-time constant in every caller: no branch splits a K-step.
-  auto issue_part = [&](WideStage &st, int kk) {
+  // 5-bit: the stage's fifth-bit words (16 bytes per row: lanes 0-31 the rows
+  // of block 0, 32-63 those of block 1) go with the weight rows into the
+  // hi-word slot of the same ring position.
+  auto issue_h = [&](HiStage<FMT> &hs) {
+    if constexpr (k5) {
+      if (half == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rh[0], lds_at(hs.h, lds_w1k), 16, hoff, 16u * (uint32_t)lc, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rh[kRes - 1], lds_at(hs.h, lds_w1k), 16, hoff,
+                                                 16u * (uint32_t)lc, 0, 0);
+    }
+  };
+  auto issue_part = [&](WideStage &st, HiStage<FMT> &hs, int kk) {
     if (kk == 0) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) issue_b(st, q);
+      issue_h(hs);
     } else if (kk <= NMB) {
       issue_a(st, kk - 1 < NMB ? kk - 1 : 0);
     }
@@ -743,7 +817,8 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
   };
   // Compute stage c of slice sl from `cur`; with MORE (a compile-time flag:
   // this is not the item's last stage) issue the cursor's loads into `nxt`.
-  auto step = [&](const WideStage &cur, WideStage &nxt, int sl, int c, auto more_c) {
+  auto step = [&](const WideStage &cur, WideStage &nxt, const HiStage<FMT> &hcur, HiStage<FMT> &hnxt, int sl, int c,
+                  auto more_c) {
     constexpr bool MORE = decltype(more_c)::value;
     compiler_fence();
     wait_vmcnt<0>();               // this wavefront's loads of this stage are done
@@ -753,7 +828,7 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
     // Scales of this stage's two 64-K halves (group of K offset kc + 32*half).
     const int win = c >> lpw;
     const bool odd = window_odd(sl, win);
-    const ScaleWindow &sw = odd ? sw1 : sw0;
+    const ScaleWindow<FMT> &sw = odd ? sw1 : sw0;
     // Asymmetric 4-bit: (s, ce), ce = -(1024 + z) (fp16 bits 0xE400 | z).
     uint32_t zwin[kNB];
     if constexpr (kAsym) {
@@ -764,10 +839,15 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
     half2_t s2[2][kNB];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const int grp = ((c * kKS + 64 * s + 32 * half) >> lg) - 8 * win;
+      const int grp = ((c * kKS + 64 * s + 32 * half) >> lg) - kWinG * win;
 #pragma unroll
       for (int nb = 0; nb < kNB; ++nb) {
-        const uint16_t bits = reinterpret_cast<const uint16_t *>(&sw.s[brow_of(wave, nb, col)])[grp];
+        uint16_t bits;
+        if constexpr (k5)  // dword grp/2 of the row, half grp%2
+          bits = reinterpret_cast<const uint16_t *>(
+              reinterpret_cast<const uint32_t *>(sw.s) + wave * 128 + (grp >> 1) * 64 + nb * 32 + col)[grp & 1];
+        else
+          bits = reinterpret_cast<const uint16_t *>(&sw.s[brow_of(wave, nb, col)])[grp];
         if constexpr (kAsym) {
           const uint32_t ce = 0xE400u | ((zwin[nb] >> (4 * grp)) & 15u);
           s2[s][nb] = __builtin_bit_cast(half2_t, (uint32_t)bits | (ce << 16));
@@ -787,8 +867,15 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
           return __builtin_bit_cast(half8, cur.a[wa_slot(mb * 32 + col, 8 * (j >> 2) + 4 * half + (j & 3))]);
         },
         [&](int j) {
-          if constexpr (MORE) issue_part(nxt, j);
+          if constexpr (MORE) issue_part(nxt, hnxt, j);
           __builtin_amdgcn_sched_barrier(0);
+        },
+        [&](int h, int nb) -> uint32_t {
+          if constexpr (k5) {
+            const uint4 w4 = hcur.h[brow_of(wave, nb, col)];
+            return dword_of(w4, 2 * h + half);
+          }
+          return 0u;
         });
     if constexpr (MORE) advance_loads();
   };
@@ -805,24 +892,24 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
   refresh_lds_offsets();
   issue_s();  // the first scale window
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) issue_part(st0, kk);
+  for (int kk = 0; kk < 8; ++kk) issue_part(st0, hs0, kk);
   advance_loads();
   const std::true_type more;
   const std::false_type last;
   const int total = nsl * nst;
   int gs = 0;
   for (; gs + 2 < total; gs += 2) {
-    step(st0, st1, sl, c, more);
+    step(st0, st1, hs0, hs1, sl, c, more);
     finish();
-    step(st1, st0, sl, c, more);
+    step(st1, st0, hs1, hs0, sl, c, more);
     finish();
   }
   const bool two = gs + 1 < total;
   if (two) {
-    step(st0, st1, sl, c, more);
+    step(st0, st1, hs0, hs1, sl, c, more);
     finish();
   }
-  step(two ? st1 : st0, st0, sl, c, last);
+  step(two ? st1 : st0, st0, two ? hs1 : hs0, hs0, sl, c, last);
   finish();
   // The last step issued nothing: no load of this item is in flight.
 }
@@ -832,13 +919,14 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
 template <int MODE, int FMT>  // MODE 0: gate/up + silu*mul -> h;  1: down -> y
 __global__ __launch_bounds__(64 * kWideW, 1) void moe_gemm_wide(GemmArgs a) {
   __shared__ WideStage st0, st1;
-  __shared__ ScaleWindow sw0, sw1;
+  __shared__ ScaleWindow<FMT> sw0, sw1;
   __shared__ ZeroWindow<FMT> zw0, zw1;
+  __shared__ HiStage<FMT> hs0, hs1;
   __shared__ RowTables rt;
   gemm_persistent<MODE>(a, rt, [&](int nmb, const Tile &tile, int slice0, int nsl) {
     dispatch_nmb(nmb, [&](auto n) {
-      gemm_tile_wide<MODE, decltype(n)::value, FMT>(a, st0, st1, sw0, sw1, zw0, zw1, rt, tile.e, tile.row0,
-                                                    tile.rows, slice0, nsl);
+      gemm_tile_wide<MODE, decltype(n)::value, FMT>(a, st0, st1, sw0, sw1, zw0, zw1, hs0, hs1, rt, tile.e,
+                                                    tile.row0, tile.rows, slice0, nsl);
     });
   });
 }
@@ -1062,10 +1150,9 @@ int persistent_grid(long long work_upper, int wg_per_cu) {
 template <int MODE>
 hipError_t launch_gemm(GemmArgs args, long long tiles_upper, int matrix_rows, int fmt, hipStream_t s) {
   // The wide pipeline addresses A through a buffer resource: 32-bit offsets.
-  // It takes the asymmetric format when K/g is a multiple of 8 (whole zero-
-  // point windows); the 5-bit format's fifth-bit words do not fit its LDS,
-  // so that one runs on the general pipeline.
-  const bool wide_fmt = fmt == kFmtInt4 || (fmt == kFmtInt4Asym && (args.K / args.g) % 8 == 0);
+  // It takes the asymmetric and 5-bit formats when K/g is a multiple of 8
+  // (whole zero-point and 4-group scale windows).
+  const bool wide_fmt = fmt == kFmtInt4 || ((fmt == kFmtInt4Asym || fmt == kFmtInt5) && (args.K / args.g) % 8 == 0);
   const bool wide = STRATA_GEMM_WIDE && wide_fmt && args.K % kKS == 0 &&
                     ((args.K / args.g) % 8 == 0 || args.K / args.g < 8) &&
                     (long long)args.a_rows * args.K * 2 < (1LL << 32);
@@ -1079,6 +1166,8 @@ hipError_t launch_gemm(GemmArgs args, long long tiles_upper, int matrix_rows, in
     const long long items = tiles_upper * ((args.nslices + args.spi - 1) / args.spi);
     if (fmt == kFmtInt4Asym)
       moe_gemm_wide<MODE, kFmtInt4Asym><<<persistent_grid(items, 1), 64 * kWideW, 0, s>>>(args);
+    else if (fmt == kFmtInt5)
+      moe_gemm_wide<MODE, kFmtInt5><<<persistent_grid(items, 1), 64 * kWideW, 0, s>>>(args);
     else
       moe_gemm_wide<MODE, kFmtInt4><<<persistent_grid(items, 1), 64 * kWideW, 0, s>>>(args);
   } else {
