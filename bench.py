@@ -4,7 +4,9 @@
 Headline: MoE-layer prefill throughput (tokens/s) on the 6144-token chunk
 (T=6144, H=2048, I=512, E=512, top-10, int4 g=64).  One step = one layer
 invocation = route + permute + ffn (fused weighted combine) on inputs already
-resident in HBM.  Also reported on the same JSON line:
+resident in HBM, the weight codes in the tiled layout (STRATA_L_TILED,
+converted once when the weights are loaded; --layout rows for row-major).
+Also reported on the same JSON line:
 
 * roofline of the dominant kernel, timed with HIP events the library records
   around its own launches (on the launch stream), over a second timed region
@@ -62,16 +64,17 @@ def source_sha(kernel: str) -> str | None:
     return h.hexdigest()[:16]
 
 
-def counted_traffic(kernel: str, workload: str):
+def counted_traffic(kernel: str, workload: str, layout: str = "tiled"):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current source of the kernel; otherwise None."""
+    taken on the current source of the kernel with weight codes in `layout`;
+    otherwise None."""
     try:
         with open(TRAFFIC_FILE) as f:
             data = json.load(f)
     except (OSError, ValueError):
         return None
     rec = data.get(f"{kernel}@{workload}")
-    if not rec or rec.get("source_sha") != source_sha(kernel):
+    if not rec or rec.get("source_sha") != source_sha(kernel) or rec.get("layout") != layout:
         return None
     return rec.get("bytes_per_launch")
 
@@ -89,7 +92,8 @@ COUNTED_KERNELS = {
 }
 
 
-def record_traffic(fetch_csv: str, write_csv: str, prefill_workload: str, decode_workload: str = "decode") -> dict:
+def record_traffic(fetch_csv: str, write_csv: str, prefill_workload: str, decode_workload: str = "decode",
+                   layout: str = "tiled") -> dict:
     """HBM bytes per launch from two rocprofv3 --pmc runs of this script with
     --calibrate-copy (FETCH_SIZE, then WRITE_SIZE; both in KiB per dispatch).
     Each counter is scaled by what it reads for the 1 GiB device copy that
@@ -122,7 +126,7 @@ def record_traffic(fetch_csv: str, write_csv: str, prefill_workload: str, decode
         workload = prefill_workload if kind == "prefill" else decode_workload
         out[f"{kernel}@{workload}"] = {
             "fetch_bytes": round(fb), "write_bytes": round(wb), "bytes_per_launch": round(fb + wb),
-            "dispatches": min(len(fk), len(wk)), "source_sha": source_sha(kernel)}
+            "dispatches": min(len(fk), len(wk)), "source_sha": source_sha(kernel), "layout": layout}
     return out
 
 
@@ -213,7 +217,7 @@ def kernel_table(qe):
     return rows
 
 
-def roofline_of(kernel: str, avg_us: float, cfg, pairs: int, distinct: int, workload: str):
+def roofline_of(kernel: str, avg_us: float, cfg, pairs: int, distinct: int, workload: str, layout: str = "tiled"):
     work, unit, bound = kernel_work(kernel, cfg, pairs, distinct)
     if work is None:
         return None
@@ -230,7 +234,7 @@ def roofline_of(kernel: str, avg_us: float, cfg, pairs: int, distinct: int, work
         "peak": peak,
         "unit": u,
         "frac": round(achieved / peak, 4),
-        "traffic": counted_traffic(kernel, workload),
+        "traffic": counted_traffic(kernel, workload, layout),
         "avg_us": round(avg_us, 2),
         "work_per_launch": work,
         "work_unit": unit,
@@ -249,7 +253,7 @@ def bench_prefill(qe, args):
     dev = torch.device("cuda:0")
     logits = torch.from_numpy(inp.logits).to(dev)
     x = torch.from_numpy(inp.x_bf16.view(np.int16)).to(dev).view(torch.bfloat16)
-    experts = qe.QuantizedExperts.from_numpy(inp.weights, cfg.g, dev)
+    experts = qe.QuantizedExperts.from_numpy(inp.weights, cfg.g, dev, layout=args.layout)
     # The step is one strata_moe_layer call (fused mode); with --fused 0 the
     # four calls of the deterministic unfused mode.  The four separate calls of
     # the fused mode are timed beside it: each is a host call of its own, and
@@ -289,12 +293,12 @@ def bench_prefill(qe, args):
 
     distinct = int((run.counts > 0).sum().item())  # experts this layer call touches
     dominant = max(table, key=lambda n: table[n]["total_ms"])
-    roof = roofline_of(dominant, table[dominant]["avg_us"], cfg, cfg.T * cfg.k, distinct, cfg.name)
+    roof = roofline_of(dominant, table[dominant]["avg_us"], cfg, cfg.T * cfg.k, distinct, cfg.name, args.layout)
     kernels = {n: round(v["avg_us"], 2) for n, v in table.items()}
     return cfg, inp, secs, secs_timed, roof, kernels, secs4, steady, timed
 
 
-def bench_decode(qe, args, name: str = "decode"):
+def bench_decode(qe, args, name: str = "decode", layout: str | None = None):
     import torch
 
     import synth
@@ -303,7 +307,8 @@ def bench_decode(qe, args, name: str = "decode"):
     inp = synth.make_inputs(cfg)
     steps = synth.decode_steps(cfg, 64)
     dev = torch.device("cuda:0")
-    experts = qe.QuantizedExperts.from_numpy(inp.weights, cfg.g, dev)
+    layout = layout or args.layout
+    experts = qe.QuantizedExperts.from_numpy(inp.weights, cfg.g, dev, layout=layout)
     L = [torch.from_numpy(lg).to(dev) for lg, _ in steps]
     X = [torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16) for _, xb in steps]
     # The step is one strata_moe_layer call (two kernels at this size); the
@@ -329,7 +334,7 @@ def bench_decode(qe, args, name: str = "decode"):
     kern = {}
     for name in ("decode_route_gateup", "decode_down_combine"):
         if name in table:
-            r = roofline_of(name, table[name]["avg_us"], cfg, cfg.T * cfg.k, avg_distinct, cfg.name)
+            r = roofline_of(name, table[name]["avg_us"], cfg, cfg.T * cfg.k, avg_distinct, cfg.name, layout)
             kern[name] = {k_: r[k_] for k_ in ("avg_us", "achieved", "frac", "traffic")}
     device_us = sum(v["total_ms"] for v in table.values()) * 1e3 / K
     pct = step_percentiles(lambda i: run(L[i % n], X[i % n]), min(K, 500))
@@ -376,6 +381,7 @@ def bench_decode(qe, args, name: str = "decode"):
     return {
         "workload": f"{cfg.name}: T={cfg.T} (1 token + {cfg.T - 1} drafts{shared}) H={cfg.H} I={cfg.I} E={cfg.E} "
                     f"k={cfg.k} g={cfg.g}, 64 rotating steps",
+        "weight_layout": layout,
         "distinct_experts_per_step": round(avg_distinct, 2),
         "us_per_step": round(us, 2),
         "device_us_per_step": round(device_us, 2),
@@ -411,18 +417,25 @@ def bench_secondary(qe, args):
 
     out = {}
     dev = torch.device("cuda:0")
-    # (name, bound, steps, one strata_moe_layer call per step instead of the
-    # separate calls); the last four are the other weight formats.
-    for name, bound, steps, single in (("tiny", None, 200, False), ("prefill512", "hbm", 50, False),
-                                       ("zipf6144", "mfma", 10, False), ("prefill6144_g32", "mfma", 50, False),
-                                       ("prefill6144_g128", "mfma", 50, False),
-                                       ("prefill6144_asym", "mfma", 30, True), ("prefill6144_int5", "mfma", 30, True),
-                                       ("decode_asym", "hbm", 500, True), ("decode_int5", "hbm", 500, True)):
+    # (record, workload, bound, steps, one strata_moe_layer call per step
+    # instead of the separate calls, weight layout); then the other weight
+    # formats, and the headline prefill chunk with the codes in the other
+    # layout.
+    other = "rows" if args.layout == "tiled" else "tiled"
+    L = args.layout
+    for key, name, bound, steps, single, layout in (
+            ("tiny", "tiny", None, 200, False, L), ("prefill512", "prefill512", "hbm", 50, False, L),
+            ("zipf6144", "zipf6144", "mfma", 10, False, L), ("prefill6144_g32", "prefill6144_g32", "mfma", 50, False, L),
+            ("prefill6144_g128", "prefill6144_g128", "mfma", 50, False, L),
+            ("prefill6144_asym", "prefill6144_asym", "mfma", 30, True, L),
+            ("prefill6144_int5", "prefill6144_int5", "mfma", 30, True, L),
+            ("decode_asym", "decode_asym", "hbm", 500, True, L), ("decode_int5", "decode_int5", "hbm", 500, True, L),
+            (f"prefill6144_{other}", "prefill6144", "mfma", 30, True, other)):
         cfg = synth.config(name)
         inp = synth.make_inputs(cfg)
         logits = torch.from_numpy(inp.logits).to(dev)
         x = torch.from_numpy(inp.x_bf16.view(np.int16)).to(dev).view(torch.bfloat16)
-        experts = qe.QuantizedExperts.from_numpy(inp.weights, cfg.g, dev)
+        experts = qe.QuantizedExperts.from_numpy(inp.weights, cfg.g, dev, layout=layout)
         run = qe.LayerRunner(experts, cfg.T, cfg.E, cfg.k, fused=True, device=dev, single_call=single)
         warm = warm_up(lambda i: run(logits, x), max(args.warmup, 3))
         secs = time_region(lambda i: run(logits, x), steps)
@@ -430,7 +443,8 @@ def bench_secondary(qe, args):
         flops, nbytes = layer_work(cfg, distinct)
         us = secs / steps * 1e6
         rec = {"workload": f"{cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} g={cfg.g}",
-               "weights": cfg.fmt, "call": "strata_moe_layer" if single else "route + permute + ffn",
+               "weights": cfg.fmt, "layout": layout,
+               "call": "strata_moe_layer" if single else "route + permute + ffn",
                "us_per_step": round(us, 2), "tokens_per_s": round(cfg.T / (us * 1e-6), 1), "steps": steps,
                "warmup_steps": warm,
                "distinct_experts": distinct, "alg_flops": flops, "alg_bytes": int(nbytes)}
@@ -438,8 +452,8 @@ def bench_secondary(qe, args):
             rec["roofline"] = {"bound": "hbm", "frac": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBS, 4)}
         elif bound == "mfma":
             rec["roofline"] = {"bound": "mfma", "frac": round(flops / (us * 1e-6) / 1e12 / PEAK_MFMA_TFLOPS, 4)}
-        out[name] = rec
-        log(f"[bench] {name}: {us:.1f} us/step")
+        out[key] = rec
+        log(f"[bench] {key}: {us:.1f} us/step")
         del experts, run, logits, x, inp
         torch.cuda.empty_cache()
     out["router6144"] = bench_router(qe, args)
@@ -662,6 +676,8 @@ def main(argv=None) -> int:
     ap.add_argument("--steady-secs", type=float, default=3.0,
                     help="length of the steady-state prefill region with per-step percentiles (0: skip)")
     ap.add_argument("--fused", type=int, default=1, help="1: fused weighted scatter-add; 0: y rows + combine")
+    ap.add_argument("--layout", choices=("tiled", "rows"), default="tiled",
+                    help="byte layout of the packed weight codes (strata_weight_layout)")
     ap.add_argument("--router-only", action="store_true",
                     help="time only the router projection + top-k call (router6144) and print its record")
     ap.add_argument("--decode-only", metavar="WORKLOAD",
@@ -677,7 +693,7 @@ def main(argv=None) -> int:
     if args.record_traffic:
         # Records of other workloads already in the file are kept.
         rec = record_traffic(*args.record_traffic, prefill_workload=args.workload,
-                             decode_workload=args.decode_only or "decode")
+                             decode_workload=args.decode_only or "decode", layout=args.layout)
         try:
             with open(TRAFFIC_FILE) as f:
                 merged = json.load(f)
@@ -739,6 +755,7 @@ def main(argv=None) -> int:
         "config": {
             "workload": f"{cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} g={cfg.g}",
             "weights": "int4 symmetric, fp16 scale per group",
+            "weight_layout": args.layout,
             "activations": "bf16 in, fp32 out",
             "global_batch": cfg.T,
             "parallelism": "single GPU",
@@ -755,6 +772,9 @@ def main(argv=None) -> int:
         # Drafts that route mostly to the first token's experts: the pairs of
         # one expert stream the same weight rows on one XCD at the same time.
         result["decode_shared"] = bench_decode(qe, args, "decode_shared")
+        # The same decode step with the codes in the other layout.
+        other = "rows" if args.layout == "tiled" else "tiled"
+        result[f"decode_{other}"] = bench_decode(qe, args, "decode", layout=other)
     if not args.no_secondary:
         result["secondary"] = bench_secondary(qe, args)
         result["kv_cache"] = bench_kv(qe, args)

@@ -74,6 +74,26 @@ typedef enum {
 } strata_weight_format;
 
 /*
+ * Byte layouts of the packed codes (gate, up, down) of strata_moe_weights.
+ *   STRATA_L_ROWS   row-major: byte j of row n of expert e at
+ *                   (e*N + n) * K/2 + j.
+ *   STRATA_L_TILED  32-row x 64-byte tiles: with r = e*N + n,
+ *                   byte ((r/32) * (K/128) + j/64) * 2048 + (r%32) * 64 + j%64.
+ *                   Every 128-wide K stage of 32 rows is one contiguous
+ *                   2 KB run, so the grouped matrix-core GEMMs, which stream
+ *                   a stage of many rows at a time, read whole cache lines
+ *                   (the row-major layout gives them half lines and about
+ *                   twice the fetched bytes).  Every call that takes weights
+ *                   reads both layouts with the same results, bit for bit;
+ *                   strata_moe_tile_weights converts once at load time.
+ * Scales, zero points and fifth-bit words are row-major in both.
+ */
+typedef enum {
+  STRATA_L_ROWS = 0,
+  STRATA_L_TILED = 1
+} strata_weight_layout;
+
+/*
  * Group-quantized expert weights (all device pointers, caller-owned).
  *
  * Each matrix W[N][K] (gate, up: N = I, K = H; down: N = H, K = I) holds
@@ -111,6 +131,7 @@ typedef struct {
   const uint32_t *gate_hi;    /* STRATA_W_INT5 only, else NULL */
   const uint32_t *up_hi;
   const uint32_t *down_hi;
+  int32_t layout;             /* strata_weight_layout of gate, up, down; 0 = STRATA_L_ROWS */
 } strata_moe_weights;
 
 /*
@@ -305,6 +326,21 @@ int strata_moe_layer(const float *logits, const uint16_t *x_bf16, int32_t T, int
 int strata_moe_layer_noalloc(const float *logits, const uint16_t *x_bf16, int32_t T, int32_t k,
                              const strata_moe_weights *w, int32_t *topk_ids, float *topk_w, int32_t *counts,
                              int32_t *offsets, int32_t *perm, int32_t *inv_perm, float *out, void *stream);
+
+/*
+ * strata_moe_tile_weights - rewrite one packed-code array from STRATA_L_ROWS
+ * to STRATA_L_TILED (a permutation of its bytes; see strata_weight_layout).
+ * Call it once per matrix (gate, up, down) when the weights are loaded.
+ *
+ *   src   in  uint8 [rows][K/2], row-major packed codes; rows = E*N of the
+ *             matrix (E*I for gate and up, E*H for down), K its row length.
+ *   dst   out uint8, rows*K/2 bytes in the tiled layout.  Must not overlap
+ *             src.  Both 16-byte aligned.
+ *   rows  a multiple of 32, K a multiple of 128 (every matrix in the
+ *         supported envelope qualifies); rows = 0 enqueues nothing.
+ *         Otherwise STRATA_ERR_INVALID_ARGUMENT.
+ */
+int strata_moe_tile_weights(const uint8_t *src, uint8_t *dst, int64_t rows, int32_t K, void *stream);
 
 /*
  * Bytes of device workspace that strata_moe_permute, strata_moe_ffn and

@@ -13,7 +13,7 @@ and the current stream.  The names follow the C ABI in ``include/strata_moe.h``:
 from __future__ import annotations
 
 import ctypes
-from dataclasses import dataclass
+from dataclasses import dataclass, replace
 
 import numpy as np
 import torch
@@ -22,6 +22,7 @@ from ._abi import LIB_PATH, StrataError, StrataMoeWeights, check, load  # noqa: 
 
 __all__ = [
     "QuantizedExperts",
+    "tile_weights",
     "StrataError",
     "route",
     "permute",
@@ -71,6 +72,9 @@ class QuantizedExperts:
     ``fmt`` (``strata_weight_format``): "int4" (q = u - 8), "int4_asym"
     (q = u - z, zero points ``*_zero`` uint8 [E, N, K/g/2], two per byte) or
     "int5" (q = u + 16 b - 16, fifth-bit words ``*_hi`` int32 [E, N, K/32]).
+    ``layout`` (``strata_weight_layout``) of the bytes of gate, up and down:
+    "rows" (row-major) or "tiled" (32-row x 128-K tiles, see
+    ``tile_weights``; the same tensor shapes).
     """
 
     gate: torch.Tensor
@@ -87,8 +91,10 @@ class QuantizedExperts:
     gate_hi: torch.Tensor | None = None
     up_hi: torch.Tensor | None = None
     down_hi: torch.Tensor | None = None
+    layout: str = "rows"
 
     FORMATS = {"int4": 0, "int4_asym": 1, "int5": 2}
+    LAYOUTS = {"rows": 0, "tiled": 1}
 
     @property
     def num_experts(self) -> int:
@@ -102,10 +108,21 @@ class QuantizedExperts:
     def hidden(self) -> int:
         return int(self.gate.shape[2] * 2)
 
+    def to_tiled(self) -> "QuantizedExperts":
+        """A copy whose gate, up and down codes are in the tiled layout
+        (``strata_moe_tile_weights``; scales and side data are shared)."""
+        if self.layout == "tiled":
+            return self
+        return replace(self, gate=tile_weights(self.gate), up=tile_weights(self.up),
+                       down=tile_weights(self.down), layout="tiled")
+
     @classmethod
-    def from_numpy(cls, w: dict, group: int, device="cuda") -> "QuantizedExperts":
+    def from_numpy(cls, w: dict, group: int, device="cuda", layout: str = "rows") -> "QuantizedExperts":
         """From host arrays by name: gate, gate_scale, ... and, for the other
-        formats, gate_zero, ... (uint8) or gate_hi, ... (uint32 words)."""
+        formats, gate_zero, ... (uint8) or gate_hi, ... (uint32 words); the
+        codes are row-major and converted on the GPU for layout="tiled"."""
+        if layout not in cls.LAYOUTS:
+            raise ValueError(f"layout must be one of {sorted(cls.LAYOUTS)}, got {layout!r}")
 
         def dev(a):
             a = np.ascontiguousarray(a)
@@ -116,8 +133,9 @@ class QuantizedExperts:
         fmt = "int4_asym" if "gate_zero" in w else "int5" if "gate_hi" in w else "int4"
         side = {name + sfx: dev(w[name + sfx]) for name in ("gate", "up", "down")
                 for sfx in ("_zero", "_hi") if name + sfx in w}
-        return cls(dev(w["gate"]), dev(w["gate_scale"]), dev(w["up"]), dev(w["up_scale"]),
-                   dev(w["down"]), dev(w["down_scale"]), group, fmt=fmt, **side)
+        ex = cls(dev(w["gate"]), dev(w["gate_scale"]), dev(w["up"]), dev(w["up_scale"]),
+                 dev(w["down"]), dev(w["down_scale"]), group, fmt=fmt, **side)
+        return ex.to_tiled() if layout == "tiled" else ex
 
     def descriptor(self) -> StrataMoeWeights:
         for name, dt in (("gate", torch.uint8), ("up", torch.uint8), ("down", torch.uint8),
@@ -126,6 +144,8 @@ class QuantizedExperts:
             _need(getattr(self, name), dt, name)
         if self.fmt not in self.FORMATS:
             raise ValueError(f"fmt must be one of {sorted(self.FORMATS)}, got {self.fmt!r}")
+        if self.layout not in self.LAYOUTS:
+            raise ValueError(f"layout must be one of {sorted(self.LAYOUTS)}, got {self.layout!r}")
         side = {}
         for name in ("gate", "up", "down"):
             for sfx, dt in (("_zero", torch.uint8), ("_hi", torch.int32)):
@@ -138,8 +158,20 @@ class QuantizedExperts:
             self.up_scale.data_ptr(), self.down.data_ptr(), self.down_scale.data_ptr(),
             self.num_experts, self.hidden, self.inter, self.group, self.FORMATS[self.fmt],
             side["gate_zero"], side["up_zero"], side["down_zero"],
-            side["gate_hi"], side["up_hi"], side["down_hi"],
+            side["gate_hi"], side["up_hi"], side["down_hi"], self.LAYOUTS[self.layout],
         )
+
+
+def tile_weights(packed: torch.Tensor) -> torch.Tensor:
+    """``strata_moe_tile_weights``: packed codes uint8 [E, N, K/2] (row-major)
+    -> a new tensor of the same shape holding them in the tiled layout."""
+    _need(packed, torch.uint8, "packed")
+    if packed.dim() != 3:
+        raise ValueError(f"packed must be [E, N, K/2], got shape {tuple(packed.shape)}")
+    E, N, KB = packed.shape
+    out = torch.empty_like(packed)
+    check(load().strata_moe_tile_weights(_p(packed), _p(out), E * N, 2 * KB, _stream(packed)))
+    return out
 
 
 def workspace_size(T: int, E: int, k: int, H: int, I: int, g: int) -> int:

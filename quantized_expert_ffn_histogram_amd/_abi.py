@@ -42,6 +42,7 @@ class StrataMoeWeights(ctypes.Structure):
         ("gate_hi", _vp),
         ("up_hi", _vp),
         ("down_hi", _vp),
+        ("layout", _i32),
     ]
 
 
@@ -63,6 +64,7 @@ SIGNATURES = {
         [_vp, _vp, _i32, _i32, ctypes.POINTER(StrataMoeWeights), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     ),
     "strata_kv_quantize": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _i32, _vp]),
+    "strata_moe_tile_weights": (ctypes.c_int, [_vp, _vp, ctypes.c_int64, _i32, _vp]),
     "strata_kv_quantize_pair": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _vp]),
     "strata_sparse_attention_workspace_size": (_sz, [_i32, _i32, _i32]),
     "strata_sparse_attention": (

@@ -80,6 +80,8 @@ int check_weights(const char *fn, const strata_moe_weights *w) {
   REQUIRE_PTR(fn, w->up_scale);
   REQUIRE_PTR(fn, w->down);
   REQUIRE_PTR(fn, w->down_scale);
+  if (w->layout != STRATA_L_ROWS && w->layout != STRATA_L_TILED)
+    return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "layout=%d is not a strata_weight_layout", (int)w->layout);
   const bool zeros = w->gate_zero || w->up_zero || w->down_zero;
   const bool his = w->gate_hi || w->up_hi || w->down_hi;
   switch (w->format) {
@@ -113,6 +115,7 @@ strata::FfnWeights ffn_weights(const strata_moe_weights *w) {
   strata::FfnWeights fw{w->gate,       w->up,         w->down,   w->gate_scale, w->up_scale,
                         w->down_scale, w->num_experts, w->hidden, w->inter,      w->group};
   fw.fmt = w->format;
+  fw.tiled = w->layout == STRATA_L_TILED;
   if (w->format == STRATA_W_INT4_ASYM) {
     fw.gate_x = w->gate_zero;
     fw.up_x = w->up_zero;
@@ -506,6 +509,21 @@ int strata_kv_quantize_pair(const uint16_t *k_bf16, const uint16_t *v_bf16, int3
   REQUIRE_PTR(fn, v_scales);
   const hipError_t e = launch_kv_quantize(k_bf16, T, Hkv, slots, L, k_codes, k_scales,
                                           static_cast<hipStream_t>(stream), v_bf16, v_codes, v_scales);
+  return e == hipSuccess ? ok() : hip_fail(fn, e);
+}
+
+int strata_moe_tile_weights(const uint8_t *src, uint8_t *dst, int64_t rows, int32_t K, void *stream) {
+  static const char *fn = "strata_moe_tile_weights";
+  if (rows < 0 || rows % 32)
+    return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "rows=%lld must be a non-negative multiple of 32", (long long)rows);
+  if (K < 128 || K % 128) return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "K=%d must be a positive multiple of 128", K);
+  if (rows == 0) return ok();
+  REQUIRE_PTR(fn, src);
+  REQUIRE_PTR(fn, dst);
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src), b = reinterpret_cast<uintptr_t>(dst);
+  const uintptr_t n = (uintptr_t)rows * (uintptr_t)(K / 2);
+  if (a < b + n && b < a + n) return fail(STRATA_ERR_INVALID_ARGUMENT, fn, "src=%p and dst=%p overlap", src, dst);
+  const hipError_t e = launch_tile_weights(src, dst, rows, K, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? ok() : hip_fail(fn, e);
 }
 

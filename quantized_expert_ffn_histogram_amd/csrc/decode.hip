@@ -58,6 +58,7 @@ struct DecodeArgs {
   float *out;      // fp32 [T][H]
   // Other weight formats: zero points or fifth-bit words of gate, up, down.
   const uint8_t *gate_x, *up_x, *down_x;
+  int tiled;  // packed codes in 32-row x 128-K tiles (packed_offset), else row-major
 };
 
 template <int EPL, int NCH, int FMT>
@@ -105,8 +106,9 @@ __global__ __launch_bounds__(256) void decode_route_gateup_kernel(DecodeArgs a) 
     for (int c = 0; c < NCH; ++c) {
       const size_t row = (size_t)e * a.I + n0 + cc;
       const int kk = 2048 * c + kl;
-      wg[cc][c] = *reinterpret_cast<const uint4 *>(a.gate + row * kb + kk / 2);
-      wu[cc][c] = *reinterpret_cast<const uint4 *>(a.up + row * kb + kk / 2);
+      const size_t wo = packed_offset(row, (uint32_t)(kk / 2), (uint32_t)kb, a.tiled != 0);
+      wg[cc][c] = *reinterpret_cast<const uint4 *>(a.gate + wo);
+      wu[cc][c] = *reinterpret_cast<const uint4 *>(a.up + wo);
       sgb[cc][c] = a.gate_s[row * ng + kk / a.g];
       sub_[cc][c] = a.up_s[row * ng + kk / a.g];
       xg[cc][c] = gemv_aux<FMT>(a.gate_x, row, a.H, a.g, kk);
@@ -204,7 +206,7 @@ __global__ __launch_bounds__(256) void decode_down_combine_kernel(DecodeArgs a) 
   for (int jj = 0; jj < KMAX; ++jj) {
     const int e = __builtin_amdgcn_readlane(eid, jj < a.k ? jj : a.k - 1);  // past k: repeat the last row
     const size_t row = (size_t)e * a.H + nc;
-    wq[jj] = *reinterpret_cast<const uint4 *>(a.down + row * kb + 16 * sub);
+    wq[jj] = *reinterpret_cast<const uint4 *>(a.down + packed_offset(row, 16u * sub, (uint32_t)kb, a.tiled != 0));
     sdb[jj] = a.down_s[row * ng + (32 * sub) / a.g];
     xd[jj] = gemv_aux<FMT>(a.down_x, row, a.I, a.g, 32 * sub);
   }
@@ -349,6 +351,7 @@ hipError_t launch_decode_layer(const float *logits, const uint16_t *x, int T, in
   a.gate_x = w.gate_x;
   a.up_x = w.up_x;
   a.down_x = w.down_x;
+  a.tiled = w.tiled;
   hipError_t err = hipSuccess;
   if (w.fmt == 1)
     launch_decode_kernels<1>(a, T, k, w, s, err);

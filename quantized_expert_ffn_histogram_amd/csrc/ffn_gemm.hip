@@ -96,6 +96,7 @@ struct GemmArgs {
   // two per byte [E][N][K/g/2] (asymmetric 4-bit), or fifth-bit words
   // [E][N][K/32] (5-bit), for B0 and B1.
   const uint8_t *X0, *X1;
+  int tiled;           // packed codes in 32-row x 128-K tiles (packed_offset), else row-major
 };
 
 // Weight formats (values of strata_weight_format).
@@ -665,11 +666,16 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
     const int r = p >> 4, c = (p & 15) ^ (r & 15);
     aoff[i] = ((uint32_t)rt.src[r] * (uint32_t)a.K + 8 * c) * 2;
   }
+  // Weight rows: row rr of a 32-row block, 16-byte quarter (swizzled) of the
+  // stage's 64 bytes; consecutive stages are 64 bytes apart in a row-major
+  // row, 2 KB apart (one tile) in the tiled layout.
   uint32_t boff[2];
+  const uint32_t b_row = a.tiled ? 64u : (uint32_t)(a.K / 2);
+  const uint32_t b_stage = a.tiled ? 2048u : (uint32_t)(kKS / 2);
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int rr = 16 * t + (lane >> 2);
-    boff[t] = (uint32_t)rr * (a.K / 2) + 16 * ((lane & 3) ^ ((rr >> 2) & 3));
+    boff[t] = (uint32_t)rr * b_row + 16 * ((lane & 3) ^ ((rr >> 2) & 3));
   }
   const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(a.A, (uint32_t)a.a_rows * (uint32_t)a.K * 2u);
 
@@ -726,7 +732,7 @@ __device__ __forceinline__ void gemm_tile_wide(const GemmArgs &a, WideStage &st0
   };
   auto issue_b = [&](WideStage &st, int q) {
     const int nb = q >> 1, t = q & 1;
-    const uint32_t so = (uint32_t)lc * (kKS / 2);
+    const uint32_t so = (uint32_t)lc * b_stage;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rb[nb], lds_at(st.b, lds_w4k + (uint32_t)(nb * 2048 + t * 1024)), 16,
                                              boff[t], so, 0, 0);
   };
@@ -1003,7 +1009,11 @@ __device__ __forceinline__ void gemm_tile_general(const GemmArgs &a, const GenRi
   const char *bbase[kNB];
   const char *sbase[kNB];
   weight_bases<MODE, kGenW>(a, e, slice, wave, valid, bbase, sbase);
-  const uint32_t boff = (uint32_t)col2 * (a.K / 2) + 16 * hh;
+  // Weight rows: row col2 of a 32-row block, 16-byte half hh of the chunk's
+  // 32 bytes (chunk c at byte 32c of a row-major row; in the tiled layout at
+  // tile c/2, byte 32*(c%2) of the row's 64).
+  const bool tiled = a.tiled != 0;
+  const uint32_t boff = (uint32_t)col2 * (tiled ? 64u : (uint32_t)(a.K / 2)) + 16 * hh;
   const uint32_t soff = ((uint32_t)col2 * (a.K / a.g)) * 2;
   const int g_shift = 31 - __clz(a.g);  // g is a power of two
   // Side data of the other formats: the row's zero-point bytes or fifth-bit words.
@@ -1028,7 +1038,8 @@ __device__ __forceinline__ void gemm_tile_general(const GemmArgs &a, const GenRi
 #pragma unroll
     for (int nb = 0; nb < kNB; ++nb) {
       const int base = brow_of(wave, nb, 0) * 2;
-      __builtin_amdgcn_global_load_lds(bbase[nb] + kc / 2 + boff, as_lds(&st.b[base]), 16, 0, 0);
+      const uint32_t kcb = tiled ? (uint32_t)(kc >> 7) * 2048u + (uint32_t)((kc >> 1) & 63) : (uint32_t)(kc >> 1);
+      __builtin_amdgcn_global_load_lds(bbase[nb] + kcb + boff, as_lds(&st.b[base]), 16, 0, 0);
       __builtin_amdgcn_global_load_lds(sbase[nb] + 2 * ((kc + 32 * hh) >> g_shift) + soff, as_lds(&st.s[base]), 2,
                                        0, 0);
       if constexpr (FMT == kFmtInt4Asym)
@@ -1222,6 +1233,7 @@ hipError_t launch_ffn_gemm(const uint16_t *x, int T, int k, const FfnWeights &w,
   g.fused = 0;
   g.X0 = w.gate_x;
   g.X1 = w.up_x;
+  g.tiled = w.tiled;
   {
     KernelTimer timer("gemm_gateup", s);
     if ((err = launch_gemm<0>(g, tiles_upper, w.I, w.fmt, s)) != hipSuccess) return err;

@@ -63,6 +63,7 @@ struct GemvArgs {
   // Other weight formats: zero points (two per byte, [E][N][K/g/2]) or
   // fifth-bit words ([E][N][K/32]) of gate, up and down.
   const uint8_t *gate_x, *up_x, *down_x;
+  int tiled;  // packed codes in 32-row x 128-K tiles (packed_offset), else row-major
 };
 
 
@@ -142,8 +143,9 @@ __global__ __launch_bounds__(256, NCH == 1 ? 4 : 2) void gemv_gateup_kernel(Gemv
     for (int c = 0; c < NCH; ++c) {
       const size_t row = (size_t)en.e * a.I + n0 + cc;
       const int kk = 2048 * c + kl;
-      wg[cc][c] = *reinterpret_cast<const uint4 *>(a.gate + row * kb + kk / 2);
-      wu[cc][c] = *reinterpret_cast<const uint4 *>(a.up + row * kb + kk / 2);
+      const size_t wo = packed_offset(row, (uint32_t)(kk / 2), (uint32_t)kb, a.tiled != 0);
+      wg[cc][c] = *reinterpret_cast<const uint4 *>(a.gate + wo);
+      wu[cc][c] = *reinterpret_cast<const uint4 *>(a.up + wo);
       sgb[cc][c] = a.gate_s[row * ng + kk / a.g];
       sub_[cc][c] = a.up_s[row * ng + kk / a.g];
       xg[cc][c] = gemv_aux<FMT>(a.gate_x, row, a.H, a.g, kk);
@@ -257,7 +259,7 @@ __global__ __launch_bounds__(256, 4) void gemv_down_kernel(GemvArgs a) {
   for (int it = 0; it < kDownIter; ++it) {
     const int n = nbase + it * RPI;
     const size_t row = (size_t)en.e * a.H + (n < a.H ? n : 0);
-    wq[it] = *reinterpret_cast<const uint4 *>(a.down + row * kb + 16 * sub);
+    wq[it] = *reinterpret_cast<const uint4 *>(a.down + packed_offset(row, 16u * sub, (uint32_t)kb, a.tiled != 0));
     sdb[it] = a.down_s[row * ng + (32 * sub) / a.g];
     xd[it] = gemv_aux<FMT>(a.down_x, row, a.I, a.g, 32 * sub);
   }
@@ -336,6 +338,7 @@ hipError_t launch_ffn_gemv(const uint16_t *x, int T, int k, const FfnWeights &w,
   a.gate_x = w.gate_x;
   a.up_x = w.up_x;
   a.down_x = w.down_x;
+  a.tiled = w.tiled;
   {
     KernelTimer timer("gemv_gateup", s);
     const int grid = entries * (w.I / kGateUpCols);

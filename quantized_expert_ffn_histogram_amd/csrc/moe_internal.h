@@ -45,9 +45,22 @@ struct FfnWeights {
   // Side data of formats 1 and 2: zero points [E][N][K/g/2] (two per byte)
   // or fifth-bit words [E][N][K/32] (as bytes).
   const uint8_t *gate_x = nullptr, *up_x = nullptr, *down_x = nullptr;
+  int tiled = 0;  // packed codes in 32-row x 128-K tiles (packed_offset), else row-major
 };
 
+// Byte offset of packed byte `kb` (K index 2*kb) of weight row `row` in a
+// matrix of `rb` = K/2 bytes per row; `row` counts the rows of all experts
+// (e*N + n; N is a multiple of 32, K of 128).  Row-major: row*rb + kb.
+// Tiled: a 32-row block's K/128 tiles of 32 rows x 64 bytes follow one
+// another, each row's 64 bytes contiguous inside its tile, so the 64 bytes of
+// one 128-wide K stage of 32 rows are one 2 KB run.
+__host__ __device__ __forceinline__ size_t packed_offset(size_t row, uint32_t kb, uint32_t rb, bool tiled) {
+  return tiled ? ((row >> 5) * (rb >> 6) + (kb >> 6)) * 2048u + (row & 31u) * 64u + (kb & 63u) : row * rb + kb;
+}
+
 // ---------------------------------------------------------------- launchers
+// Row-major packed codes [rows][K/2] -> the tiled layout of packed_offset.
+hipError_t launch_tile_weights(const uint8_t *src, uint8_t *dst, long long rows, int K, hipStream_t s);
 hipError_t launch_route(const float *logits, int T, int E, int k, int *ids, float *w,
                         hipStream_t s);
 // Router projection logits[t][e] = x[t] . w_router[e] (bf16 in, fp32 out).

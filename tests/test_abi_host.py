@@ -202,6 +202,52 @@ def test_weight_format_descriptor_is_checked(fmt, side, kw, code, needle):
     assert needle in _err(lib)
 
 
+@pytest.mark.parametrize("layout", [2, -1])
+def test_weight_layout_is_checked(layout):
+    abi, lib = _lib()
+    w = _weights(abi)
+    w.layout = layout
+    fake = ctypes.c_void_p(0x10000)
+    assert lib.strata_moe_ffn(fake, 8, 2, ctypes.byref(w), fake, fake, None, fake, fake, 1 << 30, None) == 1
+    assert f"layout={layout}" in _err(lib)
+
+
+def test_tiled_layout_passes_the_layout_check():
+    # layout 1 is accepted: the call goes on to the next check (an invalid format here)
+    abi, lib = _lib()
+    w = _weights(abi)
+    w.layout, w.format = 1, 3
+    fake = ctypes.c_void_p(0x10000)
+    assert lib.strata_moe_ffn(fake, 8, 2, ctypes.byref(w), fake, fake, None, fake, fake, 1 << 30, None) == 1
+    assert "format=3" in _err(lib) and "layout" not in _err(lib)
+
+
+@pytest.mark.parametrize(
+    "src,dst,rows,K,needle",
+    [
+        (0x10000, 0x80000, 33, 128, "rows=33"),
+        (0x10000, 0x80000, -32, 128, "rows=-32"),
+        (0x10000, 0x80000, 32, 64, "K=64"),
+        (0x10000, 0x80000, 32, 192, "K=192"),
+        (None, 0x80000, 32, 128, "src is NULL"),
+        (0x10000, None, 32, 128, "dst is NULL"),
+        (0x10000, 0x80008, 32, 128, "16-byte aligned"),
+        (0x10000, 0x10000 + 2032, 32, 128, "overlap"),   # 32 rows x 64 bytes = 2048 bytes
+        (0x10000 + 2032, 0x10000, 32, 128, "overlap"),
+    ],
+)
+def test_tile_weights_rejects_bad_arguments(src, dst, rows, K, needle):
+    abi, lib = _lib()
+    rc = lib.strata_moe_tile_weights(ctypes.c_void_p(src), ctypes.c_void_p(dst), rows, K, None)
+    assert rc == 1, _err(lib)
+    assert needle in _err(lib)
+
+
+def test_tile_weights_of_zero_rows_enqueues_nothing():
+    abi, lib = _lib()
+    assert lib.strata_moe_tile_weights(None, None, 0, 128, None) == 0
+
+
 def test_fifth_bit_words_must_be_word_aligned():
     abi, lib = _lib()
     w = _weights(abi)

@@ -108,6 +108,9 @@ def test_record_traffic_scales_counters_by_the_copy_calibration(tmp_path):
     assert gu["fetch_bytes"] == 2000 * 1024 * 2 and gu["write_bytes"] == 200 * 1024
     assert gu["bytes_per_launch"] == gu["fetch_bytes"] + gu["write_bytes"]
     assert gu["dispatches"] == 2 and gu["source_sha"] == bench.source_sha("gemm_gateup")
+    assert gu["layout"] == "tiled"
+    assert bench.record_traffic(str(fetch), str(write), "prefill6144", layout="rows")["gemm_down@prefill6144"][
+        "layout"] == "rows"
     dn = rec["gemm_down@prefill6144"]
     assert dn["bytes_per_launch"] == 500 * 1024 * 2 + 50 * 1024
     # kernels with no counter rows get no record
@@ -118,12 +121,14 @@ def test_counted_traffic_is_dropped_once_the_kernel_source_changes(monkeypatch, 
     path = tmp_path / "traffic.json"
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
     assert bench.counted_traffic("gemm_down", "prefill6144") is None  # no file
-    rec = {"gemm_down@prefill6144": {"bytes_per_launch": 123, "source_sha": bench.source_sha("gemm_down")},
-           "gemm_gateup@prefill6144": {"bytes_per_launch": 456, "source_sha": "0" * 16}}
+    rec = {"gemm_down@prefill6144": {"bytes_per_launch": 123, "source_sha": bench.source_sha("gemm_down"),
+                                     "layout": "tiled"},
+           "gemm_gateup@prefill6144": {"bytes_per_launch": 456, "source_sha": "0" * 16, "layout": "tiled"}}
     path.write_text(json.dumps(rec))
     assert bench.counted_traffic("gemm_down", "prefill6144") == 123
     assert bench.counted_traffic("gemm_gateup", "prefill6144") is None  # stale source
     assert bench.counted_traffic("gemm_down", "prefill512") is None  # other workload
+    assert bench.counted_traffic("gemm_down", "prefill6144", "rows") is None  # counted with the other layout
 
 
 def test_committed_traffic_records_are_well_formed():
@@ -139,3 +144,4 @@ def test_committed_traffic_records_are_well_formed():
         assert abs(r["bytes_per_launch"] - (r["fetch_bytes"] + r["write_bytes"])) <= 1
         assert r["fetch_bytes"] > 0 and r["write_bytes"] > 0
         assert len(r["source_sha"]) == 16
+        assert r["layout"] in ("tiled", "rows")
