@@ -11,6 +11,9 @@
 * The 6144-token prefill chunk in each format and the skewed 6144-token
   layer through the benchmark's single layer call: tiled equals row-major
   on every output element.
+* The envelope's edges through the layer call: 1024 experts on the grouped
+  GEMM and the decode paths, gate/up rows of K = 8192 and down rows of
+  K = 16384 (a block's last tile ends at the end of its buffer range).
 """
 import dataclasses
 
@@ -186,3 +189,30 @@ def test_tiled_descriptor_round_trip(qe):
     assert rows.descriptor().layout == 0 and tiled.descriptor().layout == 1
     assert tiled.to_tiled() is tiled
     assert tiled.gate.shape == rows.gate.shape and tiled.down.shape == rows.down.shape
+
+
+EDGE_CFGS = [
+    # the grouped-GEMM layer call with 1024 experts (1200 pairs: the multi-segment grouping)
+    synth.MoEConfig("tiled_fold_e1024", T=150, H=256, I=128, E=1024, k=8, g=32, seed=97),
+    # the two-kernel decode layer with 1024 experts and k = 16
+    synth.MoEConfig("tiled_decode_e1024", T=3, H=512, I=256, E=1024, k=16, g=64, seed=98),
+    # long rows: gate/up K = 8192 (64 stages of the wide pipeline, 64 tiles per 32-row block)
+    synth.MoEConfig("tiled_h8192", T=64, H=8192, I=1024, E=4, k=2, g=128, seed=99),
+    # down K = 16384: the last tile of a block ends at the end of the block's buffer range
+    synth.MoEConfig("tiled_i16384", T=48, H=256, I=16384, E=2, k=1, g=128, seed=100),
+]
+
+
+@pytest.mark.parametrize("cfg", EDGE_CFGS, ids=_ids(EDGE_CFGS))
+def test_tiled_edge_shapes_layer_call(qe, cfg):
+    """strata_moe_layer at the envelope's edges: tiled equals row-major bit for
+    bit, and both match the oracle."""
+    inp = inputs(cfg)
+    logits, x, rows, tiled = _both_layouts(inp)
+    print(f"[layout] {cfg.name}: T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} k={cfg.k} g={cfg.g}", flush=True)
+    a = qe.layer(logits, x, rows, cfg.k)
+    b = qe.layer(logits, x, tiled, cfg.k)
+    assert np.array_equal(_np(a["out"]), _np(b["out"])), cfg.name
+    ref = oracle.moe_layer(inp.logits, inp.x_bf16, inp.weights, cfg.k, cfg.g)
+    assert np.array_equal(_np(b["ids"]).reshape(-1), ref["ids"].reshape(-1))
+    check_close(_np(b["out"]), ref["out"], f"{cfg.name} out (tiled)")
