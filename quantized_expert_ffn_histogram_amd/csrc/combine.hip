@@ -68,6 +68,19 @@ __global__ __launch_bounds__(256) void combine_pairs_kernel(const uint4 *__restr
   __builtin_nontemporal_store(f32x4_t{acc[4], acc[5], acc[6], acc[7]}, reinterpret_cast<f32x4_t *>(&out[g * 2 + 1]));
 }
 
+// Instance KMAX = k for every k up to 16 (no padding rows to load), and
+// kMaxTopK above that.
+template <int KMAX>
+void combine_pairs_for_k(const uint4 *y, const float *topk_w, int T, int k, int H, float4 *out, dim3 grid,
+                         hipStream_t s) {
+  if constexpr (KMAX < 16) {
+    if (k > KMAX) return combine_pairs_for_k<KMAX + 1>(y, topk_w, T, k, H, out, grid, s);
+  } else if constexpr (KMAX == 16) {
+    if (k > KMAX) return combine_pairs_for_k<kMaxTopK>(y, topk_w, T, k, H, out, grid, s);
+  }
+  combine_pairs_kernel<KMAX><<<grid, 256, 0, s>>>(y, topk_w, T, k, H, out);
+}
+
 }  // namespace
 
 hipError_t launch_combine_pairs(const uint16_t *y16, const float *topk_w, int T, int k, int H, float *out,
@@ -75,20 +88,8 @@ hipError_t launch_combine_pairs(const uint16_t *y16, const float *topk_w, int T,
   const long long groups = (long long)T * (H / 8);
   KernelTimer timer("combine", s);
   const dim3 grid((unsigned)((groups + 255) / 256));
-  const uint4 *y = reinterpret_cast<const uint4 *>(y16);
-  float4 *o = reinterpret_cast<float4 *>(out);
-  if (k <= 2)
-    combine_pairs_kernel<2><<<grid, 256, 0, s>>>(y, topk_w, T, k, H, o);
-  else if (k <= 4)
-    combine_pairs_kernel<4><<<grid, 256, 0, s>>>(y, topk_w, T, k, H, o);
-  else if (k <= 8)
-    combine_pairs_kernel<8><<<grid, 256, 0, s>>>(y, topk_w, T, k, H, o);
-  else if (k <= 12)
-    combine_pairs_kernel<12><<<grid, 256, 0, s>>>(y, topk_w, T, k, H, o);
-  else if (k <= 16)
-    combine_pairs_kernel<16><<<grid, 256, 0, s>>>(y, topk_w, T, k, H, o);
-  else
-    combine_pairs_kernel<kMaxTopK><<<grid, 256, 0, s>>>(y, topk_w, T, k, H, o);
+  combine_pairs_for_k<1>(reinterpret_cast<const uint4 *>(y16), topk_w, T, k, H, reinterpret_cast<float4 *>(out),
+                         grid, s);
   return hipGetLastError();
 }
 

@@ -383,6 +383,26 @@ def test_layer_call(qe, cfg, path, monkeypatch):
     assert torch.equal(ids, res["ids"]) and torch.equal(w, res["w"])
 
 
+@pytest.mark.parametrize("k", list(range(1, 18)) + [32])
+def test_layer_call_combine_every_k(qe, k):
+    """The grouped-GEMM layer call finishes with the combine of the fp16 y
+    rows, which has one kernel instance per k up to 16 and a padded one above:
+    each of them against the oracle (ids bit-exact, out within the
+    tolerance)."""
+    cfg = synth.MoEConfig(f"combine_k{k}", T=120, H=256, I=128, E=max(24, k), k=k, g=32, seed=700 + k)
+    inp = inputs(cfg)
+    logits, x, ex = to_device(inp)
+    qe.timing_enable(True)
+    res = qe.layer(logits, x, ex, cfg.k)
+    names = qe.timing_kernels()
+    qe.timing_enable(False)
+    assert "combine" in names and "decode_route_gateup" not in names, names
+    ref = oracle.moe_layer(inp.logits, inp.x_bf16, inp.weights, cfg.k, cfg.g)
+    for key in ("ids", "counts", "offsets", "perm", "inv_perm"):
+        assert (_np(res[key]) == ref[key]).all(), key
+    check_close(_np(res["out"]), ref["out"], f"{cfg.name} out")
+
+
 def test_layer_call_repeatable_and_zero_tokens(qe):
     """The two-kernel decode output is bitwise repeatable across calls with a
     different step in between; T = 0 writes zero counts and offsets."""
