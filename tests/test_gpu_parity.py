@@ -403,6 +403,25 @@ def test_layer_call_combine_every_k(qe, k):
     check_close(_np(res["out"]), ref["out"], f"{cfg.name} out")
 
 
+@pytest.mark.parametrize("k", list(range(1, 17)))
+def test_layer_call_decode_every_k(qe, k):
+    """The two-kernel decode layer has one down + combine instance per range
+    of k (up to 4, 6, 8, 10, 12, 16): each of them against the oracle."""
+    cfg = synth.MoEConfig(f"decode_k{k}", T=4, H=256, I=128, E=max(32, k), k=k, g=32, seed=720 + k)
+    assert _two_kernel_shape(cfg)
+    inp = inputs(cfg)
+    logits, x, ex = to_device(inp)
+    qe.timing_enable(True)
+    res = qe.layer(logits, x, ex, cfg.k)
+    names = qe.timing_kernels()
+    qe.timing_enable(False)
+    assert "decode_down_combine" in names, names
+    ref = oracle.moe_layer(inp.logits, inp.x_bf16, inp.weights, cfg.k, cfg.g)
+    for key in ("ids", "counts", "offsets", "perm", "inv_perm"):
+        assert (_np(res[key]) == ref[key]).all(), key
+    check_close(_np(res["out"]), ref["out"], f"{cfg.name} out")
+
+
 def test_layer_call_repeatable_and_zero_tokens(qe):
     """The two-kernel decode output is bitwise repeatable across calls with a
     different step in between; T = 0 writes zero counts and offsets."""
