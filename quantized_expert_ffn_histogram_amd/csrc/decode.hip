@@ -11,9 +11,9 @@
 //   decode_route_gateup (grid: ceil(T/4) routing blocks + T*k*(I/16) others)
 //     routing blocks: one wavefront per token selects its top-k and writes
 //       topk_ids / topk_w exactly as the routing kernel does (same code);
-//     the others: block (pair p = t*k + j, 16 h columns) re-selects the j-th
-//       expert of token t in one wavefront (same code, so the same expert),
-//       then streams that expert's gate and up rows for its columns and
+//     the others: block (pair p = t*k + j, 16 h columns): each wavefront
+//       re-selects the j-th expert of token t itself (same code, so the same
+//       expert; no barrier before its weight loads), then streams that expert's gate and up rows for its columns and
 //       writes h[p] = silu(gate . x_t) * (up . x_t) in fp16, pair order,
 //       each 8 consecutive columns stored as the pairs (c, c+4) that the
 //       dot products consume (h lives only between the two kernels);
@@ -85,15 +85,12 @@ __global__ __launch_bounds__(256) void decode_route_gateup_kernel(DecodeArgs a) 
 #pragma unroll
     for (int q = 0; q < 4; ++q) xv[c][q] = reinterpret_cast<const uint4 *>(a.x + (size_t)t * a.H + 2048 * c + kl)[q];
 
-  __shared__ int e_s;
-  if (wave == 0) {
-    int my_id;
-    float my_val;
-    wave_topk<EPL>(a.logits + (size_t)t * a.E, a.E, j + 1, my_id, my_val, sc[0]);
-    if (lane == j) e_s = my_id;
-  }
-  __syncthreads();
-  const int e = e_s;
+  // Every wavefront selects the expert itself (same code, same result), so
+  // that no barrier stands between the selection and its weight loads.
+  int my_id;
+  float my_val;
+  wave_topk<EPL>(a.logits + (size_t)t * a.E, a.E, j + 1, my_id, my_val, sc[wave]);
+  const int e = __builtin_amdgcn_readlane(my_id, j);
 
   const int kb = a.H / 2, ng = a.H / a.g;
   const int n0 = cs * kDecCols + wave * kDecColsPerWave;
