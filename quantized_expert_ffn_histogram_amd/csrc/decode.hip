@@ -194,6 +194,7 @@ __global__ __launch_bounds__(256) void decode_down_combine_kernel(DecodeArgs a) 
                                                (uint32_t)(slot + lane) * 16u, 0, 0, 0);
     }
   }
+  asm volatile("" ::: "memory");  // the weight loads below are issued after the h loads
 
   // Row n of each pair's expert: this lane's 32 K values (16 bytes) and their scale.
   const int kb = a.I / 2, ng = a.I / a.g;
@@ -207,8 +208,16 @@ __global__ __launch_bounds__(256) void decode_down_combine_kernel(DecodeArgs a) 
     sdb[jj] = a.down_s[row * ng + (32 * sub) / a.g];
     xd[jj] = gemv_aux<FMT>(a.down_x, row, a.I, a.g, 32 * sub);
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wavefront's h loads have landed
-  __syncthreads();                                 // ... and everyone's
+  // This wavefront's h loads have landed once no more than the loads issued
+  // after them are outstanding: per expert slot a weight row and a scale,
+  // and for the other formats their side data.  The weight stream goes on
+  // during the chunk sums below, and the dot products wait per expert.
+  constexpr int kYounger = (FMT == 0 ? 2 : 3) * KMAX;
+  static_assert(kYounger < 64, "vmcnt range");
+  asm volatile("" ::: "memory");  // every load above is issued before the wait
+  __builtin_amdgcn_s_waitcnt((kYounger & 0xF) | ((kYounger >> 4) << 14) | 0x0F70);
+  asm volatile("" ::: "memory");
+  __syncthreads();  // ... and everyone's
   // Sum of each 32-value chunk of h (the offset correction of the dot
   // products), once per chunk: thread tid sums chunks tid, tid + 256, ...
   __shared__ float hsums[kDecodeMaxKI / 32];
