@@ -185,54 +185,66 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
   }
   __syncthreads();
 
-  // Every load of the workgroup goes out first: the chunk's value rows and
-  // scales (staged to LDS below) and this thread's key words of all rounds.
-  const int units = C * Hkv * 4;  // 16-byte units of value rows
-  constexpr int kVRegs = (C * 8 * 4 + 255) / 256;  // 16-byte value units per thread, up to Hkv = 8
-  u32x4_t vreg[kVRegs] = {};
-#pragma unroll
-  for (int r = 0; r < kVRegs; ++r) {
-    const int u = tid + 256 * r;
-    if (u < units) {
-      const int pl = u / (Hkv * 4), w = u - pl * (Hkv * 4);
-      vreg[r] = reinterpret_cast<const u32x4_t *>(a.vc + (size_t)pos_s[pl] * Hkv * (D / 2))[w];
-    }
-  }
-  constexpr int kSRegs = (C * 8 + 255) / 256;  // value scales per thread, up to Hkv = 8
-  float vsc[kSRegs];
-#pragma unroll
-  for (int r = 0; r < kSRegs; ++r) {
-    const int u = tid + 256 * r;
-    vsc[r] = 0.0f;
-    if (u < C * Hkv) {
-      const int pl = u / Hkv, g = u - pl * Hkv;
-      vsc[r] = (float)__builtin_bit_cast(_Float16, a.vs[(size_t)pos_s[pl] * Hkv + g]);
-    }
-  }
+  // Every load of the workgroup goes out before the first use: this thread's
+  // key words of all rounds and its query slices first, the values after
+  // them; loads complete in order, so the scores wait only for the keys and
+  // queries while the values are still in flight.
   // Scores: thread (position pl, head g, quarter qd) of a round, 4 * Hkv
   // threads per position.
   const int tpp = 4 * Hkv, ppr = 256 / tpp;  // threads per position, positions per round
   const int rounds = (C + ppr - 1) / ppr;    // <= kMaxRounds
   const int pr = tid / tpp, rem = tid - pr * tpp, g = rem >> 2, qd = rem & 3;
+  // The loads are unconditional, from clamped in-range indices (rounds past
+  // `rounds` and units past the chunk are loaded and never used), so that
+  // they form one straight run with no branch between them, and the fp16
+  // scales stay raw bits until their first use: a conversion next to its
+  // load would make every later load wait for it.
   u32x4_t kw[kMaxRounds];
-  float ksc[kMaxRounds];
+  uint32_t ksb[kMaxRounds];
 #pragma unroll
   for (int r = 0; r < kMaxRounds; ++r) {
     const int pl = min(r * ppr + pr, C - 1);
     const size_t row = (size_t)pos_s[pl] * Hkv + g;
-    kw[r] = r < rounds ? reinterpret_cast<const u32x4_t *>(a.kc + row * (D / 2))[qd] : u32x4_t{};
-    ksc[r] = r < rounds ? (float)__builtin_bit_cast(_Float16, a.ks[row]) : 0.0f;
+    kw[r] = reinterpret_cast<const u32x4_t *>(a.kc + row * (D / 2))[qd];
+    ksb[r] = a.ks[row];
   }
+  // This thread's query slices, loaded here and converted below.
+  u32x4_t qraw[G][4];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    const u32x4_t *qp = reinterpret_cast<const u32x4_t *>(a.q + ((size_t)t * Hq + g * G + hh) * D + 32 * qd);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) qraw[hh][c] = qp[c];
+  }
+  asm volatile("" ::: "memory");  // keeps the issue order: keys, queries, then values
+  // ... then the chunk's value rows and scales (staged to LDS below).
+  const int units = C * Hkv * 4;  // 16-byte units of value rows
+  constexpr int kVRegs = (C * 8 * 4 + 255) / 256;  // 16-byte value units per thread, up to Hkv = 8
+  u32x4_t vreg[kVRegs];
+#pragma unroll
+  for (int r = 0; r < kVRegs; ++r) {
+    const int u = min(tid + 256 * r, units - 1);
+    const int pl = u / (Hkv * 4), w = u - pl * (Hkv * 4);
+    vreg[r] = reinterpret_cast<const u32x4_t *>(a.vc + (size_t)pos_s[pl] * Hkv * (D / 2))[w];
+  }
+  constexpr int kSRegs = (C * 8 + 255) / 256;  // value scales per thread, up to Hkv = 8
+  uint32_t vsb[kSRegs];
+#pragma unroll
+  for (int r = 0; r < kSRegs; ++r) {
+    const int u = min(tid + 256 * r, C * Hkv - 1);
+    const int pl = u / Hkv, gv = u - pl * Hkv;
+    vsb[r] = a.vs[(size_t)pos_s[pl] * Hkv + gv];
+  }
+  asm volatile("" ::: "memory");  // every load above is issued before the first use below
   // This thread's query slices (G heads x 32 values) and their sums (the
   // offset term: q . (u - 8) = q . u - 8 sum(q)).
   float qv[G][32], qsum[G];
 #pragma unroll
   for (int hh = 0; hh < G; ++hh) {
-    const u32x4_t *qp = reinterpret_cast<const u32x4_t *>(a.q + ((size_t)t * Hq + g * G + hh) * D + 32 * qd);
     qsum[hh] = 0.0f;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const u32x4_t v = qp[c];
+      const u32x4_t v = qraw[hh][c];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         qv[hh][8 * c + 2 * i] = bf16_lo(v[i]);
@@ -253,7 +265,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
       float acc = 0.0f;
 #pragma unroll
       for (int i = 0; i < 32; ++i) acc = fmaf(qv[hh][i], uf[i], acc);
-      acc = fmaf(-8.0f, qsum[hh], acc) * ksc[r];
+      acc = fmaf(-8.0f, qsum[hh], acc) * (float)__builtin_bit_cast(_Float16, (uint16_t)ksb[r]);
       acc += dpp_f32<0xB1>(acc);  // quad reduction over the four quarters
       acc += dpp_f32<0x4E>(acc);
       if (qd == 0 && pl < C) score[g * G + hh][pl] = pl < cnt ? acc * a.sm_scale : -INFINITY;
@@ -266,7 +278,7 @@ __global__ __launch_bounds__(256) void attn_partial_kernel(AttnArgs a) {
 #pragma unroll
   for (int r = 0; r < kSRegs; ++r) {
     const int u = tid + 256 * r;
-    if (u < C * Hkv) vscale[u / Hkv][u % Hkv] = vsc[r];
+    if (u < C * Hkv) vscale[u / Hkv][u % Hkv] = (float)__builtin_bit_cast(_Float16, (uint16_t)vsb[r]);
   }
   __syncthreads();
 
